@@ -1,0 +1,335 @@
+/*
+ * sa_oracle.c -- plain, slow CPU oracle for index-selected sparse attention over a paged
+ * KV cache (indexer scores -> Top-K -> sparse attention).
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * load this file's library. It shares no code, header, table or constant with the HIP library
+ * and includes none of its files. Every loop below is the plain definition of the step it
+ * computes, in the order the definition states it; nothing is blocked, fused or reordered.
+ *
+ * Pages cited (by title and section):
+ *   [SameDay]  "How the Ascend Computing Platform Achieves Same-Day Inference Adaptation for
+ *              Ultra-Large Sparse Models"
+ *   [Domestic] "Engineering Path for Day-0 Adaptation of Trillion-Scale Sparse Models on
+ *              Domestic AI Accelerators"
+ *   [CANN]     "Day0 Inference Support and Performance Optimization for Next-Gen Large Models on
+ *              Huawei Ascend CANN Architecture"
+ *   [GPUGuide] "Adapting GPU Software Stacks for Ultra-Large-Scale Sparse Attention Models:
+ *              A Day-0 Engineering Guide"
+ *
+ * Arithmetic: REAL is double unless built with -DORACLE_FLOAT (then float). Inputs arrive in
+ * their storage formats (bf16 bit patterns, OCP E4M3 codes) and are decoded here from the
+ * formats' own definitions.
+ *
+ * Return codes: 0 = ok, 1 = an input violates the stated preconditions (nothing is written
+ * past the first violation, results are then undefined).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef ORACLE_FLOAT
+typedef float REAL;
+#define ORACLE_REAL_BYTES 4
+#else
+typedef double REAL;
+#define ORACLE_REAL_BYTES 8
+#endif
+
+int ora_real_bytes(void) { return ORACLE_REAL_BYTES; }
+
+/* ---------------------------------------------------------------- storage formats */
+
+/* bf16 is the upper half of an IEEE-754 binary32 word: widen by appending 16 zero bits. */
+REAL ora_bf16(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (REAL)f;
+}
+
+/* OCP 8-bit floating point, E4M3 variant: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa
+ * bits, subnormals when the exponent field is 0, no infinities, S.1111.111 is NaN.
+ * Quantized data types for the indexer and the KV cache: [CANN] §2.1 and §3. */
+REAL ora_e4m3(uint8_t code) {
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    REAL mag;
+    if (e == 15 && m == 7) return (REAL)NAN;
+    if (e == 0)
+        mag = (REAL)m / 8 * ldexp(1.0, 1 - 7);       /* subnormal: 0.m x 2^(1-bias) */
+    else
+        mag = (1 + (REAL)m / 8) * ldexp(1.0, e - 7); /* normal: 1.m x 2^(e-bias) */
+    return sign ? -mag : mag;
+}
+
+/* ---------------------------------------------------------------- paged addressing */
+
+/* Blocked KV layout: a logical position maps to (block number, offset inside the block) and
+ * the block number goes through the per-sequence page table ([Domestic] §3.2; [SameDay] §3.1;
+ * [GPUGuide] §3.2). Returns the physical slot = physical_page * page_size + offset. */
+static int64_t slot_of(const int32_t *page_table, int pages_per_seq, int page_size, int seq,
+                       int64_t pos) {
+    int64_t logical_page = pos / page_size;
+    int64_t offset = pos % page_size;
+    int64_t phys = page_table[(int64_t)seq * pages_per_seq + logical_page];
+    return phys * page_size + offset;
+}
+
+/* element i of a stored vector: format 0 = bf16 bit patterns, 1 = E4M3 codes times a per-row
+ * fp32 scale (scale_row is that row's scale; ignored for bf16). */
+static REAL elem(int fmt, const void *base, int64_t index, float scale_row) {
+    if (fmt == 0) return ora_bf16(((const uint16_t *)base)[index]);
+    return ora_e4m3(((const uint8_t *)base)[index]) * (REAL)scale_row;
+}
+
+/* ---------------------------------------------------------------- indexer scores */
+
+/*
+ * Lightweight indexer: relevance score of one history token for one query token, with
+ * head-weight weighting ([CANN] §1 and §2.1; "scoring -- reduction" in [Domestic] §3.1).
+ * The pages do not write the formula down; this library's definition is
+ *     d[h]  = sum_i q_I[h][i] * k_I[t][i]          (i ascending)
+ *     s[t]  = sum_h w[h] * max(d[h], 0)            (h ascending)
+ * with one k_I row per token shared by all indexer heads.
+ */
+static REAL score_one(int heads, int dim, const uint16_t *qrow /* [heads, dim] */,
+                      const float *wrow /* [heads] */, int fmt, const void *keys,
+                      const float *key_scale, int64_t slot) {
+    REAL s = 0;
+    float sc = key_scale ? key_scale[slot] : 1.0f;
+    for (int h = 0; h < heads; h++) {
+        REAL d = 0;
+        for (int i = 0; i < dim; i++)
+            d += ora_bf16(qrow[(int64_t)h * dim + i]) * elem(fmt, keys, slot * dim + i, sc);
+        s += (REAL)wrow[h] * (d > 0 ? d : 0);
+    }
+    return s;
+}
+
+/*
+ * Scores of every visible position for each query row.
+ *   query r belongs to sequence q_seq[r] and sits at absolute position q_pos[r]; it sees
+ *   positions 0..q_pos[r] (causal, inclusive). out[r * ncols + t] = s[t] for t <= q_pos[r],
+ *   -inf for q_pos[r] < t < ncols.
+ *   keys: [num_pages, page_size, dim] in format key_fmt; key_scale: [num_pages, page_size].
+ */
+int ora_index_scores(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads, int dim,
+                     const uint16_t *q_idx, const float *w, int key_fmt, const void *keys,
+                     const float *key_scale, const int32_t *page_table, int pages_per_seq,
+                     int page_size, int64_t ncols, REAL *out) {
+    for (int r = 0; r < nq; r++)
+        if (q_pos[r] >= ncols || q_pos[r] >= (int64_t)pages_per_seq * page_size) return 1;
+    int64_t total = (int64_t)nq * ncols;
+#pragma omp parallel for schedule(dynamic, 512)
+    for (int64_t f = 0; f < total; f++) {
+        int r = (int)(f / ncols);
+        int64_t t = f % ncols;
+        if (t > q_pos[r]) {
+            out[f] = -(REAL)INFINITY;
+            continue;
+        }
+        int64_t slot = slot_of(page_table, pages_per_seq, page_size, q_seq[r], t);
+        out[f] = score_one(heads, dim, q_idx + (int64_t)r * heads * dim, w + (int64_t)r * heads,
+                           key_fmt, keys, key_scale, slot);
+    }
+    return 0;
+}
+
+/*
+ * Coarse stage of hierarchical history-block selection ([SameDay] §3.1; [GPUGuide] §3.1):
+ * the same score formula applied to one cached summary row per block ("summary information
+ * already held in the cache"). Block j of query r is visible when j * page_size <= q_pos[r];
+ * its summary row is pooled[page_table[seq][j]] (bf16, [num_pages, dim]).
+ * out[r * nblk_cols + j] = block score, -inf for invisible columns.
+ */
+int ora_block_scores(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads, int dim,
+                     const uint16_t *q_idx, const float *w, const uint16_t *pooled,
+                     const int32_t *page_table, int pages_per_seq, int page_size,
+                     int64_t nblk_cols, REAL *out) {
+    int64_t total = (int64_t)nq * nblk_cols;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t f = 0; f < total; f++) {
+        int r = (int)(f / nblk_cols);
+        int64_t j = f % nblk_cols;
+        if (j * page_size > q_pos[r] || j >= pages_per_seq) {
+            out[f] = -(REAL)INFINITY;
+            continue;
+        }
+        int64_t phys = page_table[(int64_t)q_seq[r] * pages_per_seq + j];
+        out[f] = score_one(heads, dim, q_idx + (int64_t)r * heads * dim, w + (int64_t)r * heads,
+                           0, pooled, NULL, phys);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- Top-K */
+
+typedef struct {
+    REAL s;
+    int64_t t;
+} cand;
+
+/* order: larger score first; equal scores (which includes -0 == +0) -> lower position first */
+static int cand_cmp(const void *a, const void *b) {
+    const cand *x = (const cand *)a, *y = (const cand *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+static int pos_cmp(const void *a, const void *b) {
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Top-K filtering keeps the K most relevant positions and returns a discrete index set
+ * ([Domestic] §3.1; [CANN] §1). Candidates are (score, position) pairs; a full sort by
+ * (score desc, position asc) stands in for any selection algorithm; the first min(K, n) are
+ * kept, written in ascending position order, and the row is padded with -1. */
+static int topk_of(cand *c, int64_t n, int k, int32_t *out_row) {
+    for (int64_t i = 0; i < n; i++)
+        if (isnan((double)c[i].s)) return 1;
+    qsort(c, (size_t)n, sizeof(cand), cand_cmp);
+    int keep = n < k ? (int)n : k;
+    for (int j = 0; j < keep; j++) out_row[j] = (int32_t)c[j].t;
+    qsort(out_row, (size_t)keep, sizeof(int32_t), pos_cmp);
+    for (int j = keep; j < k; j++) out_row[j] = -1;
+    return 0;
+}
+
+/* Row-wise Top-K over scores[r * ncols + t] for t < n_valid[r]. */
+int ora_topk(int nrows, int64_t ncols, const REAL *scores, const int64_t *n_valid, int k,
+             int32_t *out) {
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int r = 0; r < nrows; r++) {
+        int64_t n = n_valid[r] < ncols ? n_valid[r] : ncols;
+        cand *c = (cand *)malloc(sizeof(cand) * (size_t)(n > 0 ? n : 1));
+        for (int64_t t = 0; t < n; t++) {
+            c[t].s = scores[(int64_t)r * ncols + t];
+            c[t].t = t;
+        }
+        bad |= topk_of(c, n, k, out + (int64_t)r * k);
+        free(c);
+    }
+    return bad;
+}
+
+/*
+ * Fine stage of the hierarchical selection ([SameDay] §3.1: "fine filtering computes only
+ * within candidate blocks"): for query r the candidates are the visible tokens of the blocks
+ * listed in blocks[r * nblk .. +nblk) (entries < 0 are ignored); their indexer scores are
+ * computed with the token formula and the Top-K among them is returned as above.
+ */
+int ora_topk_in_blocks(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads, int dim,
+                       const uint16_t *q_idx, const float *w, int key_fmt, const void *keys,
+                       const float *key_scale, const int32_t *page_table, int pages_per_seq,
+                       int page_size, const int32_t *blocks, int nblk, int k, int32_t *out) {
+    int bad = 0;
+    for (int r = 0; r < nq; r++) {
+        int64_t ncand = 0;
+        for (int j = 0; j < nblk; j++) {
+            int32_t b = blocks[(int64_t)r * nblk + j];
+            if (b < 0) continue;
+            if (b >= pages_per_seq) return 1;
+            int64_t lo = (int64_t)b * page_size, hi = lo + page_size;
+            if (hi > q_pos[r] + 1) hi = q_pos[r] + 1;
+            if (hi > lo) ncand += hi - lo;
+        }
+        cand *c = (cand *)malloc(sizeof(cand) * (size_t)(ncand > 0 ? ncand : 1));
+        int64_t n = 0;
+        for (int j = 0; j < nblk; j++) {
+            int32_t b = blocks[(int64_t)r * nblk + j];
+            if (b < 0) continue;
+            int64_t lo = (int64_t)b * page_size, hi = lo + page_size;
+            if (hi > q_pos[r] + 1) hi = q_pos[r] + 1;
+            for (int64_t t = lo; t < hi; t++) c[n++].t = t;
+        }
+#pragma omp parallel for schedule(dynamic, 256)
+        for (int64_t i = 0; i < n; i++) {
+            int64_t slot = slot_of(page_table, pages_per_seq, page_size, q_seq[r], c[i].t);
+            c[i].s = score_one(heads, dim, q_idx + (int64_t)r * heads * dim,
+                               w + (int64_t)r * heads, key_fmt, keys, key_scale, slot);
+        }
+        bad |= topk_of(c, n, k, out + (int64_t)r * k);
+        free(c);
+    }
+    return bad;
+}
+
+/* ---------------------------------------------------------------- sparse attention */
+
+/*
+ * Sparse attention over the gathered rows of the selected positions ([CANN] §1 and §2.1:
+ * the attention "reads the main attention KV precisely according to the selected indices";
+ * [Domestic] §3). For query row r, query head h (kv head g = h / (heads_q / heads_kv)):
+ *     l_j = scale * sum_i q[r][h][i] * K(t_j)[g][i]      over selected t_j >= 0
+ *     m   = max_j l_j
+ *     o   = sum_j exp(l_j - m) * V(t_j)[g] / sum_j exp(l_j - m)
+ * An empty selection gives o = 0. Element (slot, g, i) of K is k_cache[slot * k_stride +
+ * g * k_head_stride + i]; likewise V. V may be the same buffer as K (a latent row whose first
+ * dim_v entries are the value). fp8 rows (kv_fmt 1) are code * k_scale[slot] (v_scale[slot]).
+ * out: [nq, heads_q, dim_v].
+ */
+int ora_sparse_attn(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads_q,
+                    int heads_kv, int dim_qk, int dim_v, const uint16_t *q, int kv_fmt,
+                    const void *k_cache, const void *v_cache, const float *k_scale,
+                    const float *v_scale, int64_t k_stride, int64_t v_stride,
+                    int64_t k_head_stride, int64_t v_head_stride, const int32_t *page_table,
+                    int pages_per_seq, int page_size, int k, const int32_t *idx,
+                    float softmax_scale, REAL *out) {
+    if (heads_kv <= 0 || heads_q % heads_kv) return 1;
+    for (int r = 0; r < nq; r++)
+        for (int j = 0; j < k; j++) {
+            int32_t t = idx[(int64_t)r * k + j];
+            if (t > q_pos[r]) return 1;
+        }
+    int group = heads_q / heads_kv;
+    int64_t total = (int64_t)nq * heads_q;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t f = 0; f < total; f++) {
+        int r = (int)(f / heads_q), h = (int)(f % heads_q), g = h / group;
+        const uint16_t *qv = q + ((int64_t)r * heads_q + h) * dim_qk;
+        const int32_t *sel = idx + (int64_t)r * k;
+        REAL *o = out + ((int64_t)r * heads_q + h) * dim_v;
+        REAL *logit = (REAL *)malloc(sizeof(REAL) * (size_t)(k > 0 ? k : 1));
+        int64_t *slots = (int64_t *)malloc(sizeof(int64_t) * (size_t)(k > 0 ? k : 1));
+        REAL m = -(REAL)INFINITY;
+        int any = 0;
+        for (int j = 0; j < k; j++) {
+            if (sel[j] < 0) continue;
+            int64_t slot = slot_of(page_table, pages_per_seq, page_size, q_seq[r], sel[j]);
+            float ks = k_scale ? k_scale[slot] : 1.0f;
+            REAL d = 0;
+            for (int i = 0; i < dim_qk; i++)
+                d += ora_bf16(qv[i]) *
+                     elem(kv_fmt, k_cache, slot * k_stride + g * k_head_stride + i, ks);
+            logit[j] = (REAL)softmax_scale * d;
+            slots[j] = slot;
+            if (isnan((double)logit[j])) bad = 1;
+            if (logit[j] > m) m = logit[j];
+            any = 1;
+        }
+        for (int i = 0; i < dim_v; i++) o[i] = 0;
+        if (any) {
+            REAL den = 0;
+            for (int j = 0; j < k; j++) {
+                if (sel[j] < 0) continue;
+                REAL p = exp(logit[j] - m);
+                float vs = v_scale ? v_scale[slots[j]] : 1.0f;
+                den += p;
+                for (int i = 0; i < dim_v; i++)
+                    o[i] += p * elem(kv_fmt, v_cache, slots[j] * v_stride + g * v_head_stride + i,
+                                     vs);
+            }
+            for (int i = 0; i < dim_v; i++) o[i] /= den;
+        }
+        free(logit);
+        free(slots);
+    }
+    return bad;
+}
