@@ -1,0 +1,188 @@
+/*
+ * sa.h -- C ABI of the index-selected sparse attention library for AMD MI355X (gfx950).
+ *
+ * The path: a lightweight indexer scores every visible history token of a query, Top-K keeps
+ * the K most relevant positions, and attention runs only over the key/value rows of those
+ * positions, read from a paged (blocked) KV cache.
+ *
+ * Pages cited (by title and section):
+ *   [SameDay]  "How the Ascend Computing Platform Achieves Same-Day Inference Adaptation for
+ *              Ultra-Large Sparse Models"
+ *   [Domestic] "Engineering Path for Day-0 Adaptation of Trillion-Scale Sparse Models on
+ *              Domestic AI Accelerators"
+ *   [CANN]     "Day0 Inference Support and Performance Optimization for Next-Gen Large Models on
+ *              Huawei Ascend CANN Architecture"
+ *   [GPUGuide] "Adapting GPU Software Stacks for Ultra-Large-Scale Sparse Attention Models:
+ *              A Day-0 Engineering Guide"
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked "device" are HIP device allocations; "host" pointers are read during the
+ *    call only. The caller owns every buffer; the library allocates no device memory.
+ *  - All work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and is
+ *    asynchronous: no entry point synchronizes the host with the device.
+ *  - Host-detectable errors (NULL pointers, sizes out of range, unsupported combinations, a
+ *    too-small workspace) return SA_ERR_INVALID / SA_ERR_UNSUPPORTED / SA_ERR_WORKSPACE and
+ *    enqueue nothing. A failed launch returns SA_ERR_HIP; sa_last_error() then holds the
+ *    message. Device-side contents (page ids, positions, lengths) are trusted: the host copies
+ *    of the context lengths must equal the device copies, page ids must be < num_pages and
+ *    selected positions must be visible to their query (see each call).
+ *  - Positions are logical token positions (int32) inside a sequence, never physical slots,
+ *    so an index set stays valid when pages move; the consumer translates position t to
+ *    slot page_table[seq][t / page_size] * page_size + t % page_size ([Domestic] §3.2:
+ *    block number plus in-block offset; [GPUGuide] §3.1: index format aligned with the
+ *    attention consumer).
+ *  - Query rows: sequence b owns rows q_indptr[b] .. q_indptr[b+1]-1, which are its last
+ *    q_len_b tokens (appended causally); row j of b sits at position
+ *    ctx_len_b - q_len_b + (j - q_indptr[b]) and sees positions 0..that position inclusive.
+ *    With q_indptr == NULL every sequence has exactly one row (decode) at ctx_len_b - 1.
+ *  - Calls are re-entrant; calls sharing one workspace must be ordered on one stream.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_VERSION 1
+
+typedef enum sa_status {
+    SA_OK = 0,
+    SA_ERR_INVALID = 1,     /* an argument violates a precondition; nothing enqueued */
+    SA_ERR_UNSUPPORTED = 2, /* valid, but no kernel exists for this shape/type; nothing enqueued */
+    SA_ERR_WORKSPACE = 3,   /* workspace NULL, misaligned or smaller than required */
+    SA_ERR_HIP = 4          /* a HIP runtime call failed; see sa_last_error() */
+} sa_status;
+
+typedef enum sa_dtype {
+    SA_BF16 = 0,     /* bfloat16 */
+    SA_FP8_E4M3 = 1  /* OCP E4M3 codes (max 448) times one fp32 scale per stored row */
+} sa_dtype;
+
+/* Sequences, their lengths and the page table of the blocked KV layout ([Domestic] §3.2;
+ * [SameDay] §3.1 and §3.2: fixed-size blocks directly indexable by the selection; [GPUGuide]
+ * §3.2: block location metadata). */
+typedef struct sa_batch {
+    int32_t num_seqs;             /* >= 1 */
+    int32_t page_size;            /* tokens per page: a power of two, 1..4096 */
+    int32_t pages_per_seq;        /* row stride of page_table; ctx_len <= pages_per_seq*page_size */
+    int32_t num_pages;            /* physical pages held by every cache passed with this batch */
+    const int32_t *page_table;    /* device [num_seqs][pages_per_seq]: logical -> physical page */
+    const int32_t *ctx_lens;      /* device [num_seqs]: tokens in each sequence (>= 0) */
+    const int32_t *ctx_lens_host; /* host   [num_seqs]: the same values (planning, validation) */
+    const int32_t *q_indptr;      /* device [num_seqs+1] query-row offsets, or NULL (decode) */
+    const int32_t *q_indptr_host; /* host copy of q_indptr; NULL exactly when q_indptr is NULL */
+} sa_batch;
+
+/* The lightweight indexer's cache ([CANN] §1 and §2.1). One key row of `dim` entries per token,
+ * shared by all indexer heads. Score of position t for a query row with indexer queries
+ * q_I[heads][dim] and head weights w[heads] (fp32 accumulation):
+ *     s[t] = sum_h w[h] * max(q_I[h] . k_I[t], 0)
+ * (relevance scoring with head-weight weighting; the pages leave the formula open and this
+ * library fixes it as written). For E4M3 keys, k_I[t] = code * key_scale[t]. */
+typedef struct sa_indexer {
+    int32_t heads;            /* H_I: 1..64 */
+    int32_t dim;              /* d_I: 64 or 128 */
+    sa_dtype key_dtype;       /* SA_BF16 or SA_FP8_E4M3 */
+    const void *keys;         /* device [num_pages][page_size][dim] */
+    const float *key_scale;   /* device [num_pages][page_size] for E4M3 keys, else NULL */
+    const void *pooled;       /* device bf16 [num_pages][dim]: one summary key per page for
+                                 two-level selection ([SameDay] §3.1: coarse filtering over
+                                 summaries already held in the cache), or NULL */
+} sa_indexer;
+
+/* The attention KV cache. One KV head (MQA/MLA style: every query head reads the same row).
+ * Row of slot s: K = k[s][0..dim_qk), V = v[s][0..dim_v), or, when v == NULL, V is the first
+ * dim_v entries of the K row (a latent row as in MLA). For E4M3 rows, value = code *
+ * scale[s] (one scale per row, used for K and V). */
+typedef struct sa_kv {
+    int32_t heads_q;          /* query heads: 1..128 */
+    int32_t heads_kv;         /* must be 1 */
+    int32_t dim_qk;           /* 576 (latent, v == NULL, dim_v 512) or 128 (dim_v 128) */
+    int32_t dim_v;            /* 512 or 128 */
+    sa_dtype dtype;           /* SA_BF16 or SA_FP8_E4M3 (E4M3 only with v == NULL) */
+    const void *k;            /* device [num_pages][page_size][dim_qk] */
+    const void *v;            /* device [num_pages][page_size][dim_v], or NULL (latent) */
+    const float *scale;       /* device [num_pages][page_size] for E4M3, else NULL */
+    float softmax_scale;      /* logits are softmax_scale * (q . K) */
+} sa_kv;
+
+/*
+ * sa_index_score -- indexer scores of every visible position, written to HBM (used by Prefill
+ * and by tests; the fused decode path never writes scores). "Scoring -- reduction" of
+ * [Domestic] §3.1; [CANN] §2.1.
+ *   q_idx  device bf16 [rows][heads][dim]   (rows = num_seqs, or q_indptr_host[num_seqs])
+ *   w      device fp32 [rows][heads]
+ *   scores device fp32 [rows][ld]: column t holds s[t] for t <= the row's position and -inf
+ *          for the remaining columns; ld >= (largest row position) + 1.
+ */
+sa_status sa_index_score(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                         const float *w, float *scores, int64_t ld, void *stream);
+
+/*
+ * sa_topk -- Top-K filtering ([Domestic] §3.1; [CANN] §1): for each query row, the k largest
+ * of scores[row][0 .. position] ordered by (score descending, position ascending; -0 equals
+ * +0), written in ascending position order and padded with -1 when fewer than k positions are
+ * visible. Radix selection, no sort. Scores must not be NaN.
+ *   scores device fp32 [rows][ld];  idx device int32 [rows][k];  1 <= k <= 16384.
+ */
+sa_status sa_topk(const sa_batch *batch, const float *scores, int64_t ld, int32_t k,
+                  int32_t *idx, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sa_sparse_attn -- attention of each query row over the rows of its selected positions only
+ * ([CANN] §1 and §2.1: the attention reads the KV "precisely according to the selected
+ * indices"; [Domestic] §3). For query head g: logits softmax_scale * q[g] . K(t) over the
+ * selected t, softmax in fp32, o[g] = sum p * V(t) / sum p; an empty selection gives 0.
+ *   q   device bf16 [rows][heads_q][dim_qk]
+ *   idx device int32 [rows][k]: positions in any order, -1 = unused; every other entry must
+ *       be visible to its row (not checked on the device).
+ *   out device bf16 [rows][heads_q][dim_v]
+ */
+sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
+                         const int32_t *idx, int32_t k, void *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
+ * sa_decode_step -- the fused Decode path ([CANN] §2.1: scoring, head weighting and Top-K in
+ * one composite operator reading the paged cache directly; [GPUGuide] §3.3: decode fuses
+ * index selection with attention to cut launches; [GPUGuide] §3.1 and [CANN] §2: no score
+ * write-back). One query row per sequence (batch->q_indptr must be NULL). Scores stay in
+ * on-chip memory; Top-K runs across the workgroups that share a sequence.
+ * With block_k > 0, selection is hierarchical ([SameDay] §3.1; [GPUGuide] §3.1): blocks
+ * (= pages) are scored from ix->pooled, the block_k best blocks are kept (ties -> lower
+ * block), and the token Top-K is taken among the visible tokens of the kept blocks.
+ *   q_idx device bf16 [num_seqs][ix->heads][ix->dim];  w device fp32 [num_seqs][ix->heads]
+ *   q     device bf16 [num_seqs][kv->heads_q][kv->dim_qk]
+ *   idx_out device int32 [num_seqs][k] (selected positions, ascending, -1 padded) or NULL
+ *   out   device bf16 [num_seqs][kv->heads_q][kv->dim_v]
+ */
+sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                         const void *q_idx, const float *w, const void *q, int32_t k,
+                         int32_t block_k, int32_t *idx_out, void *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Workspace bytes that every entry point above needs for this batch, cache shape, k and
+ * block_k (kv may be NULL when only indexer/Top-K calls use the workspace). */
+size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int32_t block_k);
+
+/* Zero-fills a workspace on `stream` (with a kernel). Required once before the first use of a
+ * workspace; every call that completes leaves the workspace ready for the next one. */
+sa_status sa_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* Synchronizes `stream` and reads the workspace's device error word: 0 = no device-side
+ * failure, otherwise a bitmask (1 = a cross-workgroup wait exceeded its spin limit). */
+sa_status sa_workspace_error(const void *workspace, int32_t *error_host, void *stream);
+
+const char *sa_status_string(sa_status status);
+const char *sa_last_error(void); /* message of the last SA_ERR_HIP on this thread */
+int32_t sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

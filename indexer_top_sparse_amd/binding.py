@@ -1,0 +1,184 @@
+"""Thin ctypes binding of ``libsa.so`` (the C ABI declared in include/sa.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels. PyTorch
+provides device memory and the current stream. There is no fallback: if the library is not
+built, or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa.so")
+
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_BF16, SA_FP8_E4M3 = 0, 1
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"sa status {status}: {message}")
+        self.status = status
+
+
+class sa_batch(C.Structure):
+    _fields_ = [("num_seqs", C.c_int32), ("page_size", C.c_int32),
+                ("pages_per_seq", C.c_int32), ("num_pages", C.c_int32),
+                ("page_table", C.c_void_p), ("ctx_lens", C.c_void_p),
+                ("ctx_lens_host", C.c_void_p), ("q_indptr", C.c_void_p),
+                ("q_indptr_host", C.c_void_p)]
+
+
+class sa_indexer(C.Structure):
+    _fields_ = [("heads", C.c_int32), ("dim", C.c_int32), ("key_dtype", C.c_int),
+                ("keys", C.c_void_p), ("key_scale", C.c_void_p), ("pooled", C.c_void_p)]
+
+
+class sa_kv(C.Structure):
+    _fields_ = [("heads_q", C.c_int32), ("heads_kv", C.c_int32), ("dim_qk", C.c_int32),
+                ("dim_v", C.c_int32), ("dtype", C.c_int), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("scale", C.c_void_p), ("softmax_scale", C.c_float)]
+
+
+_lib = None
+EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_decode_step", "sa_workspace_size",
+           "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
+           "sa_version")
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build()")
+    lib = C.CDLL(path)
+    P, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    pb, pi, pk = C.POINTER(sa_batch), C.POINTER(sa_indexer), C.POINTER(sa_kv)
+    lib.sa_index_score.argtypes = [pb, pi, P, P, P, i64, P]
+    lib.sa_topk.argtypes = [pb, P, i64, i32, P, P, sz, P]
+    lib.sa_sparse_attn.argtypes = [pb, pk, P, P, i32, P, P, sz, P]
+    lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
+    lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
+    lib.sa_workspace_size.restype = sz
+    lib.sa_workspace_init.argtypes = [P, sz, P]
+    lib.sa_workspace_error.argtypes = [P, C.POINTER(C.c_int32), P]
+    lib.sa_status_string.argtypes = [C.c_int]
+    lib.sa_status_string.restype = C.c_char_p
+    lib.sa_last_error.restype = C.c_char_p
+    lib.sa_version.restype = i32
+    for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_decode_step",
+               "sa_workspace_init", "sa_workspace_error"):
+        getattr(lib, fn).restype = C.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != SA_OK:
+        lib = load()
+        msg = lib.sa_last_error().decode() or lib.sa_status_string(status).decode()
+        raise SaError(status, msg)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+class Batch:
+    """Page table, lengths and query rows of one call (device tensors + host copies)."""
+
+    def __init__(self, page_table: torch.Tensor, ctx_lens: torch.Tensor, ctx_lens_host,
+                 page_size: int, num_pages: int, q_indptr: torch.Tensor | None = None,
+                 q_indptr_host=None):
+        self._pt = page_table
+        self._ctx = ctx_lens
+        self._ctx_host = (C.c_int32 * len(ctx_lens_host))(*[int(x) for x in ctx_lens_host])
+        self._qi = q_indptr
+        self._qi_host = None
+        if q_indptr is not None:
+            self._qi_host = (C.c_int32 * len(q_indptr_host))(*[int(x) for x in q_indptr_host])
+        self.s = sa_batch(len(ctx_lens_host), page_size, page_table.shape[1], num_pages,
+                          page_table.data_ptr(), ctx_lens.data_ptr(),
+                          C.cast(self._ctx_host, C.c_void_p),
+                          q_indptr.data_ptr() if q_indptr is not None else None,
+                          C.cast(self._qi_host, C.c_void_p) if self._qi_host is not None
+                          else None)
+
+
+def indexer_desc(heads, dim, keys, key_scale=None, pooled=None):
+    dt = SA_FP8_E4M3 if key_scale is not None else SA_BF16
+    return sa_indexer(heads, dim, dt, keys.data_ptr(),
+                      key_scale.data_ptr() if key_scale is not None else None,
+                      pooled.data_ptr() if pooled is not None else None)
+
+
+def kv_desc(heads_q, dim_qk, dim_v, k, v=None, scale=None, softmax_scale=1.0, heads_kv=1):
+    dt = SA_FP8_E4M3 if scale is not None else SA_BF16
+    return sa_kv(heads_q, heads_kv, dim_qk, dim_v, dt, k.data_ptr(),
+                 v.data_ptr() if v is not None else None,
+                 scale.data_ptr() if scale is not None else None, float(softmax_scale))
+
+
+def workspace_size(batch: Batch, kv: sa_kv | None, k: int, block_k: int = 0) -> int:
+    lib = load()
+    n = lib.sa_workspace_size(C.byref(batch.s), C.byref(kv) if kv is not None else None, k,
+                              block_k)
+    if n == 0:
+        _check(SA_ERR_INVALID)
+    return int(n)
+
+
+def workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _check(load().sa_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def workspace_error(ws: torch.Tensor, stream=None) -> int:
+    v = C.c_int32(0)
+    _check(load().sa_workspace_error(_ptr(ws), C.byref(v), _stream(stream)))
+    return int(v.value)
+
+
+def new_workspace(batch: Batch, kv: sa_kv | None, k: int, block_k: int = 0,
+                  device="cuda") -> torch.Tensor:
+    """Allocate (through torch) and zero-initialise a workspace for these shapes."""
+    n = workspace_size(batch, kv, k, block_k)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    workspace_init(ws)
+    return ws
+
+
+def index_score(batch: Batch, ix: sa_indexer, q_idx, w, scores, stream=None) -> None:
+    _check(load().sa_index_score(C.byref(batch.s), C.byref(ix), _ptr(q_idx), _ptr(w),
+                                 _ptr(scores), scores.shape[1], _stream(stream)))
+
+
+def topk(batch: Batch, scores, k: int, idx, ws=None, stream=None) -> None:
+    _check(load().sa_topk(C.byref(batch.s), _ptr(scores), scores.shape[1], k, _ptr(idx),
+                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def sparse_attn(batch: Batch, kv: sa_kv, q, idx, out, ws, stream=None) -> None:
+    _check(load().sa_sparse_attn(C.byref(batch.s), C.byref(kv), _ptr(q), _ptr(idx),
+                                 idx.shape[1], _ptr(out), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+
+
+def decode_step(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, out, ws,
+                block_k: int = 0, idx_out=None, stream=None) -> None:
+    _check(load().sa_decode_step(C.byref(batch.s), C.byref(ix), C.byref(kv), _ptr(q_idx),
+                                 _ptr(w), _ptr(q), k, block_k, _ptr(idx_out), _ptr(out),
+                                 _ptr(ws), ws.numel(), _stream(stream)))

@@ -1,0 +1,436 @@
+// C ABI of the library: argument validation (host only, nothing is enqueued on error),
+// workspace layout, launch planning and kernel launches. Declarations and the contract of
+// every entry point are in include/sa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/sa.h"
+#include "kernels.h"
+
+using namespace sa;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char *msg) {
+    g_last_error = msg;
+    return st;
+}
+
+sa_status hip_fail(hipError_t e, const char *where) {
+    g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+    return SA_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
+// Rows of a batch and the largest row position (host side).
+struct RowPlan {
+    int rows = 0;
+    int64_t max_pos = -1;
+};
+
+sa_status check_batch(const sa_batch *b, RowPlan *rp) {
+    if (!b) return fail(SA_ERR_INVALID, "batch is NULL");
+    if (b->num_seqs < 1) return fail(SA_ERR_INVALID, "num_seqs must be >= 1");
+    if (!is_pow2(b->page_size) || b->page_size > 4096)
+        return fail(SA_ERR_INVALID, "page_size must be a power of two in [1, 4096]");
+    if (b->pages_per_seq < 1 || b->num_pages < 1)
+        return fail(SA_ERR_INVALID, "pages_per_seq and num_pages must be >= 1");
+    if ((int64_t)b->num_pages * b->page_size > INT32_MAX)
+        return fail(SA_ERR_UNSUPPORTED, "num_pages * page_size must fit in int32");
+    if (!b->page_table || !b->ctx_lens || !b->ctx_lens_host)
+        return fail(SA_ERR_INVALID, "page_table, ctx_lens and ctx_lens_host are required");
+    if ((b->q_indptr == nullptr) != (b->q_indptr_host == nullptr))
+        return fail(SA_ERR_INVALID, "q_indptr and q_indptr_host must both be set or both NULL");
+    const int64_t cap = (int64_t)b->pages_per_seq * b->page_size;
+    RowPlan p;
+    for (int s = 0; s < b->num_seqs; ++s) {
+        const int n = b->ctx_lens_host[s];
+        if (n < 0 || n > cap) return fail(SA_ERR_INVALID, "ctx_len outside [0, pages_per_seq*page_size]");
+        int ql = 1;
+        if (b->q_indptr_host) {
+            if (s == 0 && b->q_indptr_host[0] != 0) return fail(SA_ERR_INVALID, "q_indptr[0] != 0");
+            ql = b->q_indptr_host[s + 1] - b->q_indptr_host[s];
+            if (ql < 0 || ql > n) return fail(SA_ERR_INVALID, "query rows must be 0..ctx_len per sequence");
+        }
+        p.rows += ql;
+        if (ql > 0) p.max_pos = std::max<int64_t>(p.max_pos, n - 1);
+        else if (!b->q_indptr_host) p.max_pos = std::max<int64_t>(p.max_pos, n - 1);
+    }
+    *rp = p;
+    return SA_OK;
+}
+
+sa_status check_indexer(const sa_indexer *ix) {
+    if (!ix) return fail(SA_ERR_INVALID, "indexer descriptor is NULL");
+    if (ix->heads < 1 || ix->heads > 64) return fail(SA_ERR_UNSUPPORTED, "indexer heads must be 1..64");
+    if (ix->dim != 64 && ix->dim != 128) return fail(SA_ERR_UNSUPPORTED, "indexer dim must be 64 or 128");
+    if (ix->key_dtype != SA_BF16 && ix->key_dtype != SA_FP8_E4M3)
+        return fail(SA_ERR_INVALID, "unknown indexer key dtype");
+    if (!ix->keys || !aligned16(ix->keys)) return fail(SA_ERR_INVALID, "indexer keys NULL or not 16-byte aligned");
+    if ((ix->key_dtype == SA_FP8_E4M3) != (ix->key_scale != nullptr))
+        return fail(SA_ERR_INVALID, "key_scale must be given exactly for E4M3 keys");
+    if (ix->pooled && !aligned16(ix->pooled)) return fail(SA_ERR_INVALID, "pooled not 16-byte aligned");
+    return SA_OK;
+}
+
+sa_status check_kv(const sa_kv *kv) {
+    if (!kv) return fail(SA_ERR_INVALID, "kv descriptor is NULL");
+    if (kv->heads_q < 1 || kv->heads_q > 128) return fail(SA_ERR_UNSUPPORTED, "heads_q must be 1..128");
+    if (kv->heads_kv != 1) return fail(SA_ERR_UNSUPPORTED, "heads_kv must be 1");
+    const bool latent = kv->dim_qk == 576 && kv->dim_v == 512 && kv->v == nullptr;
+    const bool small = kv->dim_qk == 128 && kv->dim_v == 128;
+    if (!latent && !small) return fail(SA_ERR_UNSUPPORTED, "(dim_qk, dim_v) must be (576, 512) latent or (128, 128)");
+    if (kv->dtype != SA_BF16 && kv->dtype != SA_FP8_E4M3) return fail(SA_ERR_INVALID, "unknown kv dtype");
+    if (kv->dtype == SA_FP8_E4M3 && (!latent || !kv->scale))
+        return fail(SA_ERR_UNSUPPORTED, "E4M3 KV needs latent rows (v == NULL) and a scale array");
+    if (kv->dtype == SA_BF16 && kv->scale) return fail(SA_ERR_INVALID, "scale given for bf16 KV");
+    if (!kv->k || !aligned16(kv->k) || (kv->v && !aligned16(kv->v)))
+        return fail(SA_ERR_INVALID, "k/v NULL or not 16-byte aligned");
+    if (!(kv->softmax_scale > 0.f) || kv->softmax_scale > 1e30f)
+        return fail(SA_ERR_INVALID, "softmax_scale must be a positive finite float");
+    return SA_OK;
+}
+
+int attn_splits(int rows, int k, int heads_q) {
+    const int target = 512;  // workgroups: two rounds over 256 CUs
+    const int per_split = std::max(rows, 1) * attn_hgroups(heads_q);
+    int s = std::max(1, (target + per_split - 1) / per_split);
+    s = std::min(s, std::max(1, (k + 31) / 32));
+    return s;
+}
+int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, part_o = 0, part_ml = 0, total = 0;
+};
+
+WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int block_k) {
+    WsLayout L;
+    size_t off = 0;
+    L.err = off;
+    off += 256;
+    L.zero = off;  // stays zero: source of empty gathered rows
+    off += 2048;
+    L.sync = off;
+    off = align256(off + sizeof(SelSync) * (size_t)b->num_seqs);
+    L.blocks = off;
+    off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(block_k, 0));
+    L.idx = off;
+    off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(k, 0));
+    if (kv) {
+        const int rmax = std::max(rows, b->num_seqs);
+        // the split count only grows as rows shrink; size for the larger of the two
+        const int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
+        L.part_o = off;
+        off = align256(off + sizeof(float) * (size_t)rmax * s * kv->heads_q * kv->dim_v);
+        L.part_ml = off;
+        off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * kv->heads_q);
+    }
+    L.total = off;
+    return L;
+}
+
+sa_status check_ws(void *ws, size_t bytes, size_t need) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u))
+        return fail(SA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+    if (bytes < need) return fail(SA_ERR_WORKSPACE, "workspace smaller than sa_workspace_size()");
+    return SA_OK;
+}
+
+int device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        int n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus = n;
+    }
+    return cus;
+}
+
+// Co-resident workgroups per CU for a kernel (cached per kernel and LDS size).
+int occupancy(void *kern, int threads, size_t lds) {
+    struct Entry { void *k; size_t lds; int occ; };
+    static Entry cache[64];
+    static int n = 0;
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+        if (cache[i].k == kern && cache[i].lds == lds) return cache[i].occ;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(kern),
+                                                     threads, lds) != hipSuccess)
+        return -1;
+    if (n < 64) cache[n++] = Entry{kern, lds, occ};
+    return occ;
+}
+
+int ncand_host(int mode, int ctx, int page_size, int block_k) {
+    if (mode == 0) return ctx;
+    const int nblk = (ctx + page_size - 1) / page_size;
+    if (mode == 1) return nblk;
+    return std::min(block_k, nblk) * page_size;
+}
+
+// Cooperative launch of the fused selection for one candidate mode.
+sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
+                     int mode, int k, int block_k, const int32_t *blocks, int32_t *idx_out,
+                     uint8_t *ws, const WsLayout &L, hipStream_t st) {
+    const bool fp8 = mode != 1 && ix->key_dtype == SA_FP8_E4M3;
+    void *kern = decode_select_kernel(ix->dim, ix->heads, fp8, mode);
+    const int threads = 512;
+    const int64_t total = [&] {
+        int64_t t = 0;
+        for (int s = 0; s < b->num_seqs; ++s)
+            t += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+        return t;
+    }();
+    const int cus = device_cus();
+    const char *env = getenv("SA_SELECT_CHUNK");
+    int chunk = env ? std::max(64, atoi(env) / 64 * 64)
+                    : std::max<int>(64, (int)((total / ((int64_t)cus * 4) + 63) / 64 * 64));
+    for (;;) {
+        if (chunk > 32768) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
+        const size_t lds = (size_t)chunk * 4;
+        const int occ = occupancy(kern, threads, lds);
+        if (occ < 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
+        const int64_t cap = (int64_t)occ * cus;
+        int64_t groups = 0;
+        int gmax = 0;
+        for (int s = 0; s < b->num_seqs; ++s) {
+            const int nc = ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+            const int g = std::max(1, (nc + chunk - 1) / chunk);
+            groups += g;
+            gmax = std::max(gmax, g);
+        }
+        if (occ > 0 && groups <= cap && gmax <= kMaxGroupsPerSeq) {
+            SelectArgs a;
+            a.num_seqs = b->num_seqs;
+            a.lp = log2i(b->page_size);
+            a.pages_per_seq = b->pages_per_seq;
+            a.heads = ix->heads;
+            a.chunk = chunk;
+            a.k = k;
+            a.block_k = block_k;
+            a.page_table = b->page_table;
+            a.ctx_lens = b->ctx_lens;
+            a.blocks = blocks;
+            a.q_idx = static_cast<const uint16_t *>(q_idx);
+            a.w = w;
+            a.keys = static_cast<const uint8_t *>(mode == 1 ? ix->pooled : ix->keys);
+            a.key_scale = ix->key_scale;
+            a.idx_out = idx_out;
+            a.sync = reinterpret_cast<SelSync *>(ws + L.sync);
+            a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+            void *args[] = {&a};
+            hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)groups), dim3(threads),
+                                                      args, (unsigned)lds, st);
+            if (e != hipSuccess) return hip_fail(e, "cooperative selection launch");
+            return SA_OK;
+        }
+        chunk = std::max(chunk + 64, (chunk + chunk / 8 + 63) / 64 * 64);
+    }
+}
+
+sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
+                   const int32_t *idx, int k, void *out, uint8_t *ws, const WsLayout &L,
+                   hipStream_t st) {
+    AttnArgs a;
+    a.num_seqs = b->num_seqs;
+    a.lp = log2i(b->page_size);
+    a.pages_per_seq = b->pages_per_seq;
+    a.heads_q = kv->heads_q;
+    a.k = k;
+    a.rows = rows;
+    a.splits = attn_splits(rows, k, kv->heads_q);
+    a.hgroups = attn_hgroups(kv->heads_q);
+    a.split_len = split_len(k, a.splits);
+    a.page_table = b->page_table;
+    a.ctx_lens = b->ctx_lens;
+    a.q_indptr = b->q_indptr;
+    a.q = static_cast<const uint16_t *>(q);
+    a.idx = idx;
+    a.kc = static_cast<const uint8_t *>(kv->k);
+    a.vc = static_cast<const uint8_t *>(kv->v);
+    a.kv_scale = kv->scale;
+    a.zero_row = ws + L.zero;
+    a.scale_log2 = kv->softmax_scale * 1.4426950408889634f;
+    a.out = static_cast<uint16_t *>(out);
+    a.part_o = reinterpret_cast<float *>(ws + L.part_o);
+    a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+    if (rows == 0) return SA_OK;
+    hipError_t e = launch_sparse_attn(a, kv->dim_qk, kv->dim_v, kv->v != nullptr,
+                                      kv->dtype == SA_FP8_E4M3, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_version(void) { return SA_VERSION; }
+
+const char *sa_last_error(void) { return g_last_error.c_str(); }
+
+const char *sa_status_string(sa_status s) {
+    switch (s) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported shape or type";
+        case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int32_t block_k) {
+    RowPlan rp;
+    if (check_batch(batch, &rp) != SA_OK) return 0;
+    return ws_layout(batch, rp.rows, kv, k, block_k).total;
+}
+
+sa_status sa_workspace_init(void *ws, size_t bytes, void *stream) {
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) || bytes < 256)
+        return fail(SA_ERR_WORKSPACE, "workspace NULL, misaligned or smaller than 256 bytes");
+    hipError_t e = launch_zero(ws, bytes & ~(size_t)15, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "workspace zero-fill");
+    return SA_OK;
+}
+
+sa_status sa_workspace_error(const void *ws, int32_t *error_host, void *stream) {
+    if (!ws || !error_host) return fail(SA_ERR_INVALID, "workspace or error_host is NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(error_host, ws, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "reading the workspace error word");
+    return SA_OK;
+}
+
+sa_status sa_index_score(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                         const float *w, float *scores, int64_t ld, void *stream) {
+    RowPlan rp;
+    sa_status st = check_batch(batch, &rp);
+    if (st != SA_OK) return st;
+    if ((st = check_indexer(ix)) != SA_OK) return st;
+    if (!q_idx || !aligned16(q_idx) || !w || !scores)
+        return fail(SA_ERR_INVALID, "q_idx (16-byte aligned), w and scores are required");
+    if (ld < std::max<int64_t>(rp.max_pos + 1, 1)) return fail(SA_ERR_INVALID, "ld smaller than the largest row position + 1");
+    if (rp.rows == 0) return SA_OK;
+    ScoreArgs a;
+    a.num_seqs = batch->num_seqs;
+    a.lp = log2i(batch->page_size);
+    a.pages_per_seq = batch->pages_per_seq;
+    a.heads = ix->heads;
+    a.page_table = batch->page_table;
+    a.ctx_lens = batch->ctx_lens;
+    a.q_indptr = batch->q_indptr;
+    a.q_idx = static_cast<const uint16_t *>(q_idx);
+    a.w = w;
+    a.keys = static_cast<const uint8_t *>(ix->keys);
+    a.key_scale = ix->key_scale;
+    a.scores = scores;
+    a.ld = ld;
+    hipError_t e = launch_index_score(a, ix->dim, ix->heads, ix->key_dtype == SA_FP8_E4M3,
+                                      rp.rows, ld, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "index score launch");
+    return SA_OK;
+}
+
+sa_status sa_topk(const sa_batch *batch, const float *scores, int64_t ld, int32_t k,
+                  int32_t *idx, void *ws, size_t ws_bytes, void *stream) {
+    RowPlan rp;
+    sa_status st = check_batch(batch, &rp);
+    if (st != SA_OK) return st;
+    (void)ws;
+    (void)ws_bytes;
+    if (!scores || !idx) return fail(SA_ERR_INVALID, "scores and idx are required");
+    if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
+    if (ld < 1) return fail(SA_ERR_INVALID, "ld must be >= 1");
+    if (rp.rows == 0) return SA_OK;
+    TopkArgs a;
+    a.num_seqs = batch->num_seqs;
+    a.k = k;
+    a.ctx_lens = batch->ctx_lens;
+    a.q_indptr = batch->q_indptr;
+    a.scores = scores;
+    a.ld = ld;
+    a.idx = idx;
+    hipError_t e = launch_topk_rows(a, rp.rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return SA_OK;
+}
+
+sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
+                         const int32_t *idx, int32_t k, void *out, void *ws, size_t ws_bytes,
+                         void *stream) {
+    RowPlan rp;
+    sa_status st = check_batch(batch, &rp);
+    if (st != SA_OK) return st;
+    if ((st = check_kv(kv)) != SA_OK) return st;
+    if (!q || !aligned16(q) || !idx || !out || (reinterpret_cast<uintptr_t>(out) & 7u))
+        return fail(SA_ERR_INVALID, "q (16-byte aligned), idx and out (8-byte aligned) are required");
+    if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
+    const WsLayout L = ws_layout(batch, rp.rows, kv, k, 0);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
+    return run_attn(batch, rp.rows, kv, q, idx, k, out, static_cast<uint8_t *>(ws), L,
+                    static_cast<hipStream_t>(stream));
+}
+
+sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                         const void *q_idx, const float *w, const void *q, int32_t k,
+                         int32_t block_k, int32_t *idx_out, void *out, void *ws,
+                         size_t ws_bytes, void *stream) {
+    RowPlan rp;
+    sa_status st = check_batch(batch, &rp);
+    if (st != SA_OK) return st;
+    if (batch->q_indptr) return fail(SA_ERR_INVALID, "sa_decode_step takes one query row per sequence (q_indptr must be NULL)");
+    if ((st = check_indexer(ix)) != SA_OK) return st;
+    if ((st = check_kv(kv)) != SA_OK) return st;
+    if (!q_idx || !aligned16(q_idx) || !w || !q || !aligned16(q) || !out ||
+        (reinterpret_cast<uintptr_t>(out) & 7u))
+        return fail(SA_ERR_INVALID, "q_idx, q (16-byte aligned), w and out are required");
+    if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
+    if (block_k < 0 || block_k > 65536) return fail(SA_ERR_INVALID, "block_k must be in [0, 65536]");
+    if (block_k > 0 && !ix->pooled) return fail(SA_ERR_INVALID, "two-level selection needs ix->pooled");
+    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
+    if (block_k > 0) {
+        int32_t *blocks = reinterpret_cast<int32_t *>(wsb + L.blocks);
+        if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks, wsb, L,
+                             hs)) != SA_OK)
+            return st;
+        if ((st = run_select(batch, ix, q_idx, w, 2, k, block_k, blocks, idx, wsb, L, hs)) !=
+            SA_OK)
+            return st;
+    } else {
+        if ((st = run_select(batch, ix, q_idx, w, 0, k, 0, nullptr, idx, wsb, L, hs)) != SA_OK)
+            return st;
+    }
+    return run_attn(batch, rp.rows, kv, q, idx, k, out, wsb, L, hs);
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// Device helpers shared by the gfx950 kernels: MFMA wrappers, bf16 packing, order-preserving
+// float keys, block-wide scans and the per-sequence cross-workgroup barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define SA_LDS __attribute__((address_space(3)))
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l holds
+// A[l%16][8*(l/16) + e], B[8*(l/16) + e][l%16] (e = 0..7) and D[4*(l/16) + i][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32). Lane l holds A[l%32][8*(l/32) + e], B[8*(l/32) + e][l%32]
+// and D[8*j + 4*(l/32) + i][l%32] in register 4*j + i.
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Four E4M3 codes (one 32-bit word, byte 0 first) -> four bf16 (two words). E4M3 values are
+// exact in fp32 and in bf16, so the conversion through fp32 is exact.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t codes) {
+    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+    u32x2 r;
+    r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
+    r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
+    return r;
+}
+
+// Order-preserving map float -> uint32 (larger float <=> larger key). -0 maps like +0. Key 0
+// only arises from NaN patterns, so it doubles as the "no candidate" marker.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        uint32_t t = __shfl_up(v, o, 64);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Exclusive prefix sum across the block (NT threads); `scratch` needs NT/64 + 1 words.
+// Returns the exclusive prefix and stores the block total in *total. Contains barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratch,
+                                                    uint32_t *total) {
+    constexpr int NWV = NT / 64;
+    const uint32_t incl = wave_incl_scan(v);
+    __syncthreads();
+    if (lane_id() == 63) scratch[wave_id()] = incl;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+        const uint32_t s = scratch[i];
+        base += (i < wave_id()) ? s : 0u;
+        tot += s;
+    }
+    *total = tot;
+    return base + incl - v;
+}
+
+// ---------------------------------------------------------------- cross-workgroup barrier
+// Workgroups that share one sequence meet here. Co-residency of all of them is guaranteed by
+// the cooperative launch. `count` returns to 0 after every barrier; `gen` only grows. A
+// bounded spin keeps every wave finite: on expiry bit 0 of *err is set and the call returns
+// false (results of that launch are then undefined, and the host can read the flag).
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+__device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, uint32_t n,
+                                              uint32_t *err) {
+    __shared__ int s_ok;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __threadfence();
+        const uint32_t arrived =
+            __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (arrived == n - 1) {
+            __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kSpinLimit) {
+                    __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    ok = 0;
+                    break;
+                }
+            }
+        }
+        __threadfence();
+        s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void add_agent(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte global load that the compiler keeps as one dwordx4.
+__device__ __forceinline__ u32x4 ldg16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+}  // namespace sa

@@ -1,0 +1,512 @@
+// Lightweight indexer on gfx950: page-table-driven key stream, 64-head dot products on
+// MFMA, ReLU + head-weighted reduction in registers, and (decode) an exact radix Top-K across
+// the workgroups of a sequence with the scores kept in LDS.
+//
+// Pages cited: "Day0 Inference Support and Performance Optimization for Next-Gen Large Models on
+// Huawei Ascend CANN Architecture" (CANN) §1, §2.1; "Engineering Path for Day-0 Adaptation of
+// Trillion-Scale Sparse Models on Domestic AI Accelerators" (Domestic) §3.1-§3.3; "How the
+// Ascend Computing Platform Achieves Same-Day Inference Adaptation for Ultra-Large Sparse
+// Models" (SameDay) §3.1; "Adapting GPU Software Stacks for Ultra-Large-Scale Sparse Attention
+// Models: A Day-0 Engineering Guide" (GPUGuide) §3.1-§3.3.
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+// Candidate sources of the selection.
+//   kTokens:     candidate i is token position i; key row = slot of i.
+//   kBlocks:     candidate j is block (page) j; key row = its physical page in the pooled
+//                summary table (SameDay §3.1 coarse filtering over cached summaries).
+//   kCandidates: candidate i is token (blocks[i / P] * P + i % P) of a kept block (fine stage).
+enum { kTokens = 0, kBlocks = 1, kCandidates = 2 };
+
+struct SeqCtx {
+    int seq;
+    int ctx;
+    int ncand;
+    const int32_t *pt;
+    const int32_t *blocks;
+};
+
+__device__ __forceinline__ int ncand_of(int mode, int ctx, int lp, int block_k) {
+    if (mode == kTokens) return ctx;
+    const int nblk = (ctx + (1 << lp) - 1) >> lp;
+    if (mode == kBlocks) return nblk;
+    return min(block_k, nblk) << lp;
+}
+
+// Map candidate i to (logical position, key row); row < 0 when the candidate is not visible.
+template <int MODE>
+__device__ __forceinline__ void cand_row(const SeqCtx &s, int i, int lp, int &pos, int64_t &row) {
+    const int P = 1 << lp;
+    if (MODE == kTokens) {
+        pos = i;
+        row = (int64_t)s.pt[i >> lp] * P + (i & (P - 1));
+    } else if (MODE == kBlocks) {
+        pos = i;
+        row = s.pt[i];
+    } else {
+        const int blk = s.blocks[i >> lp];
+        pos = blk * P + (i & (P - 1));
+        row = (blk >= 0 && pos < s.ctx) ? (int64_t)s.pt[blk] * P + (i & (P - 1)) : -1;
+        if (blk < 0) pos = -1;
+    }
+}
+
+// Indexer query fragments for one query row: A operands of the 16x16x32 MFMA for HT head
+// tiles of 16 heads and KS k-steps of 32 entries. For E4M3 keys the d ordering inside each
+// pair of k-steps is permuted so that a lane's 16 key bytes are contiguous; the query
+// fragment follows the same order (the dot product does not depend on it).
+template <int DIM, int HT, bool FP8>
+struct IdxQuery {
+    static constexpr int KS = DIM / 32;
+    u32x4 a[HT][KS];
+    float w[HT][4];
+
+    __device__ __forceinline__ static int d_of(int s, int g) {
+        // first entry of the 8 consecutive d's this lane group holds at k-step s
+        return FP8 ? (64 * (s >> 1) + 16 * g + 8 * (s & 1)) : (32 * s + 8 * g);
+    }
+
+    __device__ __forceinline__ void load(const uint16_t *q_row, const float *w_row, int heads) {
+        const int l = lane_id(), g = l >> 4;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int h = 16 * ht + (l & 15);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (h < heads) v = ldg16(q_row + (size_t)h * DIM + d_of(s, g));
+                a[ht][s] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hh = 16 * ht + 4 * g + i;
+                w[ht][i] = hh < heads ? w_row[hh] : 0.f;
+            }
+        }
+    }
+};
+
+// Raw key fragment of one 16-candidate tile for one lane: the lane's token is l % 16, and it
+// holds KS k-steps of 8 bf16 (or, for E4M3, KS/2 chunks of 16 codes).
+template <int DIM, bool FP8>
+struct KeyFrag {
+    static constexpr int NV = FP8 ? DIM / 32 : DIM / 16 / 2;  // 16-byte loads per lane
+    u32x4 v[FP8 ? DIM / 64 : DIM / 32];
+};
+
+template <int DIM, bool FP8>
+__device__ __forceinline__ void load_key_frag(KeyFrag<DIM, FP8> &f, const uint8_t *keys,
+                                              int64_t row) {
+    const int g = lane_id() >> 4;
+    constexpr int RB = FP8 ? DIM : DIM * 2;  // bytes per key row
+    const uint8_t *p = keys + row * RB;
+    if (FP8) {
+#pragma unroll
+        for (int c = 0; c < DIM / 64; ++c) f.v[c] = ldg16(p + 64 * c + 16 * g);
+    } else {
+#pragma unroll
+        for (int s = 0; s < DIM / 32; ++s) f.v[s] = ldg16(p + 64 * s + 16 * g);
+    }
+}
+
+// Score of the lane's candidate (lane l % 16; every lane of the 4 groups gets the same value).
+template <int DIM, int HT, bool FP8>
+__device__ __forceinline__ float score_tile(const IdxQuery<DIM, HT, FP8> &q,
+                                            const KeyFrag<DIM, FP8> &f) {
+    constexpr int KS = DIM / 32;
+    f32x4 acc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 b;
+        if (FP8) {
+            const u32x4 raw = f.v[s >> 1];
+            const int base = (s & 1) * 2;
+            const u32x2 lo = e4m3x4_to_bf16(raw[base]);
+            const u32x2 hi = e4m3x4_to_bf16(raw[base + 1]);
+            b = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            b = f.v[s];
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(q.a[ht][s], b, acc[ht]);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(q.w[ht][i], fmaxf(acc[ht][i], 0.f), part);
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    return part;
+}
+
+// ============================================================== scores to HBM (sa_index_score)
+// Grid: (row, chunk of 1024 candidates). 4 waves; each wave walks 16-token tiles.
+constexpr int kScoreChunk = 1024;
+
+template <int DIM, int HT, bool FP8>
+__global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+    const int row = blockIdx.y;
+    int seq, qoff, qlen;
+    row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
+    const int ctx = a.ctx_lens[seq];
+    const int nvis = ctx - qlen + qoff + 1;  // positions 0 .. row position
+    const int64_t c0 = (int64_t)blockIdx.x * kScoreChunk;
+    float *out = a.scores + (int64_t)row * a.ld;
+    for (int64_t t = c0 + threadIdx.x; t < min(c0 + kScoreChunk, a.ld); t += 256)
+        if (t >= nvis) out[t] = -__builtin_inff();
+    const int c1 = (int)min(c0 + kScoreChunk, (int64_t)nvis);
+    if (c1 <= c0) return;
+
+    IdxQuery<DIM, HT, FP8> q;
+    q.load(a.q_idx + (size_t)row * a.heads * DIM, a.w + (size_t)row * a.heads, a.heads);
+    SeqCtx s{seq, ctx, ctx, a.page_table + (int64_t)seq * a.pages_per_seq, nullptr};
+    const int l = lane_id();
+    const int ntiles = (c1 - (int)c0 + 15) >> 4;
+    for (int tt = wave_id(); tt < ntiles; tt += 4) {
+        int i = (int)c0 + 16 * tt + (l & 15);
+        const bool valid = i < c1;
+        if (!valid) i = (int)c0;
+        int pos;
+        int64_t krow;
+        cand_row<kTokens>(s, i, a.lp, pos, krow);
+        KeyFrag<DIM, FP8> f;
+        load_key_frag<DIM, FP8>(f, a.keys, krow);
+        float sc = score_tile<DIM, HT, FP8>(q, f);
+        if (FP8) sc *= a.key_scale[krow];
+        if (valid && l < 16) out[i] = sc;
+    }
+}
+
+// ================================================================ decode selection (fused)
+// One workgroup per chunk of a sequence's candidates; all chunks of all sequences are
+// co-resident (cooperative launch). Scores never leave LDS: they become order-preserving keys
+// and an exact radix select runs over the sequence with per-pass global histograms and a
+// barrier per pass. Selected candidates are written in ascending position order; ties at the
+// threshold go to the lower positions.
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kHistBins = 2048;
+constexpr int kPre = 2;  // key tiles in flight per wave
+
+struct SelShared {
+    uint32_t hist[kHistBins];
+    uint32_t scan[kSelWaves + 1];
+    uint32_t res[8];
+    uint32_t grp[2];
+};
+
+template <int DIM, int HT, bool FP8, int MODE>
+__global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
+    extern __shared__ uint32_t s_key[];  // [chunk]
+    __shared__ SelShared sh;
+    const int tid = threadIdx.x, l = lane_id();
+
+    // ---- locate this workgroup's (sequence, chunk): chunk counts prefix over sequences
+    if (tid < 64) {
+        uint32_t base = 0;
+        int found_seq = -1, found_chunk = 0, found_G = 0;
+        for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+            const int b = b0 + l;
+            uint32_t nchunks = 0;
+            if (b < a.num_seqs) {
+                const int nc = ncand_of(MODE, a.ctx_lens[b], a.lp, a.block_k);
+                nchunks = max(1, (nc + a.chunk - 1) / a.chunk);
+            }
+            const uint32_t incl = wave_incl_scan(nchunks);
+            const uint32_t excl = base + incl - nchunks;
+            if (b < a.num_seqs && blockIdx.x >= excl && blockIdx.x < excl + nchunks) {
+                found_seq = b;
+                found_chunk = blockIdx.x - excl;
+                found_G = nchunks;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+        // exactly one lane (over all iterations) found it
+        const uint64_t m = __ballot(found_seq >= 0);
+        const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        const int fs = __shfl(found_seq, src, 64);
+        const int fc = __shfl(found_chunk, src, 64);
+        const int fg = __shfl(found_G, src, 64);
+        if (tid == 0) {
+            sh.res[0] = m ? fs : 0xFFFFFFFFu;
+            sh.res[1] = fc;
+            sh.res[2] = fg;
+        }
+    }
+    __syncthreads();
+    if (sh.res[0] == 0xFFFFFFFFu) return;  // grid padding (never co-waited on)
+    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2];
+    SeqCtx s;
+    s.seq = seq;
+    s.ctx = a.ctx_lens[seq];
+    s.ncand = ncand_of(MODE, s.ctx, a.lp, a.block_k);
+    s.pt = a.page_table + (int64_t)seq * a.pages_per_seq;
+    s.blocks = MODE == kCandidates ? a.blocks + (int64_t)seq * a.block_k : nullptr;
+    const int c0 = chunk * a.chunk;
+    const int c1 = min(c0 + a.chunk, s.ncand);
+    const int cnt = max(0, c1 - c0);
+
+    // ---- scores of this chunk -> LDS keys (0 = not a candidate)
+    if (cnt > 0) {
+        IdxQuery<DIM, HT, FP8> q;
+        q.load(a.q_idx + (size_t)seq * a.heads * DIM, a.w + (size_t)seq * a.heads, a.heads);
+        const int ntiles = (cnt + 15) >> 4;
+        const int w = wave_id();
+        const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
+        KeyFrag<DIM, FP8> f[kPre];
+        int64_t rows[kPre];
+        int poss[kPre];
+        auto issue = [&](int slot, int k) {
+            const int tt = w + k * kSelWaves;
+            int i = c0 + 16 * tt + (l & 15);
+            if (k >= my_tiles || i >= c1) i = c0;
+            int pos;
+            int64_t row;
+            cand_row<MODE>(s, i, a.lp, pos, row);
+            poss[slot] = pos;
+            rows[slot] = row;
+            load_key_frag<DIM, FP8>(f[slot], a.keys, row < 0 ? 0 : row);
+        };
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) issue(k, k);
+        for (int k0 = 0; k0 < my_tiles; k0 += kPre) {
+#pragma unroll
+            for (int j = 0; j < kPre; ++j) {
+                const int k = k0 + j;
+                if (k < my_tiles) {
+                    const int tt = w + k * kSelWaves;
+                    const int li = 16 * tt + (l & 15);
+                    float sc = score_tile<DIM, HT, FP8>(q, f[j]);
+                    const int64_t row = rows[j];
+                    if (FP8 && row >= 0) sc *= a.key_scale[row];
+                    const bool ok = (c0 + li < c1) && row >= 0;
+                    if (l < 16 && c0 + li < c1) s_key[li] = ok ? float_key(sc) : 0u;
+                    issue(j, k + kPre);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- radix select over the sequence
+    SelSync *ss = a.sync + seq;
+    uint32_t prefix = 0;
+    int pbits = 0;
+    uint32_t need = 0, total = 0;
+    bool exact = false;  // every candidate in the threshold bin is selected
+    bool ok = true;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int bits = pass < 2 ? 11 : 10;
+        const int shift = 32 - pbits - bits;
+        const int nb = 1 << bits;
+        for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < cnt; i += kSelThreads) {
+            const uint32_t k = s_key[i];
+            if (k == 0u) continue;
+            if (pbits && (k >> (32 - pbits)) != prefix) continue;
+            atomicAdd(&sh.hist[(k >> shift) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t *gh = ss->hist[pass];
+        for (int i = tid; i < nb; i += kSelThreads)
+            if (sh.hist[i]) add_agent(&gh[i], sh.hist[i]);
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t)
+        uint32_t hv[4];
+        uint32_t csum = 0;
+        const int top = nb - 4 * tid - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = top - j;
+            hv[j] = b >= 0 ? ld_agent(&gh[b]) : 0u;
+            csum += hv[j];
+        }
+        uint32_t tot;
+        const uint32_t above0 = block_excl_scan<kSelThreads>(csum, sh.scan, &tot);
+        if (pass == 0) {
+            total = tot;
+            need = min((uint32_t)a.k, tot);
+        }
+        if (need == 0u) break;
+        if (tid == 0) sh.res[3] = 0xFFFFFFFFu;
+        __syncthreads();
+        uint32_t run = above0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (run < need && run + hv[j] >= need) {
+                sh.res[3] = (uint32_t)(top - j);
+                sh.res[4] = run;
+                sh.res[5] = hv[j];
+            }
+            run += hv[j];
+        }
+        __syncthreads();
+        const uint32_t T = sh.res[3];
+        need -= sh.res[4];
+        prefix = (prefix << bits) | T;
+        pbits += bits;
+        if (sh.res[5] == need) {
+            exact = true;
+            break;
+        }
+    }
+
+    // ---- per-workgroup counts -> global offsets
+    const int K = a.k;
+    int32_t *out = a.idx_out + (int64_t)seq * K;
+    const uint32_t k_eff = min((uint32_t)K, total);
+    if (k_eff > 0) {
+        const int sh_bits = 32 - pbits;
+        uint32_t above = 0, eq = 0;
+        for (int i = tid; i < cnt; i += kSelThreads) {
+            const uint32_t k = s_key[i];
+            if (k == 0u) continue;
+            const uint32_t p = k >> sh_bits;
+            above += p > prefix;
+            eq += p == prefix;
+        }
+        uint32_t tmp;
+        above = wave_sum(above);
+        eq = wave_sum(eq);
+        __syncthreads();
+        if (l == 0) {
+            sh.scan[wave_id()] = above;
+            sh.hist[wave_id()] = eq;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t A = 0, Eq = 0;
+            for (int i = 0; i < kSelWaves; ++i) {
+                A += sh.scan[i];
+                Eq += sh.hist[i];
+            }
+            st_agent(&ss->cnt[chunk][0], A);
+            st_agent(&ss->cnt[chunk][1], Eq);
+        }
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        // prefix over the earlier workgroups of this sequence (chunk order = position order);
+        // G <= kSelThreads, so thread h reads the record of workgroup h
+        uint32_t Ah = 0, Eh = 0;
+        if (tid < chunk) {
+            Ah = ld_agent(&ss->cnt[tid][0]);
+            Eh = ld_agent(&ss->cnt[tid][1]);
+        }
+        uint32_t eq_before;
+        const uint32_t e_excl = block_excl_scan<kSelThreads>(Eh, sh.scan, &eq_before);
+        const uint32_t taken = exact ? Eh : (need > e_excl ? min(Eh, need - e_excl) : 0u);
+        uint32_t off;
+        block_excl_scan<kSelThreads>(Ah + taken, sh.scan, &off);
+        // ordered emission: thread t owns local candidates [t*E, t*E + E)
+        const int E = (cnt + kSelThreads - 1) / kSelThreads;
+        const int i0 = min(cnt, tid * E), i1 = min(cnt, i0 + E);
+        uint32_t my_eq = 0;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t k = s_key[i];
+            my_eq += (k != 0u) && ((k >> sh_bits) == prefix);
+        }
+        const uint32_t eq_rank0 = eq_before + block_excl_scan<kSelThreads>(my_eq, sh.scan, &tmp);
+        uint32_t my_sel = 0;
+        {
+            uint32_t er = eq_rank0;
+            for (int i = i0; i < i1; ++i) {
+                const uint32_t k = s_key[i];
+                if (k == 0u) continue;
+                const uint32_t p = k >> sh_bits;
+                if (p > prefix) ++my_sel;
+                else if (p == prefix) {
+                    if (exact || er < need) ++my_sel;
+                    ++er;
+                }
+            }
+        }
+        uint32_t dst = off + block_excl_scan<kSelThreads>(my_sel, sh.scan, &tmp);
+        {
+            uint32_t er = eq_rank0;
+            for (int i = i0; i < i1; ++i) {
+                const uint32_t k = s_key[i];
+                if (k == 0u) continue;
+                const uint32_t p = k >> sh_bits;
+                bool take = p > prefix;
+                if (p == prefix) {
+                    take = exact || er < need;
+                    ++er;
+                }
+                if (take) {
+                    int pos;
+                    int64_t row;
+                    cand_row<MODE>(s, c0 + i, a.lp, pos, row);
+                    if (dst < (uint32_t)K) out[dst] = pos;
+                    ++dst;
+                }
+            }
+        }
+    }
+    if (chunk == G - 1)
+        for (int j = (int)k_eff + tid; j < K; j += kSelThreads) out[j] = -1;
+
+    // ---- leave the histograms zeroed for the next launch. Every histogram read happens
+    //      before the count-exchange barrier; without that barrier (nothing to select) one
+    //      more barrier separates the last reads from the clearing.
+    if (k_eff == 0) ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+    for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
+        st_agent(&ss->hist[0][0] + i, 0u);
+    (void)ok;
+}
+
+// ------------------------------------------------------------------ launchers
+template <int DIM, int HT, bool FP8>
+static hipError_t launch_score_t(const ScoreArgs &a, int rows, int64_t max_cols, hipStream_t st) {
+    dim3 grid((unsigned)((max_cols + kScoreChunk - 1) / kScoreChunk), (unsigned)rows);
+    hipLaunchKernelGGL((k_index_score<DIM, HT, FP8>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, int rows,
+                              int64_t max_cols, hipStream_t st) {
+    const bool small = heads <= 16;
+    if (dim == 128) {
+        if (fp8) return small ? launch_score_t<128, 1, true>(a, rows, max_cols, st)
+                              : launch_score_t<128, 4, true>(a, rows, max_cols, st);
+        return small ? launch_score_t<128, 1, false>(a, rows, max_cols, st)
+                     : launch_score_t<128, 4, false>(a, rows, max_cols, st);
+    }
+    if (fp8) return small ? launch_score_t<64, 1, true>(a, rows, max_cols, st)
+                          : launch_score_t<64, 4, true>(a, rows, max_cols, st);
+    return small ? launch_score_t<64, 1, false>(a, rows, max_cols, st)
+                 : launch_score_t<64, 4, false>(a, rows, max_cols, st);
+}
+
+template <int DIM, int HT, bool FP8, int MODE>
+static void *select_kernel_ptr() {
+    return reinterpret_cast<void *>(&k_decode_select<DIM, HT, FP8, MODE>);
+}
+
+template <int DIM, int HT, bool FP8>
+static void *select_kernel_mode(int mode) {
+    if (mode == kTokens) return select_kernel_ptr<DIM, HT, FP8, kTokens>();
+    if (mode == kBlocks) return select_kernel_ptr<DIM, HT, false, kBlocks>();
+    return select_kernel_ptr<DIM, HT, FP8, kCandidates>();
+}
+
+void *decode_select_kernel(int dim, int heads, bool fp8, int mode) {
+    const bool small = heads <= 16;
+    if (dim == 128) {
+        if (fp8) return small ? select_kernel_mode<128, 1, true>(mode)
+                              : select_kernel_mode<128, 4, true>(mode);
+        return small ? select_kernel_mode<128, 1, false>(mode)
+                     : select_kernel_mode<128, 4, false>(mode);
+    }
+    if (fp8) return small ? select_kernel_mode<64, 1, true>(mode)
+                          : select_kernel_mode<64, 4, true>(mode);
+    return small ? select_kernel_mode<64, 1, false>(mode) : select_kernel_mode<64, 4, false>(mode);
+}
+
+size_t decode_select_static_lds() { return sizeof(SelShared); }
+
+}  // namespace sa

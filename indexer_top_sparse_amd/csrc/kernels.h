@@ -1,0 +1,102 @@
+// Kernel argument blocks, the per-sequence synchronisation record and the launchers that the
+// C ABI (api.hip) calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kMaxGroupsPerSeq = 512;  // workgroups sharing one sequence in a selection
+
+// Per-sequence record in the workspace used by the cross-workgroup selection. `count` and the
+// histograms return to zero at the end of every launch; `gen` only grows.
+struct SelSync {
+    uint32_t count;
+    uint32_t gen;
+    uint32_t pad[62];
+    uint32_t hist[3][2048];
+    uint32_t cnt[kMaxGroupsPerSeq][2];
+};
+
+// Query row -> (sequence, offset inside the sequence's rows, rows of that sequence).
+__device__ __forceinline__ void row_info(const int32_t *q_indptr, int num_seqs, int row,
+                                         int &seq, int &qoff, int &qlen) {
+    if (!q_indptr) {
+        seq = row;
+        qoff = 0;
+        qlen = 1;
+        return;
+    }
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {  // last b with q_indptr[b] <= row
+        const int mid = (lo + hi + 1) >> 1;
+        if (q_indptr[mid] <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    seq = lo;
+    qoff = row - q_indptr[lo];
+    qlen = q_indptr[lo + 1] - q_indptr[lo];
+}
+
+struct ScoreArgs {
+    int num_seqs, lp, pages_per_seq, heads;
+    const int32_t *page_table, *ctx_lens, *q_indptr;
+    const uint16_t *q_idx;
+    const float *w;
+    const uint8_t *keys;
+    const float *key_scale;
+    float *scores;
+    int64_t ld;
+};
+
+struct SelectArgs {
+    int num_seqs, lp, pages_per_seq, heads, chunk, k, block_k;
+    const int32_t *page_table, *ctx_lens;
+    const int32_t *blocks;  // [num_seqs][block_k] for the fine stage, else null
+    const uint16_t *q_idx;
+    const float *w;
+    const uint8_t *keys;
+    const float *key_scale;
+    int32_t *idx_out;  // [num_seqs][k]
+    SelSync *sync;
+    uint32_t *err;
+};
+
+struct TopkArgs {
+    int num_seqs, k;
+    const int32_t *ctx_lens, *q_indptr;
+    const float *scores;
+    int64_t ld;
+    int32_t *idx;
+};
+
+// Wave pairs per attention workgroup (32 query heads per pair) and head groups per row.
+inline int attn_pairs(int heads_q) { return heads_q > 32 ? 2 : 1; }
+inline int attn_hgroups(int heads_q) { return (heads_q + 32 * attn_pairs(heads_q) - 1) / (32 * attn_pairs(heads_q)); }
+
+struct AttnArgs {
+    int num_seqs, lp, pages_per_seq, heads_q, k, splits, split_len, rows, hgroups;
+    const int32_t *page_table, *ctx_lens, *q_indptr;
+    const uint16_t *q;
+    const int32_t *idx;
+    const uint8_t *kc;  // K rows (or latent rows)
+    const uint8_t *vc;  // V rows, or null when V is the head of each K row
+    const float *kv_scale;
+    const uint8_t *zero_row;  // >= 1152 zero bytes (source of empty staged rows)
+    float scale_log2;   // softmax_scale * log2(e)
+    uint16_t *out;      // bf16 [rows][heads_q][dv] (splits == 1)
+    float *part_o;      // [rows][splits][heads_q][dv]   (splits > 1)
+    float *part_ml;     // [rows][splits][heads_q][2]
+};
+
+hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, int rows,
+                              int64_t max_cols, hipStream_t st);
+void *decode_select_kernel(int dim, int heads, bool fp8, int mode);
+size_t decode_select_static_lds();
+hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);
+hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, bool fp8,
+                              hipStream_t st);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,137 @@
+// Row-wise Top-K over scores in HBM (the unfused selection used by Prefill and by tests):
+// one workgroup per query row, radix select on order-preserving keys (three digits of
+// 11/11/10 bits, stopping as soon as the threshold bin is taken whole), then an ordered
+// emission that keeps ascending positions and gives ties at the threshold to the lower
+// positions. "Top-K filtering ... custom operator" of "Engineering Path for Day-0 Adaptation of
+// Trillion-Scale Sparse Models on Domestic AI Accelerators" §3.1.
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+constexpr int kTkThreads = 512;
+constexpr int kTkWaves = kTkThreads / 64;
+
+__global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t scan[kTkWaves + 1];
+    __shared__ uint32_t res[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    int seq, qoff, qlen;
+    row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
+    const int64_t pos_q = (int64_t)a.ctx_lens[seq] - qlen + qoff;
+    const int n = (int)min(pos_q + 1, a.ld);
+    const float *sc = a.scores + (int64_t)row * a.ld;
+    int32_t *out = a.idx + (int64_t)row * a.k;
+    const uint32_t k_eff = (uint32_t)min(a.k, max(n, 0));
+
+    uint32_t prefix = 0, need = k_eff;
+    int pbits = 0;
+    bool exact = false;
+    for (int pass = 0; pass < 3 && need > 0; ++pass) {
+        const int bits = pass < 2 ? 11 : 10;
+        const int shift = 32 - pbits - bits;
+        const int nb = 1 << bits;
+        for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < n; i += kTkThreads) {
+            const uint32_t k = float_key(sc[i]);
+            if (pbits && (k >> (32 - pbits)) != prefix) continue;
+            atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t hv[4], csum = 0;
+        const int top = nb - 4 * tid - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hv[j] = top - j >= 0 ? hist[top - j] : 0u;
+            csum += hv[j];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan<kTkThreads>(csum, scan, &tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (run < need && run + hv[j] >= need) {
+                res[0] = (uint32_t)(top - j);
+                res[1] = run;
+                res[2] = hv[j];
+            }
+            run += hv[j];
+        }
+        __syncthreads();
+        need -= res[1];
+        prefix = (prefix << bits) | res[0];
+        pbits += bits;
+        if (res[2] == need) {
+            exact = true;
+            break;
+        }
+        __syncthreads();
+    }
+
+    if (k_eff > 0) {
+        const int shb = 32 - pbits;
+        uint32_t dst_base = 0, eq_base = 0;
+        for (int base = 0; base < n; base += 4 * kTkThreads) {
+            uint32_t keys[4];
+            int my_eq = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + 4 * tid + j;
+                keys[j] = i < n ? float_key(sc[i]) : 0u;
+                my_eq += (i < n) && ((keys[j] >> shb) == prefix);
+            }
+            uint32_t tot_eq, tot_sel;
+            uint32_t er = eq_base + block_excl_scan<kTkThreads>(my_eq, scan, &tot_eq);
+            bool take[4];
+            int my_sel = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + 4 * tid + j;
+                const uint32_t p = keys[j] >> shb;
+                take[j] = false;
+                if (i < n) {
+                    if (p > prefix) take[j] = true;
+                    else if (p == prefix) {
+                        take[j] = exact || er < need;
+                        ++er;
+                    }
+                }
+                my_sel += take[j];
+            }
+            uint32_t dst = dst_base + block_excl_scan<kTkThreads>(my_sel, scan, &tot_sel);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (take[j]) {
+                    if (dst < k_eff) out[dst] = base + 4 * tid + j;
+                    ++dst;
+                }
+            dst_base += tot_sel;
+            eq_base += tot_eq;
+        }
+    }
+    for (int j = (int)k_eff + tid; j < a.k; j += kTkThreads) out[j] = -1;
+}
+
+hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st) {
+    hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kTkThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+__global__ void k_zero(uint4 *p, size_t n16) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t st) {
+    const size_t n16 = bytes / 16;
+    if (n16) {
+        const size_t want = (n16 + 255) / 256;
+        const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+        hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, st, (uint4 *)p, n16);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sa

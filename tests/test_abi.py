@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point, and
+rejects invalid arguments before touching the device (these tests need no GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+from indexer_top_sparse_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.load()
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert "sa_decode_step" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sa_version() == 1
+    for st in range(5):
+        assert lib.sa_status_string(st)
+    assert lib.sa_status_string(99) == b"unknown status"
+
+
+class _FakeDev:
+    """Host tensors standing in for device buffers: validation never dereferences them."""
+
+    def __init__(self, B_=2, ctx=(100, 7), P=64, pages=4):
+        self.pt = torch.zeros((B_, pages), dtype=torch.int32)
+        self.ctx = torch.tensor(ctx, dtype=torch.int32)
+        self.batch = B.Batch(self.pt, self.ctx, list(ctx), P, 8)
+        self.keys = torch.zeros((8, P, 128), dtype=torch.bfloat16)
+        self.kvc = torch.zeros((8, P, 576), dtype=torch.bfloat16)
+        self.ix = B.indexer_desc(64, 128, self.keys)
+        self.kv = B.kv_desc(128, 576, 512, self.kvc, softmax_scale=1 / 24)
+
+
+def test_workspace_size_grows_with_batch(lib):
+    a = _FakeDev()
+    n1 = B.workspace_size(a.batch, a.kv, 2048)
+    n2 = B.workspace_size(a.batch, a.kv, 4096)
+    n3 = B.workspace_size(a.batch, a.kv, 2048, block_k=512)
+    assert 0 < n1 < n2 and n1 < n3
+    assert B.workspace_size(a.batch, None, 2048) < n1
+
+
+def _decode(lib, a, **over):
+    args = dict(batch=C.byref(a.batch.s), ix=C.byref(a.ix), kv=C.byref(a.kv),
+                q_idx=C.c_void_p(a.keys.data_ptr()), w=C.c_void_p(a.keys.data_ptr()),
+                q=C.c_void_p(a.kvc.data_ptr()), k=2048, block_k=0, idx=None,
+                out=C.c_void_p(a.kvc.data_ptr()), ws=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return lib.sa_decode_step(args["batch"], args["ix"], args["kv"], args["q_idx"], args["w"],
+                              args["q"], args["k"], args["block_k"], args["idx"], args["out"],
+                              args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_invalid_arguments_are_rejected_on_the_host(lib):
+    a = _FakeDev()
+    assert _decode(lib, a, batch=None) == B.SA_ERR_INVALID
+    assert _decode(lib, a, k=0) == B.SA_ERR_INVALID
+    assert _decode(lib, a, q_idx=None) == B.SA_ERR_INVALID
+    assert _decode(lib, a, block_k=64) == B.SA_ERR_INVALID  # no pooled summaries
+    assert _decode(lib, a) == B.SA_ERR_WORKSPACE              # no workspace
+    # unsupported shapes
+    bad = B.kv_desc(128, 320, 256, a.kvc, softmax_scale=0.1)
+    assert _decode(lib, a, kv=C.byref(bad)) == B.SA_ERR_UNSUPPORTED
+    bad = B.indexer_desc(65, 128, a.keys)
+    assert _decode(lib, a, ix=C.byref(bad)) == B.SA_ERR_UNSUPPORTED
+    bad = B.kv_desc(128, 576, 512, a.kvc, softmax_scale=0.0)
+    assert _decode(lib, a, kv=C.byref(bad)) == B.SA_ERR_INVALID
+    # context longer than the page table can address
+    b2 = B.Batch(a.pt, a.ctx, [100, 257], 64, 8)
+    assert _decode(lib, a, batch=C.byref(b2.s)) == B.SA_ERR_INVALID
+    # page size must be a power of two
+    b3 = B.Batch(a.pt, a.ctx, [100, 7], 48, 8)
+    assert _decode(lib, a, batch=C.byref(b3.s)) == B.SA_ERR_INVALID
+    # decode takes one row per sequence
+    qi = torch.tensor([0, 1, 2], dtype=torch.int32)
+    b4 = B.Batch(a.pt, a.ctx, [100, 7], 64, 8, qi, [0, 1, 2])
+    assert _decode(lib, a, batch=C.byref(b4.s)) == B.SA_ERR_INVALID
+    assert b"q_indptr" in lib.sa_last_error()
+
+
+def test_index_score_and_topk_validation(lib):
+    a = _FakeDev()
+    sc = torch.zeros((2, 100), dtype=torch.float32)
+    P = C.c_void_p
+    # ld smaller than the longest visible row
+    st = lib.sa_index_score(C.byref(a.batch.s), C.byref(a.ix), P(a.keys.data_ptr()),
+                            P(sc.data_ptr()), P(sc.data_ptr()), 50, None)
+    assert st == B.SA_ERR_INVALID
+    st = lib.sa_topk(C.byref(a.batch.s), P(sc.data_ptr()), 100, 0, P(sc.data_ptr()), None, 0,
+                     None)
+    assert st == B.SA_ERR_INVALID
+    # misaligned indexer queries
+    st = lib.sa_index_score(C.byref(a.batch.s), C.byref(a.ix), P(a.keys.data_ptr() + 2),
+                            P(sc.data_ptr()), P(sc.data_ptr()), 100, None)
+    assert st == B.SA_ERR_INVALID
+
+
+def test_sparse_attn_needs_a_large_enough_workspace(lib):
+    a = _FakeDev()
+    need = B.workspace_size(a.batch, a.kv, 2048)
+    ws = torch.zeros(need + 512, dtype=torch.uint8)
+    base = ws.data_ptr() + ((-ws.data_ptr()) % 256)
+    idx = torch.zeros((2, 2048), dtype=torch.int32)
+    P = C.c_void_p
+    st = lib.sa_sparse_attn(C.byref(a.batch.s), C.byref(a.kv), P(a.kvc.data_ptr()),
+                            P(idx.data_ptr()), 2048, P(a.kvc.data_ptr()), P(base), need - 256,
+                            None)
+    assert st == B.SA_ERR_WORKSPACE
+    st = lib.sa_sparse_attn(C.byref(a.batch.s), C.byref(a.kv), P(a.kvc.data_ptr()),
+                            P(idx.data_ptr()), 2048, P(a.kvc.data_ptr()), P(base + 16), need,
+                            None)
+    assert st == B.SA_ERR_WORKSPACE  # not 256-byte aligned
