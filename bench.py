@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of index-selected sparse attention on one MI355X.
+
+One step = the whole Decode hot path for a batch: indexer scores over every cached token,
+Top-K selection and sparse attention over the selected rows (sa_decode_step). Inputs are
+seeded synthetic tensors already resident in HBM; R replicas of the caches are rotated so that
+no step finds its inputs in the 256 MB last-level cache left warm by the previous step.
+
+Prints one JSON line (rank 0) with the throughput, the roofline of the dominant kernel, and the
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s (indexer+TopK+sparse attn), B=32 ctx=32K; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "indexer_top_sparse_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl):
+    """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
+    P, K = wl.page_size, wl.topk
+    key_row = wl.idx_dim * (1 if wl.idx_dtype == "fp8" else 2) + (4 if wl.idx_dtype == "fp8" else 0)
+    kv_row = wl.k_row * (1 if wl.kv_dtype == "fp8" else 2) + (4 if wl.kv_dtype == "fp8" else 0)
+    sel = attn = 0
+    for n in wl.ctx_lens:
+        npg = math.ceil(n / P)
+        k_eff = min(K, n)
+        sel += (n * key_row + wl.idx_heads * wl.idx_dim * 2 + wl.idx_heads * 4 + npg * 4 + 4
+                + K * 4)
+        attn += (k_eff * kv_row + wl.heads_q * wl.dim_qk * 2 + wl.heads_q * wl.dim_v * 2
+                 + K * 4 + npg * 4)
+    # the fused step: everything above except the index set, which never has to leave the op
+    step = sel + attn - 2 * 4 * K * wl.num_seqs
+    return {"select": sel, "attention": attn, "step": step}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode32k",
+                    help="input preset (decode32k is the headline configuration)")
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from indexer_top_sparse_amd import binding as B
+    from indexer_top_sparse_amd import device, inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load()
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    wl = inputs.make(args.workload)
+    log(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s")
+
+    # replicas: same content at different addresses
+    reps = [device.to_device(wl, "cuda:0")]
+    for r in range(1, args.replicas):
+        d = device.to_device(wl, "cuda:0")
+        reps.append(d)
+    ws = device.new_workspace(reps[0])
+    out = torch.empty((wl.num_seqs, wl.heads_q, wl.dim_v), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((wl.num_seqs, wl.topk), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {args.replicas} replicas resident, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * 2**30) // 4
+        a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n * 4 / 2**30:.2f} GiB read + written")
+        del a, b
+
+    def step(i):
+        d = reps[i % len(reps)]
+        device.decode_step(d, ws, out=out, idx=idx)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    assert B.workspace_error(ws) == 0, "device-side wait failed"
+    log(f"[bench] warmup {args.warmup} done")
+
+    # ---- headline: K fused decode steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
+
+    # ---- per-kernel durations, measured live on the same stream: the step split into its two
+    #      launches (selection, then attention + split merge) with events between them
+    sel_ms, att_ms = [], []
+    for i in range(args.steps):
+        d = reps[i % len(reps)]
+        a0, a1, a2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a0.record(stream)
+        device.index_select(d, ws, idx=idx)
+        a1.record(stream)
+        B.sparse_attn(d.batch, d.kv, d.t["q"], idx, out, ws)
+        a2.record(stream)
+        sel_ms.append((a0, a1))
+        att_ms.append((a1, a2))
+    torch.cuda.synchronize()
+    sel_avg = sum(x.elapsed_time(y) for x, y in sel_ms) / len(sel_ms)
+    att_avg = sum(x.elapsed_time(y) for x, y in att_ms) / len(att_ms)
+    assert B.workspace_error(ws) == 0
+    log(f"[bench] per launch: select {sel_avg * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us")
+
+    ab = algorithmic_bytes(wl)
+    tokens_per_s = wl.num_seqs / (ms_step * 1e-3)
+    step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+
+    dominant = "select" if sel_avg >= att_avg else "attention"
+    dom_ms = sel_avg if dominant == "select" else att_avg
+    achieved = ab[dominant] / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    tfile = os.path.join(PROFILES, f"traffic_{args.workload}.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_hash") == kernel_source_hash() and dominant in t.get("kernels", {}):
+            traffic = t["kernels"][dominant]["hbm_bytes_per_launch"]
+
+    # ---- CPU baseline: the oracle (fp64 C, OpenMP) on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        t1 = time.perf_counter()
+        oracle.decode_step(wl, rows=[0])
+        one = time.perf_counter() - t1
+        n_rows = max(1, min(wl.num_seqs, int(args.cpu_seconds / max(one, 1e-3))))
+        t1 = time.perf_counter()
+        oracle.decode_step(wl, rows=list(range(n_rows)))
+        el = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        cpu = {"value": n_rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_rows} of {wl.num_seqs} sequences of the same workload, full path "
+                         f"(scores, Top-K, attention) in fp64, {el:.1f}s"}
+        log(f"[bench] cpu baseline {cpu}")
+
+    res = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic: seeded N(0,1) caches and queries, randomly permuted pages, "
+                f"{args.replicas} rotating replicas resident in HBM",
+        "config": {
+            "workload": f"{args.workload}: decode B={wl.num_seqs} ctx={max(wl.ctx_lens)} "
+                        f"page={wl.page_size} indexer {wl.idx_heads}x{wl.idx_dim} "
+                        f"K={wl.topk} heads_q={wl.heads_q} qk/v={wl.dim_qk}/{wl.dim_v} "
+                        f"{wl.kv_dtype}",
+            "global_batch": wl.num_seqs, "seq_len": max(wl.ctx_lens), "parallelism": "none",
+        },
+        "step_hbm": {"algorithmic_bytes": ab["step"], "achieved_gbs": step_gbs,
+                     "frac_of_peak": step_gbs / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": ab[dominant],
+                     "avg_launch_us": dom_ms * 1e3},
+        "kernels_us": {"select": sel_avg * 1e3, "attention": att_avg * 1e3},
+        "cpu_baseline": cpu,
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -147,11 +147,25 @@ sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
                          size_t workspace_bytes, void *stream);
 
 /*
- * sa_decode_step -- the fused Decode path ([CANN] §2.1: scoring, head weighting and Top-K in
- * one composite operator reading the paged cache directly; [GPUGuide] §3.3: decode fuses
- * index selection with attention to cut launches; [GPUGuide] §3.1 and [CANN] §2: no score
- * write-back). One query row per sequence (batch->q_indptr must be NULL). Scores stay in
- * on-chip memory; Top-K runs across the workgroups that share a sequence.
+ * sa_index_select -- the lightweight indexer as one composite Decode operator ([CANN] §2.1:
+ * relevance scoring, head-weight weighting and Top-K fused, reading the paged cache directly;
+ * [CANN] §2.2: the indexer returns top-k indices). One query row per sequence
+ * (batch->q_indptr must be NULL). Scores are never written to HBM: each workgroup keeps its
+ * chunk of a sequence's scores in LDS, and an exact radix selection runs across the
+ * workgroups that share the sequence. Hierarchical selection when block_k > 0 as described
+ * for sa_decode_step.
+ *   q_idx device bf16 [num_seqs][ix->heads][ix->dim];  w device fp32 [num_seqs][ix->heads]
+ *   idx_out device int32 [num_seqs][k]: selected positions, ascending, -1 padded
+ */
+sa_status sa_index_select(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                          const float *w, int32_t k, int32_t block_k, int32_t *idx_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sa_decode_step -- the fused Decode path: sa_index_select followed by sa_sparse_attn on the
+ * same stream, with the index set kept in the workspace ([GPUGuide] §3.3: decode fuses index
+ * selection with attention to cut launches; [GPUGuide] §3.1 and [CANN] §2: no score
+ * write-back). One query row per sequence (batch->q_indptr must be NULL).
  * With block_k > 0, selection is hierarchical ([SameDay] §3.1; [GPUGuide] §3.1): blocks
  * (= pages) are scored from ix->pooled, the block_k best blocks are kept (ties -> lower
  * block), and the token Top-K is taken among the visible tokens of the kept blocks.

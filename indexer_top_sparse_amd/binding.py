@@ -44,7 +44,8 @@ class sa_kv(C.Structure):
 
 
 _lib = None
-EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_decode_step", "sa_workspace_size",
+EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_decode_step",
+           "sa_workspace_size",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -62,6 +63,7 @@ def load(path: str = LIB_PATH):
     lib.sa_index_score.argtypes = [pb, pi, P, P, P, i64, P]
     lib.sa_topk.argtypes = [pb, P, i64, i32, P, P, sz, P]
     lib.sa_sparse_attn.argtypes = [pb, pk, P, P, i32, P, P, sz, P]
+    lib.sa_index_select.argtypes = [pb, pi, P, P, i32, i32, P, P, sz, P]
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
@@ -71,7 +73,7 @@ def load(path: str = LIB_PATH):
     lib.sa_status_string.restype = C.c_char_p
     lib.sa_last_error.restype = C.c_char_p
     lib.sa_version.restype = i32
-    for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_decode_step",
+    for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_decode_step",
                "sa_workspace_init", "sa_workspace_error"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
@@ -175,6 +177,12 @@ def sparse_attn(batch: Batch, kv: sa_kv, q, idx, out, ws, stream=None) -> None:
     _check(load().sa_sparse_attn(C.byref(batch.s), C.byref(kv), _ptr(q), _ptr(idx),
                                  idx.shape[1], _ptr(out), _ptr(ws), ws.numel(),
                                  _stream(stream)))
+
+
+def index_select(batch: Batch, ix: sa_indexer, q_idx, w, k: int, idx_out, ws, block_k: int = 0,
+                 stream=None) -> None:
+    _check(load().sa_index_select(C.byref(batch.s), C.byref(ix), _ptr(q_idx), _ptr(w), k,
+                                  block_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def decode_step(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, out, ws,

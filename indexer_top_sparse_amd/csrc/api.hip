@@ -107,7 +107,7 @@ sa_status check_kv(const sa_kv *kv) {
 }
 
 int attn_splits(int rows, int k, int heads_q) {
-    const int target = 512;  // workgroups: two rounds over 256 CUs
+    const int target = 256;  // workgroups: one per CU (about 100 KB of LDS each)
     const int per_split = std::max(rows, 1) * attn_hgroups(heads_q);
     int s = std::max(1, (target + per_split - 1) / per_split);
     s = std::min(s, std::max(1, (k + 31) / 32));
@@ -211,7 +211,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
                     : std::max<int>(64, (int)((total / ((int64_t)cus * 4) + 63) / 64 * 64));
     for (;;) {
         if (chunk > 32768) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
-        const size_t lds = (size_t)chunk * 4;
+        const size_t lds = decode_select_dynamic_lds(mode, chunk, log2i(b->page_size));
         const int occ = occupancy(kern, threads, lds);
         if (occ < 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
         const int64_t cap = (int64_t)occ * cus;
@@ -397,39 +397,65 @@ sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
                     static_cast<hipStream_t>(stream));
 }
 
-sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
-                         const void *q_idx, const float *w, const void *q, int32_t k,
-                         int32_t block_k, int32_t *idx_out, void *out, void *ws,
-                         size_t ws_bytes, void *stream) {
-    RowPlan rp;
-    sa_status st = check_batch(batch, &rp);
-    if (st != SA_OK) return st;
-    if (batch->q_indptr) return fail(SA_ERR_INVALID, "sa_decode_step takes one query row per sequence (q_indptr must be NULL)");
-    if ((st = check_indexer(ix)) != SA_OK) return st;
-    if ((st = check_kv(kv)) != SA_OK) return st;
-    if (!q_idx || !aligned16(q_idx) || !w || !q || !aligned16(q) || !out ||
-        (reinterpret_cast<uintptr_t>(out) & 7u))
-        return fail(SA_ERR_INVALID, "q_idx, q (16-byte aligned), w and out are required");
-    if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
-    if (block_k < 0 || block_k > 65536) return fail(SA_ERR_INVALID, "block_k must be in [0, 65536]");
-    if (block_k > 0 && !ix->pooled) return fail(SA_ERR_INVALID, "two-level selection needs ix->pooled");
-    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k);
-    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
-    uint8_t *wsb = static_cast<uint8_t *>(ws);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
+static sa_status select_impl(const sa_batch *batch, const RowPlan &rp, const sa_indexer *ix,
+                             const void *q_idx, const float *w, int32_t k, int32_t block_k,
+                             int32_t *idx, uint8_t *wsb, const WsLayout &L, hipStream_t hs) {
+    (void)rp;
+    sa_status st;
     if (block_k > 0) {
         int32_t *blocks = reinterpret_cast<int32_t *>(wsb + L.blocks);
         if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks, wsb, L,
                              hs)) != SA_OK)
             return st;
-        if ((st = run_select(batch, ix, q_idx, w, 2, k, block_k, blocks, idx, wsb, L, hs)) !=
-            SA_OK)
-            return st;
-    } else {
-        if ((st = run_select(batch, ix, q_idx, w, 0, k, 0, nullptr, idx, wsb, L, hs)) != SA_OK)
-            return st;
+        return run_select(batch, ix, q_idx, w, 2, k, block_k, blocks, idx, wsb, L, hs);
     }
+    return run_select(batch, ix, q_idx, w, 0, k, 0, nullptr, idx, wsb, L, hs);
+}
+
+static sa_status check_select(const sa_batch *batch, RowPlan *rp, const sa_indexer *ix,
+                              const void *q_idx, const float *w, int32_t k, int32_t block_k) {
+    sa_status st = check_batch(batch, rp);
+    if (st != SA_OK) return st;
+    if (batch->q_indptr)
+        return fail(SA_ERR_INVALID, "decode selection takes one query row per sequence (q_indptr must be NULL)");
+    if ((st = check_indexer(ix)) != SA_OK) return st;
+    if (!q_idx || !aligned16(q_idx) || !w) return fail(SA_ERR_INVALID, "q_idx (16-byte aligned) and w are required");
+    if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
+    if (block_k < 0 || block_k > 65536) return fail(SA_ERR_INVALID, "block_k must be in [0, 65536]");
+    if (block_k > 0 && !ix->pooled) return fail(SA_ERR_INVALID, "two-level selection needs ix->pooled");
+    return SA_OK;
+}
+
+sa_status sa_index_select(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                          const float *w, int32_t k, int32_t block_k, int32_t *idx_out,
+                          void *ws, size_t ws_bytes, void *stream) {
+    RowPlan rp;
+    sa_status st = check_select(batch, &rp, ix, q_idx, w, k, block_k);
+    if (st != SA_OK) return st;
+    if (!idx_out) return fail(SA_ERR_INVALID, "idx_out is required");
+    const WsLayout L = ws_layout(batch, rp.rows, nullptr, k, block_k);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
+    return select_impl(batch, rp, ix, q_idx, w, k, block_k, idx_out, static_cast<uint8_t *>(ws),
+                       L, static_cast<hipStream_t>(stream));
+}
+
+sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                         const void *q_idx, const float *w, const void *q, int32_t k,
+                         int32_t block_k, int32_t *idx_out, void *out, void *ws,
+                         size_t ws_bytes, void *stream) {
+    RowPlan rp;
+    sa_status st = check_select(batch, &rp, ix, q_idx, w, k, block_k);
+    if (st != SA_OK) return st;
+    if ((st = check_kv(kv)) != SA_OK) return st;
+    if (!q || !aligned16(q) || !out || (reinterpret_cast<uintptr_t>(out) & 7u))
+        return fail(SA_ERR_INVALID, "q (16-byte aligned) and out (8-byte aligned) are required");
+    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
+    if ((st = select_impl(batch, rp, ix, q_idx, w, k, block_k, idx, wsb, L, hs)) != SA_OK)
+        return st;
     return run_attn(batch, rp.rows, kv, q, idx, k, out, wsb, L, hs);
 }
 

@@ -54,11 +54,19 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
     constexpr int ND = DV / 32 / 2;    // 32-wide d_v tiles per wave
     constexpr int NWV = 2 * NP;
 
+    // Staging buffers as separate objects: the loop rotates through them at compile time, so
+    // the compiler can tell that the reads of one never alias the global->LDS copies into the
+    // others and keeps those copies in flight across the reads. bf16 rows use a ring of three
+    // (two tiles in flight); E4M3 rows, staged through registers, use two.
+    __shared__ __attribute__((aligned(16))) uint8_t stage_a[S::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_b[S::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_c[FP8 ? 16 : S::BUF];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // lds layout: [2][BUF] staged rows, then [NWV][32][32] fp32 partial scores
-    float *s_part = reinterpret_cast<float *>(lds + 2 * S::BUF);
-    __shared__ int32_t s_slot[2][kTile];
-    __shared__ __attribute__((aligned(16))) float s_sig[2][kTile];  // scale or 1; < 0 = empty
+    // dynamic lds: [NWV][32][32] fp32 partial scores | [split_len] int32 slots |
+    //              [split_len] fp32 row flags (scale or 1; < 0 empty)
+    float *s_part = reinterpret_cast<float *>(lds);
+    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + NWV * 4096);
+    float *s_sig = reinterpret_cast<float *>(s_slot + a.split_len);
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int h = l >> 5, lm = l & 31;
@@ -77,8 +85,20 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
     const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
     const int P = 1 << a.lp;
 
-    // query fragments (B operand of S^T = K Q^T): head 32*pair + l%32, d = 16s + 8h + e for
-    // this wave's k-steps s in [half*KS, half*KS + KS)
+    // ---- slot and flag of every selected row of this split (the loop below then issues no
+    //      dependent global loads)
+    for (int j = tid; j < ntiles * kTile; j += NT) {
+        int32_t slot = -1;
+        if (j0 + j < j1) {
+            const int e = idx[j0 + j];
+            if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
+        }
+        s_slot[j] = slot;
+        s_sig[j] = slot < 0 ? -1.f : (FP8 ? a.kv_scale[slot] : 1.f);
+    }
+
+    // query fragments (B operand of S^T = K Q^T): head 32 (NP hg + pair) + l%32,
+    // d = 16s + 8h + e for this wave's k-steps s in [half*KS, half*KS + KS)
     const int head = 32 * (NP * hg + pair) + lm;
     u32x4 qf[KS];
     {
@@ -88,46 +108,27 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
             qf[s] = head < a.heads_q ? ldg16(qr + 16 * (half * KS + s)) : u32x4{0u, 0u, 0u, 0u};
     }
 
-    auto tile_slots = [&](int t, int buf) {
-        if (tid < kTile) {
-            const int j = j0 + t * kTile + tid;
-            int32_t slot = -1;
-            if (t < ntiles && j < j1) {
-                const int e = idx[j];
-                if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
-            }
-            s_slot[buf][tid] = slot;
-        }
-    };
-
-    // Gather of one tile into LDS buffer `buf`. bf16 rows go global -> LDS directly (lane i of
-    // an instruction fills LDS chunk base + i; the swizzle is applied on the global side);
-    // empty rows read a zero row. E4M3 rows go through registers and are widened to bf16.
-    constexpr int FP8_CH = kTile * (DQK / 16);           // 16-byte global chunks of a fp8 tile
+    // Gather of tile t into LDS buffer `buf`. bf16 rows go global -> LDS directly (lane i of an
+    // instruction fills LDS chunk base + i; the swizzle is applied on the global side); empty
+    // rows read a zero row. E4M3 rows go through registers and are widened to bf16.
+    constexpr int FP8_CH = kTile * (DQK / 16);  // 16-byte global chunks of a fp8 tile
     constexpr int FP8_PER = (FP8_CH + NT - 1) / NT;
     u32x4 stg[FP8 ? FP8_PER : 1];
-    auto gather = [&](int buf) {
-        // row flags of the tile being gathered (read by the softmax of that tile)
-        if (tid < kTile) {
-            const int32_t slot = s_slot[buf][tid];
-            s_sig[buf][tid] = slot < 0 ? -1.f : (FP8 ? a.kv_scale[slot] : 1.f);
-        }
+    auto gather = [&](int t, uint8_t *base) {
+        const int32_t *slots = s_slot + t * kTile;
         if (!FP8) {
-            uint8_t *base = lds + buf * S::BUF;
             for (int ins = w; ins * 64 < S::NCHUNK; ins += NWV) {
                 const int ch = ins * 64 + l;
+                const bool isv = SEPV && ch >= kTile * S::CPR_K;
+                const int cc = isv ? ch - kTile * S::CPR_K : ch;
+                const int cpr = isv ? S::CPR_V : S::CPR_K;
+                const int r = cc / cpr, c = cc % cpr;
+                const int32_t slot = slots[r];
                 const uint8_t *src = a.zero_row;
-                if (ch < S::NCHUNK) {
-                    const bool isv = SEPV && ch >= kTile * S::CPR_K;
-                    const int cc = isv ? ch - kTile * S::CPR_K : ch;
-                    const int cpr = isv ? S::CPR_V : S::CPR_K;
-                    const int r = cc / cpr, c = cc % cpr;
-                    const int32_t slot = s_slot[buf][r];
-                    if (slot >= 0)
-                        src = (isv ? a.vc + (int64_t)slot * S::VROW_G
-                                   : a.kc + (int64_t)slot * S::KROW_G) +
-                              16 * (c ^ swz(r));
-                }
+                if (slot >= 0)
+                    src = (isv ? a.vc + (int64_t)slot * S::VROW_G
+                               : a.kc + (int64_t)slot * S::KROW_G) +
+                          16 * (c ^ swz(r));
                 __builtin_amdgcn_global_load_lds(src, (SA_LDS void *)(base + ins * 1024), 16, 0, 0);
             }
         } else {
@@ -137,16 +138,15 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
                 u32x4 v = {0u, 0u, 0u, 0u};
                 if (c < FP8_CH) {
                     const int r = c / (DQK / 16), col = c % (DQK / 16);
-                    const int32_t slot = s_slot[buf][r];
+                    const int32_t slot = slots[r];
                     if (slot >= 0) v = ldg16(a.kc + (int64_t)slot * S::KROW_G + 16 * col);
                 }
                 stg[i] = v;
             }
         }
     };
-    auto stage_fp8 = [&](int buf) {
+    auto stage_fp8 = [&](uint8_t *kb) {
         if (FP8) {
-            uint8_t *kb = lds + buf * S::BUF;
 #pragma unroll
             for (int i = 0; i < FP8_PER; ++i) {
                 const int c = tid + i * NT;
@@ -171,51 +171,71 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[n][r] = 0.f;
     float m_run = -__builtin_inff(), l_run = 0.f;
 
+    __syncthreads();  // slot table ready
+    // this wave's global->LDS copy instructions per tile (the last tile's loads that a wave
+    // may leave in flight at the end-of-tile wait)
+    constexpr int NI_MIN = (S::NCHUNK / 64) / NWV;
     if (ntiles > 0) {
-        tile_slots(0, 0);
-        tile_slots(1, 1);
-        __syncthreads();
-        gather(0);
-        stage_fp8(0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): direct-to-LDS loads have landed
-        __syncthreads();
+        gather(0, stage_a);
+        if (!FP8 && ntiles > 1) gather(1, stage_b);
+        stage_fp8(stage_a);
+        if (!FP8) {
+            // tile 0 landed (tile 1's copies, issued last, may still be in flight)
+            if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI_MIN));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        full_barrier_lds_only_after_wait();
     }
     const int g = l >> 4, jj = l & 15;
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < ntiles) gather(buf ^ 1);
+    auto tile = [&](int t, const uint8_t *kb, uint8_t *next) {
+        // bf16: copy tile t+2 into the buffer of tile t-1 (free since the last barrier);
+        // E4M3: load tile t+1 into registers, widened into `next` at the end
+        if (FP8) {
+            if (t + 1 < ntiles) gather(t + 1, next);
+        } else {
+            if (t + 2 < ntiles) gather(t + 2, next);
+        }
 
-        const uint8_t *kb = lds + buf * S::BUF;
         const uint8_t *vb = SEPV ? kb + S::KBUF : kb;
         constexpr int VROWB = SEPV ? S::ROWB_V : S::ROWB_K;
-        // ---- partial S^T = K Q^T over this wave's half of d
-        f32x16 sacc;
+        // ---- partial S^T = K Q^T over this wave's half of d: two independent accumulation
+        //      chains (even / odd k-steps), fragment reads running ahead
+        f32x16 sacc, sacc2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) sacc[r] = sacc2[r] = 0.f;
         const uint8_t *krow = kb + lm * S::ROWB_K;
         const int sw = swz(lm);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        auto kfrag = [&](int s) {
             const int c = 2 * (half * KS + s) + h;
-            sacc = mfma32x32x16(*reinterpret_cast<const u32x4 *>(krow + 16 * (c ^ sw)), qf[s],
-                                sacc);
+            return *reinterpret_cast<const u32x4 *>(krow + 16 * (c ^ sw));
+        };
+        u32x4 ka = kfrag(0), kb2 = kfrag(1);
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            const u32x4 a0 = ka, a1 = kb2;
+            if (s + 2 < KS) ka = kfrag(s + 2);
+            if (s + 3 < KS) kb2 = kfrag(s + 3);
+            sacc = mfma32x32x16(a0, qf[s], sacc);
+            if (s + 1 < KS) sacc2 = mfma32x32x16(a1, qf[s + 1], sacc2);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] += sacc2[r];
         // exchange partial scores with the other wave of the pair
         float *mine = s_part + (w * 32 + lm) * 32 + 16 * h;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             *reinterpret_cast<f32x4 *>(mine + 4 * q4) =
                 f32x4{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
-        tile_slots(t + 2, buf);
-        __syncthreads();
+        lds_barrier();
         // both waves add in the same order (a + b == b + a), so their softmax states agree;
         // logits in the log2 domain, -inf for empty rows
         const float *theirs = s_part + ((w ^ 1) * 32 + lm) * 32 + 16 * h;
+        const float *sig = s_sig + t * kTile;
         float m_tile = -__builtin_inff();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 ov = *reinterpret_cast<const f32x4 *>(theirs + 4 * j);
-            const f32x4 sv = *reinterpret_cast<const f32x4 *>(&s_sig[buf][8 * j + 4 * h]);
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(sig + 8 * j + 4 * h);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
@@ -228,7 +248,8 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
         const bool grow = m_tile > m_run + kRescale;
         if (__any(grow)) {
             const float m_new = grow ? m_tile : m_run;
-            const float alpha = grow ? exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+            // alpha = 0 when m_run = -inf (nothing accumulated yet)
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
             l_run *= alpha;
 #pragma unroll
             for (int n = 0; n < ND; ++n)
@@ -236,6 +257,9 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
                 for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
             m_run = m_new;
         }
+        // exp2(-inf - m) = 0 for empty rows; m_run is finite once any row was seen, and while
+        // it is -inf every logit is -inf too, which the select below maps to 0
+        const bool none = m_run == -__builtin_inff();
         u32x4 pb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -246,9 +270,9 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
                 for (int e1 = 0; e1 < 2; ++e1) {
                     const int r = 8 * u + 2 * e2 + e1;
-                    const float p = sacc[r] == -__builtin_inff() ? 0.f : exp2f(sacc[r] - m_run);
+                    const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[r] - m_run);
                     l_run += p;
-                    pp[e1] = FP8 ? p * fmaxf(s_sig[buf][8 * (r >> 2) + 4 * h + (r & 3)], 0.f) : p;
+                    pp[e1] = FP8 ? p * fmaxf(sig[8 * (r >> 2) + 4 * h + (r & 3)], 0.f) : p;
                 }
                 pk[e2] = pack_bf16x2(pp[0], pp[1]);
             }
@@ -273,9 +297,28 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
                 o[n] = mfma32x32x16(u32x4{w0[0], w0[1], w1[0], w1[1]}, pb[u], o[n]);
             }
         }
-        if (t + 1 < ntiles) stage_fp8(buf ^ 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+        if (FP8) {
+            if (t + 1 < ntiles) stage_fp8(next);
+            full_barrier();  // tile t+1 staged; everyone is done with this buffer
+        } else {
+            // tile t+1 has landed once at most this wave's copies of tile t+2 are in flight
+            if (t + 2 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI_MIN));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            full_barrier_lds_only_after_wait();
+        }
+    };
+    if (FP8) {
+        for (int t = 0; t < ntiles; t += 2) {
+            tile(t, stage_a, stage_b);
+            if (t + 1 < ntiles) tile(t + 1, stage_b, stage_a);
+        }
+    } else {
+        // tile t reads buffer t % 3 and copies tile t+2 into buffer (t+2) % 3
+        for (int t = 0; t < ntiles; t += 3) {
+            tile(t, stage_a, stage_c);
+            if (t + 1 < ntiles) tile(t + 1, stage_b, stage_a);
+            if (t + 2 < ntiles) tile(t + 2, stage_c, stage_b);
+        }
     }
 
     // ---- epilogue: this wave owns d_v tiles [half*ND, half*ND + ND) of head `head`
@@ -345,8 +388,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 template <int NP, int DQK, int DV, bool SEPV, bool FP8>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-    using S = AttnShape<DQK, DV, SEPV, FP8>;
-    const size_t lds = 2 * (size_t)S::BUF + (size_t)2 * NP * 32 * 32 * sizeof(float);
+    const size_t lds = (size_t)2 * NP * 4096 + (size_t)a.split_len * 8;
     auto kern = k_sparse_attn<NP, DQK, DV, SEPV, FP8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

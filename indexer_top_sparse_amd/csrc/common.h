@@ -31,14 +31,12 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+// two fp32 -> two bf16 in one word (v_cvt_pk_bf16_f32: round to nearest even), lo first
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    const f32x2v f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -103,30 +101,66 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
     return base + incl - v;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then meets the
+// other waves. Unlike __syncthreads() it does not wait for outstanding global loads, so a
+// global->LDS prefetch into another buffer stays in flight across it. The signal fences keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// LDS barrier for use right after an explicit s_waitcnt on vector memory: waits for this
+// wave's LDS operations, then meets the other waves.
+__device__ __forceinline__ void full_barrier_lds_only_after_wait() { lds_barrier(); }
+
+// The same after all of this wave's global loads (including global->LDS copies) landed.
+__device__ __forceinline__ void full_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- cross-workgroup barrier
 // Workgroups that share one sequence meet here. Co-residency of all of them is guaranteed by
-// the cooperative launch. `count` returns to 0 after every barrier; `gen` only grows. A
-// bounded spin keeps every wave finite: on expiry bit 0 of *err is set and the call returns
-// false (results of that launch are then undefined, and the host can read the flag).
+// the cooperative launch. All data the workgroups exchange (histograms, counts) is written and
+// read only with device-scope atomic operations, which are performed at the device coherence
+// point rather than in a per-XCD L2; so no cache-wide fence is needed. Ordering comes from
+// waiting until every atomic this workgroup issued has completed (s_waitcnt) before arriving,
+// and from reading shared data only after the release has been observed.
+// `count` returns to 0 after every barrier; `gen` only grows. A bounded spin keeps every wave
+// finite: on expiry bit 0 of *err is set and the call returns false (results of that launch
+// are then undefined, and the host can read the flag).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, uint32_t n,
                                               uint32_t *err) {
     __shared__ int s_ok;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics and stores have been performed
     __syncthreads();
     if (threadIdx.x == 0) {
         int ok = 1;
         const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);
         const uint32_t arrived =
-            __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (arrived == n - 1) {
             __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_s_waitcnt(0);  // the reset lands before the release below
+            __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             uint32_t spins = 0;
-            while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-                __builtin_amdgcn_s_sleep(2);
+            while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+                __builtin_amdgcn_s_sleep(1);
                 if (++spins > kSpinLimit) {
                     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     ok = 0;
@@ -134,7 +168,7 @@ __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, ui
                 }
             }
         }
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);
         s_ok = ok;
     }
     __syncthreads();

@@ -92,19 +92,20 @@ struct IdxQuery {
 // holds KS k-steps of 8 bf16 (or, for E4M3, KS/2 chunks of 16 codes).
 template <int DIM, bool FP8>
 struct KeyFrag {
-    static constexpr int NV = FP8 ? DIM / 32 : DIM / 16 / 2;  // 16-byte loads per lane
     u32x4 v[FP8 ? DIM / 64 : DIM / 32];
+    float scale;  // E4M3 row scale (loaded with the codes so that no later load waits on it)
 };
 
 template <int DIM, bool FP8>
 __device__ __forceinline__ void load_key_frag(KeyFrag<DIM, FP8> &f, const uint8_t *keys,
-                                              int64_t row) {
+                                              const float *key_scale, int64_t row) {
     const int g = lane_id() >> 4;
     constexpr int RB = FP8 ? DIM : DIM * 2;  // bytes per key row
     const uint8_t *p = keys + row * RB;
     if (FP8) {
 #pragma unroll
         for (int c = 0; c < DIM / 64; ++c) f.v[c] = ldg16(p + 64 * c + 16 * g);
+        f.scale = key_scale[row];
     } else {
 #pragma unroll
         for (int s = 0; s < DIM / 32; ++s) f.v[s] = ldg16(p + 64 * s + 16 * g);
@@ -175,9 +176,9 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
         int64_t krow;
         cand_row<kTokens>(s, i, a.lp, pos, krow);
         KeyFrag<DIM, FP8> f;
-        load_key_frag<DIM, FP8>(f, a.keys, krow);
+        load_key_frag<DIM, FP8>(f, a.keys, a.key_scale, krow);
         float sc = score_tile<DIM, HT, FP8>(q, f);
-        if (FP8) sc *= a.key_scale[krow];
+        if (FP8) sc *= f.scale;
         if (valid && l < 16) out[i] = sc;
     }
 }
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
-constexpr int kPre = 2;  // key tiles in flight per wave
+constexpr int kPre = 4;  // key tiles in flight per wave
 
 struct SelShared {
     uint32_t hist[kHistBins];
@@ -200,9 +201,40 @@ struct SelShared {
     uint32_t grp[2];
 };
 
+// Per-chunk address table in LDS (built once, so the key stream never waits on a page-table
+// load): for kTokens / kCandidates one entry per page touched by the chunk (row of the page's
+// first token, and for kCandidates the kept block id); for kBlocks one row per candidate.
+template <int MODE>
+struct ChunkRows {
+    int first;          // first page (kTokens / kCandidates) touched by the chunk
+    int32_t *row;       // LDS
+    int32_t *blk;       // LDS (kCandidates)
+
+    __device__ __forceinline__ void cand(const SeqCtx &s, int i, int c0, int lp, int &pos,
+                                         int64_t &r) const {
+        const int P = 1 << lp;
+        if (MODE == kTokens) {
+            pos = i;
+            r = (int64_t)row[(i >> lp) - first] + (i & (P - 1));
+        } else if (MODE == kBlocks) {
+            pos = i;
+            r = row[i - c0];
+        } else {
+            const int j = (i >> lp) - first;
+            const int b = blk[j];
+            pos = b >= 0 ? b * P + (i & (P - 1)) : -1;
+            r = (b >= 0 && pos < s.ctx) ? (int64_t)row[j] + (i & (P - 1)) : -1;
+        }
+    }
+};
+
+__host__ __device__ inline int chunk_table_entries(int mode, int chunk, int lp) {
+    return mode == kBlocks ? chunk : (chunk >> lp) + 2;
+}
+
 template <int DIM, int HT, bool FP8, int MODE>
 __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
-    extern __shared__ uint32_t s_key[];  // [chunk]
+    extern __shared__ uint32_t s_key[];  // [chunk] keys, then the chunk address table
     __shared__ SelShared sh;
     const int tid = threadIdx.x, l = lane_id();
 
@@ -251,6 +283,31 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     const int c1 = min(c0 + a.chunk, s.ncand);
     const int cnt = max(0, c1 - c0);
 
+    // ---- address table of the chunk
+    ChunkRows<MODE> cr;
+    cr.first = c0 >> a.lp;
+    cr.row = reinterpret_cast<int32_t *>(s_key + a.chunk);
+    cr.blk = cr.row + chunk_table_entries(MODE, a.chunk, a.lp);
+    if (cnt > 0) {
+        const int P = 1 << a.lp;
+        if (MODE == kBlocks) {
+            for (int i = tid; i < cnt; i += kSelThreads) cr.row[i] = s.pt[c0 + i];
+        } else {
+            const int npg = ((c1 - 1) >> a.lp) - cr.first + 1;
+            for (int j = tid; j < npg; j += kSelThreads) {
+                const int pg = cr.first + j;
+                if (MODE == kTokens) {
+                    cr.row[j] = s.pt[pg] * P;
+                } else {
+                    const int b = s.blocks[pg];
+                    cr.blk[j] = b;
+                    cr.row[j] = b >= 0 ? s.pt[b] * P : -1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
     // ---- scores of this chunk -> LDS keys (0 = not a candidate)
     if (cnt > 0) {
         IdxQuery<DIM, HT, FP8> q;
@@ -260,17 +317,15 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
         KeyFrag<DIM, FP8> f[kPre];
         int64_t rows[kPre];
-        int poss[kPre];
         auto issue = [&](int slot, int k) {
             const int tt = w + k * kSelWaves;
             int i = c0 + 16 * tt + (l & 15);
             if (k >= my_tiles || i >= c1) i = c0;
             int pos;
             int64_t row;
-            cand_row<MODE>(s, i, a.lp, pos, row);
-            poss[slot] = pos;
+            cr.cand(s, i, c0, a.lp, pos, row);
             rows[slot] = row;
-            load_key_frag<DIM, FP8>(f[slot], a.keys, row < 0 ? 0 : row);
+            load_key_frag<DIM, FP8>(f[slot], a.keys, a.key_scale, row < 0 ? 0 : row);
         };
 #pragma unroll
         for (int k = 0; k < kPre; ++k) issue(k, k);
@@ -282,9 +337,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                     const int tt = w + k * kSelWaves;
                     const int li = 16 * tt + (l & 15);
                     float sc = score_tile<DIM, HT, FP8>(q, f[j]);
-                    const int64_t row = rows[j];
-                    if (FP8 && row >= 0) sc *= a.key_scale[row];
-                    const bool ok = (c0 + li < c1) && row >= 0;
+                    if (FP8) sc *= f[j].scale;
+                    const bool ok = (c0 + li < c1) && rows[j] >= 0;
                     if (l < 16 && c0 + li < c1) s_key[li] = ok ? float_key(sc) : 0u;
                     issue(j, k + kPre);
                 }
@@ -440,7 +494,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 if (take) {
                     int pos;
                     int64_t row;
-                    cand_row<MODE>(s, c0 + i, a.lp, pos, row);
+                    cr.cand(s, c0 + i, c0, a.lp, pos, row);
                     if (dst < (uint32_t)K) out[dst] = pos;
                     ++dst;
                 }
@@ -508,5 +562,10 @@ void *decode_select_kernel(int dim, int heads, bool fp8, int mode) {
 }
 
 size_t decode_select_static_lds() { return sizeof(SelShared); }
+
+size_t decode_select_dynamic_lds(int mode, int chunk, int lp) {
+    const int t = chunk_table_entries(mode, chunk, lp);
+    return 4 * ((size_t)chunk + t + (mode == kCandidates ? t : 0));
+}
 
 }  // namespace sa

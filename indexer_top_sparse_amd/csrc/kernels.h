@@ -94,6 +94,7 @@ hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, 
                               int64_t max_cols, hipStream_t st);
 void *decode_select_kernel(int dim, int heads, bool fp8, int mode);
 size_t decode_select_static_lds();
+size_t decode_select_dynamic_lds(int mode, int chunk, int lp);
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);
 hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, bool fp8,
                               hipStream_t st);

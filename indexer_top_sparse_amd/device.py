@@ -80,6 +80,15 @@ def sparse_attn(dw: DeviceWorkload, idx, ws):
     return out
 
 
+def index_select(dw: DeviceWorkload, ws, idx=None):
+    wl = dw.wl
+    if idx is None:
+        idx = torch.empty((wl.num_seqs, wl.topk), dtype=torch.int32, device=dw.t["q"].device)
+    B.index_select(dw.batch, dw.ix, dw.t["q_idx"], dw.t["w"], wl.topk, idx, ws,
+                   block_k=wl.block_topk)
+    return idx
+
+
 def decode_step(dw: DeviceWorkload, ws, want_idx=True, out=None, idx=None):
     wl = dw.wl
     dev = dw.t["q"].device
