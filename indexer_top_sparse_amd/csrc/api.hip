@@ -107,7 +107,7 @@ sa_status check_kv(const sa_kv *kv) {
 }
 
 int attn_splits(int rows, int k, int heads_q) {
-    const int target = 256;  // workgroups: one per CU (about 100 KB of LDS each)
+    const int target = 512;  // workgroups: two per CU (about 60 KB of LDS each)
     const int per_split = std::max(rows, 1) * attn_hgroups(heads_q);
     int s = std::max(1, (target + per_split - 1) / per_split);
     s = std::min(s, std::max(1, (k + 31) / 32));
@@ -242,10 +242,14 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
             a.idx_out = idx_out;
             a.sync = reinterpret_cast<SelSync *>(ws + L.sync);
             a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+            // The grid never exceeds what the device holds at once (checked above), so every
+            // workgroup becomes resident once the work queued before it has drained and the
+            // waits between workgroups of a sequence end; the waits are also spin-bounded.
+            // A plain launch is used: the cooperative launch API adds a device-wide
+            // synchronisation that costs more than the whole selection at small batch sizes.
             void *args[] = {&a};
-            hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)groups), dim3(threads),
-                                                      args, (unsigned)lds, st);
-            if (e != hipSuccess) return hip_fail(e, "cooperative selection launch");
+            hipError_t e = hipLaunchKernel(kern, dim3((unsigned)groups), dim3(threads), args, lds, st);
+            if (e != hipSuccess) return hip_fail(e, "selection launch");
             return SA_OK;
         }
         chunk = std::max(chunk + 64, (chunk + chunk / 8 + 63) / 64 * 64);

@@ -5,9 +5,9 @@
 // selected indices); "Engineering Path for Day-0 Adaptation of Trillion-Scale Sparse Models on
 // Domestic AI Accelerators" §3.1-§3.2 (non-contiguous access by index; block number + offset).
 //
-// One workgroup = one query row x one split of its index list, 32 query heads per wave. All
-// heads share one KV row (MQA / MLA latent rows), so each gathered row is staged once in LDS
-// and used by every wave:
+// One workgroup = one query row x one head group x one split of its index list. All heads
+// share one KV row (MQA / MLA latent rows), so each gathered row is staged once in LDS and
+// used by every wave:
 //   S^T[tok][head] = K[tok][:] . Q[head][:]          (32x32x16 bf16 MFMA, K from LDS)
 //   online softmax per head (lazy rescaling; a lane holds 16 tokens of one head)
 //   O^T[d][head]  += V^T[d][tok] . P^T[tok][head]    (V^T fragments by transposing LDS reads)
@@ -18,6 +18,9 @@
 namespace sa {
 
 constexpr int kTile = 32;          // gathered rows per iteration
+// floats per lane row of the partial-score exchange: 32 scores + 4 padding, so that the
+// 16-byte accesses of 16 consecutive lanes fall on distinct LDS banks
+constexpr int kPartRow = 36;
 constexpr float kRescale = 8.f;    // log2 growth tolerated before O is rescaled
 
 // LDS row swizzle: 16-byte chunk c of staged row r lives at chunk c ^ swz(r). The XOR only
@@ -32,45 +35,46 @@ struct AttnShape {
     static constexpr int VROW_G = 2 * DV;                // (separate V rows are bf16)
     static constexpr int ROWB_K = 2 * DQK;               // LDS bytes per staged row (bf16)
     static constexpr int ROWB_V = 2 * DV;
-    static constexpr int CPR_K = ROWB_K / 16;            // 16-byte LDS chunks per row
-    static constexpr int CPR_V = SEPV ? ROWB_V / 16 : 0;
     static constexpr int KBUF = kTile * ROWB_K;
     static constexpr int BUF = KBUF + (SEPV ? kTile * ROWB_V : 0);
-    static constexpr int NCHUNK = kTile * (CPR_K + CPR_V);  // LDS chunks per tile
-    // a direct-to-LDS instruction always fills 64 chunks: tiles must be whole instructions
-    static_assert(NCHUNK % 64 == 0, "staged tile must be a multiple of 64 chunks");
+    static constexpr int GCH_K = KROW_G / 16;            // 16-byte global chunks per K row
+    static constexpr int GCH_V = SEPV ? VROW_G / 16 : 0;
+    static constexpr int GCH = kTile * (GCH_K + GCH_V);  // global chunks per tile
 };
 
-// One workgroup = NP wave pairs of one head group; pair p owns query heads
-// [32 (NP hg + p), +32). The two waves of a
-// pair split the QK^T contraction over d (each adds half of the k-steps; the partial scores
-// are exchanged through LDS) and split the PV output over d_v, so each wave holds half of the
-// query fragments and half of the output accumulator.
-template <int NP, int DQK, int DV, bool SEPV, bool FP8>
-__global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
+// One workgroup = one quad of waves for one head group of 32 query heads. The four waves
+// split the QK^T contraction over d (each adds a quarter of the k-steps; the partial scores are
+// exchanged through LDS and summed in the same order by all four) and split the PV output
+// over d_v (a quarter each). Each wave therefore holds a quarter of the query fragments and
+// of the output accumulator, and two workgroups share a CU (two waves per SIMD) with about
+// 60 KB of LDS each; running unsynchronised, the two overlap each other's MFMA, LDS and VALU
+// phases. Gathered rows go global -> registers (one tile ahead) -> the single LDS tile.
+template <int DQK, int DV, bool SEPV, bool FP8>
+__global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
     using S = AttnShape<DQK, DV, SEPV, FP8>;
-    constexpr int NT = 128 * NP;
-    constexpr int KS = DQK / 16 / 2;   // k-steps per wave
-    constexpr int ND = DV / 32 / 2;    // 32-wide d_v tiles per wave
-    constexpr int NWV = 2 * NP;
+    constexpr int NT = 256;
+    constexpr int NWV = 4;
+    constexpr int NQ = 1;
+    constexpr int KSP = DQK / 16 / 4;  // k-steps per wave
+    constexpr int NDP = DV / 32 / 4;   // 32-wide d_v tiles per wave
+    // staging: TPR threads per gathered row; thread (row, j) moves chunks j, j + TPR, ...
+    constexpr int TPR = NT / kTile;
+    constexpr int PER_K = (S::GCH_K + TPR - 1) / TPR;
+    constexpr int PER_V = (S::GCH_V + TPR - 1) / TPR;
+    constexpr int PER = PER_K + PER_V;
+    static_assert(KSP * 64 == DQK && NDP * 128 == DV, "quarters of d and d_v");
 
-    // Staging buffers as separate objects: the loop rotates through them at compile time, so
-    // the compiler can tell that the reads of one never alias the global->LDS copies into the
-    // others and keeps those copies in flight across the reads. bf16 rows use a ring of three
-    // (two tiles in flight); E4M3 rows, staged through registers, use two.
-    __shared__ __attribute__((aligned(16))) uint8_t stage_a[S::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_b[S::BUF];
-    __shared__ __attribute__((aligned(16))) uint8_t stage_c[FP8 ? 16 : S::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[S::BUF];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // dynamic lds: [NWV][32][32] fp32 partial scores | [split_len] int32 slots |
+    // dynamic lds: [NWV][32][kPartRow] fp32 partial scores | [split_len] int32 slots |
     //              [split_len] fp32 row flags (scale or 1; < 0 empty)
     float *s_part = reinterpret_cast<float *>(lds);
-    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + NWV * 4096);
+    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + NWV * 32 * kPartRow * 4);
     float *s_sig = reinterpret_cast<float *>(s_slot + a.split_len);
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int h = l >> 5, lm = l & 31;
-    const int pair = w >> 1, half = w & 1;
+    const int quad = 0, part = w;
     // block -> (row, head group, split); rows vary fastest so that with rows % 8 == 0 all
     // workgroups of one row land on the same XCD (blocks are dealt round-robin over XCDs)
     const int row = blockIdx.x % a.rows;
@@ -97,154 +101,126 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
         s_sig[j] = slot < 0 ? -1.f : (FP8 ? a.kv_scale[slot] : 1.f);
     }
 
-    // query fragments (B operand of S^T = K Q^T): head 32 (NP hg + pair) + l%32,
-    // d = 16s + 8h + e for this wave's k-steps s in [half*KS, half*KS + KS)
-    const int head = 32 * (NP * hg + pair) + lm;
-    u32x4 qf[KS];
+    // query fragments (B operand of S^T = K Q^T): head `head`, d = 16 s + 8 h + e for this
+    // wave's k-steps s in [part * KSP, part * KSP + KSP)
+    const int head = 32 * (NQ * hg + quad) + lm;
+    u32x4 qf[KSP];
     {
         const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + head) * DQK + 8 * h;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qf[s] = head < a.heads_q ? ldg16(qr + 16 * (half * KS + s)) : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < KSP; ++s)
+            qf[s] = head < a.heads_q ? ldg16(qr + 16 * (part * KSP + s)) : u32x4{0u, 0u, 0u, 0u};
     }
+    // Query fragments and the slot table complete here, so that inside the tile loop the only
+    // vector-memory loads in flight are the staging loads of the next tile, which nothing in
+    // the loop body before the staging store waits for.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // slot table ready
 
-    // Gather of tile t into LDS buffer `buf`. bf16 rows go global -> LDS directly (lane i of an
-    // instruction fills LDS chunk base + i; the swizzle is applied on the global side); empty
-    // rows read a zero row. E4M3 rows go through registers and are widened to bf16.
-    constexpr int FP8_CH = kTile * (DQK / 16);  // 16-byte global chunks of a fp8 tile
-    constexpr int FP8_PER = (FP8_CH + NT - 1) / NT;
-    u32x4 stg[FP8 ? FP8_PER : 1];
-    auto gather = [&](int t, uint8_t *base) {
-        const int32_t *slots = s_slot + t * kTile;
-        if (!FP8) {
-            for (int ins = w; ins * 64 < S::NCHUNK; ins += NWV) {
-                const int ch = ins * 64 + l;
-                const bool isv = SEPV && ch >= kTile * S::CPR_K;
-                const int cc = isv ? ch - kTile * S::CPR_K : ch;
-                const int cpr = isv ? S::CPR_V : S::CPR_K;
-                const int r = cc / cpr, c = cc % cpr;
-                const int32_t slot = slots[r];
-                const uint8_t *src = a.zero_row;
-                if (slot >= 0)
-                    src = (isv ? a.vc + (int64_t)slot * S::VROW_G
-                               : a.kc + (int64_t)slot * S::KROW_G) +
-                          16 * (c ^ swz(r));
-                __builtin_amdgcn_global_load_lds(src, (SA_LDS void *)(base + ins * 1024), 16, 0, 0);
-            }
-        } else {
+    // ---- gather: global chunk i of the tile -> registers -> swizzled LDS chunk(s)
+    u32x4 stg[PER];
+    const int srow = tid / TPR, sj = tid % TPR;
+    auto load = [&](int t, u32x4 (&v)[PER]) {
+        const int32_t slot = t < ntiles ? s_slot[t * kTile + srow] : -1;
+        const uint8_t *kr = a.kc + (int64_t)(slot < 0 ? 0 : slot) * S::KROW_G;
+        const uint8_t *vr = SEPV ? a.vc + (int64_t)(slot < 0 ? 0 : slot) * S::VROW_G : nullptr;
 #pragma unroll
-            for (int i = 0; i < FP8_PER; ++i) {
-                const int c = tid + i * NT;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (c < FP8_CH) {
-                    const int r = c / (DQK / 16), col = c % (DQK / 16);
-                    const int32_t slot = slots[r];
-                    if (slot >= 0) v = ldg16(a.kc + (int64_t)slot * S::KROW_G + 16 * col);
-                }
-                stg[i] = v;
-            }
+        for (int i = 0; i < PER; ++i) {
+            const bool isv = i >= PER_K;
+            const int col = sj + TPR * (isv ? i - PER_K : i);
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (slot >= 0 && col < (isv ? S::GCH_V : S::GCH_K))
+                x = ldg16((isv ? vr : kr) + 16 * col);
+            v[i] = x;
         }
     };
-    auto stage_fp8 = [&](uint8_t *kb) {
-        if (FP8) {
+    auto store = [&](const u32x4 (&v)[PER], uint8_t *buf) {
+        const int r = srow, sw = swz(srow);
 #pragma unroll
-            for (int i = 0; i < FP8_PER; ++i) {
-                const int c = tid + i * NT;
-                if (c < FP8_CH) {
-                    const int r = c / (DQK / 16), col = c % (DQK / 16);
-                    const u32x2 q0 = e4m3x4_to_bf16(stg[i][0]), q1 = e4m3x4_to_bf16(stg[i][1]);
-                    const u32x2 q2 = e4m3x4_to_bf16(stg[i][2]), q3 = e4m3x4_to_bf16(stg[i][3]);
-                    uint8_t *rowp = kb + r * S::ROWB_K;
-                    *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col) ^ swz(r))) =
+        for (int i = 0; i < PER; ++i) {
+            const bool isv = i >= PER_K;
+            const int col = sj + TPR * (isv ? i - PER_K : i);
+            if (col < (isv ? S::GCH_V : S::GCH_K)) {
+                uint8_t *rowp = isv ? buf + S::KBUF + r * S::ROWB_V : buf + r * S::ROWB_K;
+                if (FP8) {
+                    // 16 codes -> 16 bf16 (exact); the row scale is applied to logits and P
+                    const u32x2 q0 = e4m3x4_to_bf16(v[i][0]), q1 = e4m3x4_to_bf16(v[i][1]);
+                    const u32x2 q2 = e4m3x4_to_bf16(v[i][2]), q3 = e4m3x4_to_bf16(v[i][3]);
+                    *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col) ^ sw)) =
                         u32x4{q0[0], q0[1], q1[0], q1[1]};
-                    *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col + 1) ^ swz(r))) =
+                    *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col + 1) ^ sw)) =
                         u32x4{q2[0], q2[1], q3[0], q3[1]};
+                } else {
+                    *reinterpret_cast<u32x4 *>(rowp + 16 * (col ^ sw)) = v[i];
                 }
             }
         }
     };
 
-    f32x16 o[ND];
+    f32x16 o[NDP];
 #pragma unroll
-    for (int n = 0; n < ND; ++n)
+    for (int n = 0; n < NDP; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[n][r] = 0.f;
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    __syncthreads();  // slot table ready
-    // this wave's global->LDS copy instructions per tile (the last tile's loads that a wave
-    // may leave in flight at the end-of-tile wait)
-    constexpr int NI_MIN = (S::NCHUNK / 64) / NWV;
+    // prologue: tile 0 into LDS, tile 1 into registers
     if (ntiles > 0) {
-        gather(0, stage_a);
-        if (!FP8 && ntiles > 1) gather(1, stage_b);
-        stage_fp8(stage_a);
-        if (!FP8) {
-            // tile 0 landed (tile 1's copies, issued last, may still be in flight)
-            if (ntiles > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI_MIN));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-        full_barrier_lds_only_after_wait();
+        load(0, stg);
+        store(stg, stage);
+        load(1, stg);
+        lds_barrier();
     }
     const int g = l >> 4, jj = l & 15;
-    auto tile = [&](int t, const uint8_t *kb, uint8_t *next) {
-        // bf16: copy tile t+2 into the buffer of tile t-1 (free since the last barrier);
-        // E4M3: load tile t+1 into registers, widened into `next` at the end
-        if (FP8) {
-            if (t + 1 < ntiles) gather(t + 1, next);
-        } else {
-            if (t + 2 < ntiles) gather(t + 2, next);
-        }
-
-        const uint8_t *vb = SEPV ? kb + S::KBUF : kb;
+    // tile t is in `stage`; the registers hold tile t+1, written into `stage` once every wave
+    // is done with tile t, and then receive the loads of tile t+2
+    for (int t = 0; t < ntiles; ++t) {
+        const uint8_t *cur = stage;
+        const uint8_t *vb = SEPV ? cur + S::KBUF : cur;
         constexpr int VROWB = SEPV ? S::ROWB_V : S::ROWB_K;
-        // ---- partial S^T = K Q^T over this wave's half of d: two independent accumulation
-        //      chains (even / odd k-steps), fragment reads running ahead
-        f32x16 sacc, sacc2;
+        // ---- partial S^T = K Q^T over this wave's quarter of d
+        f32x16 sacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = sacc2[r] = 0.f;
-        const uint8_t *krow = kb + lm * S::ROWB_K;
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        const uint8_t *krow = cur + lm * S::ROWB_K;
         const int sw = swz(lm);
-        auto kfrag = [&](int s) {
-            const int c = 2 * (half * KS + s) + h;
-            return *reinterpret_cast<const u32x4 *>(krow + 16 * (c ^ sw));
-        };
-        u32x4 ka = kfrag(0), kb2 = kfrag(1);
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            const u32x4 a0 = ka, a1 = kb2;
-            if (s + 2 < KS) ka = kfrag(s + 2);
-            if (s + 3 < KS) kb2 = kfrag(s + 3);
-            sacc = mfma32x32x16(a0, qf[s], sacc);
-            if (s + 1 < KS) sacc2 = mfma32x32x16(a1, qf[s + 1], sacc2);
+        for (int s = 0; s < KSP; ++s) {
+            const int c = 2 * (part * KSP + s) + h;
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + 16 * (c ^ sw));
+            sacc = mfma32x32x16(kf, qf[s], sacc);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] += sacc2[r];
-        // exchange partial scores with the other wave of the pair
-        float *mine = s_part + (w * 32 + lm) * 32 + 16 * h;
+        float *mine_s = s_part + (w * 32 + lm) * kPartRow + 16 * h;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4 *>(mine + 4 * q4) =
+            *reinterpret_cast<f32x4 *>(mine_s + 4 * q4) =
                 f32x4{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
         lds_barrier();
-        // both waves add in the same order (a + b == b + a), so their softmax states agree;
-        // logits in the log2 domain, -inf for empty rows
-        const float *theirs = s_part + ((w ^ 1) * 32 + lm) * 32 + 16 * h;
+        // ---- full scores: the quad's four partials summed in the same order by every wave;
+        //      logits in the log2 domain, -inf for empty rows
         const float *sig = s_sig + t * kTile;
         float m_tile = -__builtin_inff();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const f32x4 ov = *reinterpret_cast<const f32x4 *>(theirs + 4 * j);
+            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f32x4 v =
+                    p == part ? f32x4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]}
+                              : *reinterpret_cast<const f32x4 *>(
+                                    s_part + ((quad * 4 + p) * 32 + lm) * kPartRow + 16 * h + 4 * j);
+                sum = p == 0 ? v : sum + v;
+            }
             const f32x4 sv = *reinterpret_cast<const f32x4 *>(sig + 8 * j + 4 * h);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                const float v = (sacc[r] + ov[i]) * a.scale_log2 * (FP8 ? sv[i] : 1.f);
-                sacc[r] = sv[i] < 0.f ? -__builtin_inff() : v;
+                const float x = sum[i] * a.scale_log2 * (FP8 ? sv[i] : 1.f);
+                sacc[r] = sv[i] < 0.f ? -__builtin_inff() : x;
                 m_tile = fmaxf(m_tile, sacc[r]);
             }
         }
-        m_tile = fmaxf(m_tile, __shfl_xor(m_tile, 32, 64));
+        m_tile = max_xor32(m_tile);
         const bool grow = m_tile > m_run + kRescale;
         if (__any(grow)) {
             const float m_new = grow ? m_tile : m_run;
@@ -252,13 +228,12 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
             l_run *= alpha;
 #pragma unroll
-            for (int n = 0; n < ND; ++n)
+            for (int n = 0; n < NDP; ++n)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
             m_run = m_new;
         }
-        // exp2(-inf - m) = 0 for empty rows; m_run is finite once any row was seen, and while
-        // it is -inf every logit is -inf too, which the select below maps to 0
+        // while m_run is -inf every logit seen so far was -inf: p = 0
         const bool none = m_run == -__builtin_inff();
         u32x4 pb[2];
 #pragma unroll
@@ -278,7 +253,7 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
             }
             pb[u] = u32x4{pk[0], pk[1], pk[2], pk[3]};
         }
-        // ---- O^T += V^T P^T over this wave's half of d_v: two 16-token k-steps
+        // ---- O^T += V^T P^T over this wave's quarter of d_v: two 16-token k-steps
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int ra = 16 * u + 4 * (g >> 1) + (jj >> 2), rb = ra + 8;
@@ -286,8 +261,8 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
             const int swa = swz(ra), swb = swz(rb);
             const int byte_in = 8 * (jj & 1);
 #pragma unroll
-            for (int n = 0; n < ND; ++n) {
-                const int c = 4 * (half * ND + n) + 2 * (g & 1) + ((jj & 3) >> 1);
+            for (int n = 0; n < NDP; ++n) {
+                const int c = 4 * (part * NDP + n) + 2 * (g & 1) + ((jj & 3) >> 1);
                 const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (SA_LDS i16x4 *)(va + 16 * (c ^ swa) + byte_in));
                 const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -297,41 +272,24 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
                 o[n] = mfma32x32x16(u32x4{w0[0], w0[1], w1[0], w1[1]}, pb[u], o[n]);
             }
         }
-        if (FP8) {
-            if (t + 1 < ntiles) stage_fp8(next);
-            full_barrier();  // tile t+1 staged; everyone is done with this buffer
-        } else {
-            // tile t+1 has landed once at most this wave's copies of tile t+2 are in flight
-            if (t + 2 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI_MIN));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-            full_barrier_lds_only_after_wait();
-        }
-    };
-    if (FP8) {
-        for (int t = 0; t < ntiles; t += 2) {
-            tile(t, stage_a, stage_b);
-            if (t + 1 < ntiles) tile(t + 1, stage_b, stage_a);
-        }
-    } else {
-        // tile t reads buffer t % 3 and copies tile t+2 into buffer (t+2) % 3
-        for (int t = 0; t < ntiles; t += 3) {
-            tile(t, stage_a, stage_c);
-            if (t + 1 < ntiles) tile(t + 1, stage_b, stage_a);
-            if (t + 2 < ntiles) tile(t + 2, stage_c, stage_b);
-        }
+        // ---- stage tile t+1 (loaded during this tile) and start the loads of tile t+2
+        lds_barrier();  // every wave is done reading tile t
+        if (t + 1 < ntiles) store(stg, stage);
+        load(t + 2, stg);
+        lds_barrier();
     }
 
-    // ---- epilogue: this wave owns d_v tiles [half*ND, half*ND + ND) of head `head`
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    // ---- epilogue: this wave owns d_v tiles [part * NDP, part * NDP + NDP) of head `head`
+    const float l_tot = sum_xor32(l_run);
     if (head >= a.heads_q) return;
     if (a.splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t *orow = a.out + ((int64_t)row * a.heads_q + head) * DV;
 #pragma unroll
-        for (int n = 0; n < ND; ++n)
+        for (int n = 0; n < NDP; ++n)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 32 * (half * ND + n) + 8 * j + 4 * h;
+                const int d = 32 * (part * NDP + n) + 8 * j + 4 * h;
                 u32x2 v = {pack_bf16x2(o[n][4 * j] * inv, o[n][4 * j + 1] * inv),
                            pack_bf16x2(o[n][4 * j + 2] * inv, o[n][4 * j + 3] * inv)};
                 *reinterpret_cast<u32x2 *>(orow + d) = v;
@@ -340,14 +298,14 @@ __global__ __launch_bounds__(128 * NP) void k_sparse_attn(AttnArgs a) {
         const int64_t ph = ((int64_t)row * a.splits + split) * a.heads_q + head;
         float *orow = a.part_o + ph * DV;
 #pragma unroll
-        for (int n = 0; n < ND; ++n)
+        for (int n = 0; n < NDP; ++n)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int d = 32 * (half * ND + n) + 8 * j + 4 * h;
+                const int d = 32 * (part * NDP + n) + 8 * j + 4 * h;
                 *reinterpret_cast<f32x4 *>(orow + d) =
                     f32x4{o[n][4 * j], o[n][4 * j + 1], o[n][4 * j + 2], o[n][4 * j + 3]};
             }
-        if (h == 0 && half == 0) {
+        if (h == 0 && part == 0) {
             a.part_ml[2 * ph] = m_run;
             a.part_ml[2 * ph + 1] = l_tot;
         }
@@ -386,15 +344,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         *reinterpret_cast<uint32_t *>(orow + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
 }
 
-template <int NP, int DQK, int DV, bool SEPV, bool FP8>
+template <int DQK, int DV, bool SEPV, bool FP8>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)2 * NP * 4096 + (size_t)a.split_len * 8;
-    auto kern = k_sparse_attn<NP, DQK, DV, SEPV, FP8>;
+    const size_t lds = (size_t)4 * 32 * kPartRow * 4 + (size_t)a.split_len * 8;
+    auto kern = k_sparse_attn<DQK, DV, SEPV, FP8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.rows * a.splits * a.hgroups)), dim3(128 * NP), lds,
-                       st, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.rows * a.splits * a.hgroups)), dim3(256), lds, st,
+                       a);
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(k_attn_merge<DV>, dim3((unsigned)a.rows, (unsigned)((a.heads_q + 3) / 4)),
@@ -404,19 +362,12 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
 
 hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, bool fp8,
                               hipStream_t st) {
-    const int np = attn_pairs(a.heads_q);
-#define SA_ATTN_NP(DQK, DV, SEPV, FP8)                                         \
-    if (np == 1) return launch_attn_t<1, DQK, DV, SEPV, FP8>(a, st);           \
-    return launch_attn_t<2, DQK, DV, SEPV, FP8>(a, st);
-    if (dqk == 576 && dv == 512 && !sep_v) {
-        if (fp8) { SA_ATTN_NP(576, 512, false, true) }
-        SA_ATTN_NP(576, 512, false, false)
-    }
-    if (dqk == 128 && dv == 128 && !fp8) {
-        if (sep_v) { SA_ATTN_NP(128, 128, true, false) }
-        SA_ATTN_NP(128, 128, false, false)
-    }
-#undef SA_ATTN_NP
+    if (dqk == 576 && dv == 512 && !sep_v)
+        return fp8 ? launch_attn_t<576, 512, false, true>(a, st)
+                   : launch_attn_t<576, 512, false, false>(a, st);
+    if (dqk == 128 && dv == 128 && !fp8)
+        return sep_v ? launch_attn_t<128, 128, true, false>(a, st)
+                     : launch_attn_t<128, 128, false, false>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -61,6 +61,19 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Combine each lane's value with the one 32 lanes away (v_permlane32_swap with itself yields
+// both halves' values in every lane; the results are identical in the two lanes of a pair).
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -71,9 +71,8 @@ struct TopkArgs {
     int32_t *idx;
 };
 
-// Wave pairs per attention workgroup (32 query heads per pair) and head groups per row.
-inline int attn_pairs(int heads_q) { return heads_q > 32 ? 2 : 1; }
-inline int attn_hgroups(int heads_q) { return (heads_q + 32 * attn_pairs(heads_q) - 1) / (32 * attn_pairs(heads_q)); }
+// Head groups per query row: one attention workgroup per 32 query heads.
+inline int attn_hgroups(int heads_q) { return (heads_q + 31) / 32; }
 
 struct AttnArgs {
     int num_seqs, lp, pages_per_seq, heads_q, k, splits, split_len, rows, hgroups;
