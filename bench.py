@@ -16,6 +16,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -33,11 +34,13 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed (code changes only)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "indexer_top_sparse_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            code = re.sub(r"//[^\n]*", "", fh.read())
+        h.update(f.encode() + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -59,6 +62,50 @@ def algorithmic_bytes(wl):
     return {"select": sel, "attention": attn, "step": step}
 
 
+# kernels of each launch the bench times (a launch may consist of several kernels)
+LAUNCH_KERNELS = {"select": ("k_decode_select",), "attention": ("k_sparse_attn", "k_attn_merge")}
+
+
+def write_traffic(workload, csvs, copy_gib):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch).
+
+    Each counter is scaled by the ratio between the bytes a plain device copy of known size moves
+    and what the same counter reads for that copy (the largest __amd_rocclr_copyBuffer dispatch,
+    made by --copy-calibration-gib)."""
+    import csv
+    assert copy_gib > 0, "--copy-calibration-gib must name the calibration copy size"
+    known = copy_gib * 2**30
+    res = {"workload": workload, "source_hash": kernel_source_hash(), "calibration": {},
+           "kernels": {}}
+    per = {}
+    for counter, path in zip(("FETCH_SIZE", "WRITE_SIZE"), csvs):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"]]
+        factor = known / (max(copies) * 1024.0)
+        res["calibration"][counter] = {"copy_bytes": known, "counter_kib": max(copies),
+                                       "factor": factor}
+        for launch, names in LAUNCH_KERNELS.items():
+            tot = 0.0
+            for n in names:
+                vals = [float(r["Counter_Value"]) for r in rows if n in r["Kernel_Name"]]
+                if not vals:
+                    break
+                tot += sum(vals) / len(vals) * 1024.0 * factor
+            else:
+                per.setdefault(launch, {})[counter] = tot
+    for launch, d in per.items():
+        if len(d) == 2:
+            res["kernels"][launch] = {"fetch_bytes": d["FETCH_SIZE"],
+                                      "write_bytes": d["WRITE_SIZE"],
+                                      "hbm_bytes_per_launch": d["FETCH_SIZE"] + d["WRITE_SIZE"]}
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"traffic_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,7 +119,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="also run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--traffic-csv", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-calibration-gib into "
+                         "profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.traffic_csv:
+        write_traffic(args.workload, args.traffic_csv, args.copy_calibration_gib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -138,22 +192,29 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
 
-    # ---- per-kernel durations, measured live on the same stream: the step split into its two
-    #      launches (selection, then attention + split merge) with events between them
-    sel_ms, att_ms = [], []
-    for i in range(args.steps):
-        d = reps[i % len(reps)]
-        a0, a1, a2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a0.record(stream)
-        device.index_select(d, ws, idx=idx)
-        a1.record(stream)
-        B.sparse_attn(d.batch, d.kv, d.t["q"], idx, out, ws)
-        a2.record(stream)
-        sel_ms.append((a0, a1))
-        att_ms.append((a1, a2))
+    # ---- per-kernel durations, measured live on the same stream: K launches of the selection
+    #      alone, then K launches of the attention (plus its split merge) alone, each loop
+    #      bracketed by events; the average includes only the gaps between back-to-back launches
+    idxs = [torch.empty_like(idx) for _ in reps]
+    for r, d in enumerate(reps):
+        device.index_select(d, ws, idx=idxs[r])
     torch.cuda.synchronize()
-    sel_avg = sum(x.elapsed_time(y) for x, y in sel_ms) / len(sel_ms)
-    att_avg = sum(x.elapsed_time(y) for x, y in att_ms) / len(att_ms)
+
+    def timed(fn):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / args.steps
+
+    sel_avg = timed(lambda i: device.index_select(reps[i % len(reps)], ws,
+                                                  idx=idxs[i % len(reps)]))
+    att_avg = timed(lambda i: B.sparse_attn(reps[i % len(reps)].batch, reps[i % len(reps)].kv,
+                                            reps[i % len(reps)].t["q"], idxs[i % len(reps)],
+                                            out, ws))
     assert B.workspace_error(ws) == 0
     log(f"[bench] per launch: select {sel_avg * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us")
 

@@ -144,8 +144,9 @@ __device__ __forceinline__ void full_barrier() {
 }
 
 // ---------------------------------------------------------------- cross-workgroup barrier
-// Workgroups that share one sequence meet here. Co-residency of all of them is guaranteed by
-// the cooperative launch. All data the workgroups exchange (histograms, counts) is written and
+// Workgroups that share one sequence meet here. The launch never holds more workgroups than the
+// device keeps resident at once, so all of them become resident once earlier work has drained.
+// All data the workgroups exchange (histograms, counts) is written and
 // read only with device-scope atomic operations, which are performed at the device coherence
 // point rather than in a per-XCD L2; so no cache-wide fence is needed. Ordering comes from
 // waiting until every atomic this workgroup issued has completed (s_waitcnt) before arriving,

@@ -185,10 +185,10 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 
 // ================================================================ decode selection (fused)
 // One workgroup per chunk of a sequence's candidates; all chunks of all sequences are
-// co-resident (cooperative launch). Scores never leave LDS: they become order-preserving keys
-// and an exact radix select runs over the sequence with per-pass global histograms and a
-// barrier per pass. Selected candidates are written in ascending position order; ties at the
-// threshold go to the lower positions.
+// co-resident (the grid is sized within the device's resident capacity). Scores never leave
+// LDS: they become order-preserving keys and an exact radix select runs over the sequence
+// with per-pass global histograms and a barrier per pass. Selected candidates are written in
+// ascending position order; ties at the threshold go to the lower positions.
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;

@@ -89,7 +89,7 @@ static REAL elem(int fmt, const void *base, int64_t index, float scale_row) {
 
 /*
  * Lightweight indexer: relevance score of one history token for one query token, with
- * head-weight weighting ([CANN] §1 and §2.1; "scoring -- reduction" in [Domestic] §3.1).
+ * head-weight weighting ([CANN] §1 and §2.1; the score-then-reduce step of [Domestic] §3.1).
  * The pages do not write the formula down; this library's definition is
  *     d[h]  = sum_i q_I[h][i] * k_I[t][i]          (i ascending)
  *     s[t]  = sum_h w[h] * max(d[h], 0)            (h ascending)
@@ -140,8 +140,8 @@ int ora_index_scores(int nq, const int32_t *q_seq, const int64_t *q_pos, int hea
 
 /*
  * Coarse stage of hierarchical history-block selection ([SameDay] §3.1; [GPUGuide] §3.1):
- * the same score formula applied to one cached summary row per block ("summary information
- * already held in the cache"). Block j of query r is visible when j * page_size <= q_pos[r];
+ * the same score formula applied to one summary row per block that the cache already keeps,
+ * so no token of an unchosen block is read. Block j of query r is visible when j * page_size <= q_pos[r];
  * its summary row is pooled[page_table[seq][j]] (bf16, [num_pages, dim]).
  * out[r * nblk_cols + j] = block score, -inf for invisible columns.
  */
@@ -219,8 +219,8 @@ int ora_topk(int nrows, int64_t ncols, const REAL *scores, const int64_t *n_vali
 }
 
 /*
- * Fine stage of the hierarchical selection ([SameDay] §3.1: "fine filtering computes only
- * within candidate blocks"): for query r the candidates are the visible tokens of the blocks
+ * Fine stage of the hierarchical selection ([SameDay] §3.1: token scores are computed only
+ * inside the blocks the coarse stage kept): for query r the candidates are the visible tokens of the blocks
  * listed in blocks[r * nblk .. +nblk) (entries < 0 are ignored); their indexer scores are
  * computed with the token formula and the Top-K among them is returned as above.
  */
@@ -264,8 +264,7 @@ int ora_topk_in_blocks(int nq, const int32_t *q_seq, const int64_t *q_pos, int h
 
 /*
  * Sparse attention over the gathered rows of the selected positions ([CANN] §1 and §2.1:
- * the attention "reads the main attention KV precisely according to the selected indices";
- * [Domestic] §3). For query row r, query head h (kv head g = h / (heads_q / heads_kv)):
+ * the attention reads only the KV rows named by the selected indices; [Domestic] §3). For query row r, query head h (kv head g = h / (heads_q / heads_kv)):
  *     l_j = scale * sum_i q[r][h][i] * K(t_j)[g][i]      over selected t_j >= 0
  *     m   = max_j l_j
  *     o   = sum_j exp(l_j - m) * V(t_j)[g] / sum_j exp(l_j - m)
