@@ -127,15 +127,15 @@ sa_status sa_index_score(const sa_batch *batch, const sa_indexer *ix, const void
  * of scores[row][0 .. position] ordered by (score descending, position ascending; -0 equals
  * +0), written in ascending position order and padded with -1 when fewer than k positions are
  * visible. Radix selection, no sort. Scores must not be NaN.
- *   scores device fp32 [rows][ld];  idx device int32 [rows][k];  1 <= k <= 16384.
+ *   scores device fp32 [rows][ld];  idx device int32 [rows][k];  1 <= k <= 65536.
  */
 sa_status sa_topk(const sa_batch *batch, const float *scores, int64_t ld, int32_t k,
                   int32_t *idx, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sa_sparse_attn -- attention of each query row over the rows of its selected positions only
- * ([CANN] §1 and §2.1: the attention reads the KV "precisely according to the selected
- * indices"; [Domestic] §3). For query head g: logits softmax_scale * q[g] . K(t) over the
+ * ([CANN] §1 and §2.1: the attention reads only the KV rows that the index set names;
+ * [Domestic] §3). For query head g: logits softmax_scale * q[g] . K(t) over the
  * selected t, softmax in fp32, o[g] = sum p * V(t) / sum p; an empty selection gives 0.
  *   q   device bf16 [rows][heads_q][dim_qk]
  *   idx device int32 [rows][k]: positions in any order, -1 = unused; every other entry must
@@ -159,6 +159,21 @@ sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
  */
 sa_status sa_index_select(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
                           const float *w, int32_t k, int32_t block_k, int32_t *idx_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sa_block_select -- the coarse stage of hierarchical selection on its own ([SameDay] §3.1:
+ * candidate blocks are shortlisted from summaries the cache already holds; [GPUGuide] §3.1).
+ * Block j (= logical page j) of sequence b is scored with the indexer formula on its summary
+ * row ix->pooled[page_table[b][j]]; the block_k best visible blocks are kept (ties -> lower
+ * block). This is the first launch of the hierarchical path of sa_index_select and
+ * sa_decode_step. One query row per sequence (batch->q_indptr must be NULL).
+ *   q_idx device bf16 [num_seqs][ix->heads][ix->dim];  w device fp32 [num_seqs][ix->heads]
+ *   blocks_out device int32 [num_seqs][block_k]: kept logical block numbers, ascending,
+ *       -1 padded when a sequence has fewer than block_k blocks;  1 <= block_k <= 65536.
+ */
+sa_status sa_block_select(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                          const float *w, int32_t block_k, int32_t *blocks_out,
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*

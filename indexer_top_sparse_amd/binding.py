@@ -44,8 +44,8 @@ class sa_kv(C.Structure):
 
 
 _lib = None
-EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_decode_step",
-           "sa_workspace_size",
+EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
+           "sa_decode_step", "sa_workspace_size",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH):
     lib.sa_topk.argtypes = [pb, P, i64, i32, P, P, sz, P]
     lib.sa_sparse_attn.argtypes = [pb, pk, P, P, i32, P, P, sz, P]
     lib.sa_index_select.argtypes = [pb, pi, P, P, i32, i32, P, P, sz, P]
+    lib.sa_block_select.argtypes = [pb, pi, P, P, i32, P, P, sz, P]
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
@@ -73,8 +74,8 @@ def load(path: str = LIB_PATH):
     lib.sa_status_string.restype = C.c_char_p
     lib.sa_last_error.restype = C.c_char_p
     lib.sa_version.restype = i32
-    for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_decode_step",
-               "sa_workspace_init", "sa_workspace_error"):
+    for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
+               "sa_decode_step", "sa_workspace_init", "sa_workspace_error"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -183,6 +184,12 @@ def index_select(batch: Batch, ix: sa_indexer, q_idx, w, k: int, idx_out, ws, bl
                  stream=None) -> None:
     _check(load().sa_index_select(C.byref(batch.s), C.byref(ix), _ptr(q_idx), _ptr(w), k,
                                   block_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def block_select(batch: Batch, ix: sa_indexer, q_idx, w, block_k: int, blocks_out, ws,
+                 stream=None) -> None:
+    _check(load().sa_block_select(C.byref(batch.s), C.byref(ix), _ptr(q_idx), _ptr(w), block_k,
+                                  _ptr(blocks_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def decode_step(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, out, ws,

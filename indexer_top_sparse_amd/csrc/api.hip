@@ -192,7 +192,7 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
     return std::min(block_k, nblk) * page_size;
 }
 
-// Cooperative launch of the fused selection for one candidate mode.
+// Launch of the fused selection for one candidate mode.
 sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
                      int mode, int k, int block_k, const int32_t *blocks, int32_t *idx_out,
                      uint8_t *ws, const WsLayout &L, hipStream_t st) {
@@ -441,6 +441,20 @@ sa_status sa_index_select(const sa_batch *batch, const sa_indexer *ix, const voi
     if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
     return select_impl(batch, rp, ix, q_idx, w, k, block_k, idx_out, static_cast<uint8_t *>(ws),
                        L, static_cast<hipStream_t>(stream));
+}
+
+sa_status sa_block_select(const sa_batch *batch, const sa_indexer *ix, const void *q_idx,
+                          const float *w, int32_t block_k, int32_t *blocks_out, void *ws,
+                          size_t ws_bytes, void *stream) {
+    RowPlan rp;
+    if (block_k < 1) return fail(SA_ERR_INVALID, "block_k must be in [1, 65536]");
+    sa_status st = check_select(batch, &rp, ix, q_idx, w, block_k, block_k);
+    if (st != SA_OK) return st;
+    if (!blocks_out) return fail(SA_ERR_INVALID, "blocks_out is required");
+    const WsLayout L = ws_layout(batch, rp.rows, nullptr, block_k, block_k);
+    if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
+    return run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks_out,
+                      static_cast<uint8_t *>(ws), L, static_cast<hipStream_t>(stream));
 }
 
 sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,

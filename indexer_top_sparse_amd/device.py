@@ -89,6 +89,15 @@ def index_select(dw: DeviceWorkload, ws, idx=None):
     return idx
 
 
+def block_select(dw: DeviceWorkload, ws, blocks=None):
+    wl = dw.wl
+    if blocks is None:
+        blocks = torch.empty((wl.num_seqs, wl.block_topk), dtype=torch.int32,
+                             device=dw.t["q"].device)
+    B.block_select(dw.batch, dw.ix, dw.t["q_idx"], dw.t["w"], wl.block_topk, blocks, ws)
+    return blocks
+
+
 def decode_step(dw: DeviceWorkload, ws, want_idx=True, out=None, idx=None):
     wl = dw.wl
     dev = dw.t["q"].device

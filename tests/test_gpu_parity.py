@@ -192,20 +192,29 @@ def test_fp8_ragged_small():
 
 
 def test_two_level_small():
-    wl = inputs.make("long1m", num_seqs=2, ctx=[40000, 9000], block_topk=64)
-    _say("two-level B=2 ctx 40000/9000, 64 blocks")
+    """Blocks first (near-tie rule at block level), then tokens against the oracle's fine stage
+    on the GPU's kept blocks; a partial last block and a sequence with fewer blocks than
+    block_k are included."""
+    wl = inputs.make("long1m", num_seqs=3, ctx=[40000, 9000, 3000], block_topk=64)
+    _say("two-level B=3 ctx 40000/9000/3000, 64 blocks")
     dw = device.to_device(wl)
     ws = device.new_workspace(dw)
+    blocks = device.block_select(dw, ws).cpu().numpy()
     out, idx = device.decode_step(dw, ws)
     torch.cuda.synchronize()
     assert binding.workspace_error(ws) == 0
-    ref = oracle.decode_step(wl)
+    bs = oracle.block_scores(wl)
+    nblk = [-(-n // wl.page_size) for n in wl.ctx_lens]
+    ref_blocks = oracle.topk(bs, np.array(nblk), wl.block_topk)
     got = idx.cpu().numpy()
-    for b in range(2):
-        # restrict the comparison to the oracle's token stage on the oracle's blocks
+    ref_tok = oracle.topk_in_blocks(wl, blocks, k=wl.topk)
+    for b, n in enumerate(wl.ctx_lens):
+        msg = check_topk_row(blocks[b], ref_blocks[b], bs[b], nblk[b], wl.block_topk)
+        assert msg == "", f"seq {b} blocks: {msg}"
         s_row = oracle.index_scores(wl, rows=[b])[0]
-        msg = check_topk_row(got[b], ref["idx"][b], s_row, wl.ctx_lens[b], wl.topk)
-        assert msg == "", msg
+        msg = check_topk_row(got[b], ref_tok[b], s_row, n, wl.topk)
+        assert msg == "", f"seq {b} tokens: {msg}"
+    assert np.all(blocks[2, nblk[2]:] == -1)
     err = np.abs(out.float().cpu().numpy() - oracle.sparse_attn(wl, got)).max()
     _say(f"  two-level max abs error {err:.3e}")
     assert err <= 2e-2
