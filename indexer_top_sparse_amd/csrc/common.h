@@ -204,4 +204,11 @@ __device__ __forceinline__ u32x4 ldg16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// The same with the nontemporal hint, for data read exactly once per launch (a streamed key
+// cache): it does not displace reused lines from the caches, and streams of such loads over
+// randomly placed pages reach a higher HBM read rate than plain loads.
+__device__ __forceinline__ u32x4 ldg16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
 }  // namespace sa

@@ -104,12 +104,50 @@ __device__ __forceinline__ void load_key_frag(KeyFrag<DIM, FP8> &f, const uint8_
     const uint8_t *p = keys + row * RB;
     if (FP8) {
 #pragma unroll
-        for (int c = 0; c < DIM / 64; ++c) f.v[c] = ldg16(p + 64 * c + 16 * g);
+        for (int c = 0; c < DIM / 64; ++c) f.v[c] = ldg16_stream(p + 64 * c + 16 * g);
         f.scale = key_scale[row];
     } else {
 #pragma unroll
-        for (int s = 0; s < DIM / 32; ++s) f.v[s] = ldg16(p + 64 * s + 16 * g);
+        for (int s = 0; s < DIM / 32; ++s) f.v[s] = ldg16_stream(p + 64 * s + 16 * g);
     }
+}
+
+// Coalesced key tile of 16 consecutive candidates, as the decode selection streams it: load x
+// of lane l is the 16-byte chunk (l % CPR) of tile row (TPL * x + l / CPR), so every load of a
+// wave covers whole rows (64 contiguous bytes per 4 lanes at least) instead of one 16-byte
+// piece of 16 different rows. Streams of such loads with the nontemporal hint reach a higher
+// HBM rate; a per-wave LDS transpose (tile_to_frag) then yields the MFMA fragments.
+template <int DIM, bool FP8>
+struct KeyTile {
+    static constexpr int RB = FP8 ? DIM : 2 * DIM;  // bytes per key row
+    static constexpr int CPR = RB / 16;             // 16-byte chunks per row
+    static constexpr int NL = RB / 64;              // loads per lane per tile
+    static constexpr int TPL = 64 / CPR;            // tile rows covered by one load
+    static constexpr int RPB = 16 / CPR;            // tile rows per 256-byte LDS line
+    u32x4 v[NL];
+    float scale;  // E4M3 scale of the lane's own candidate (lane l % 16)
+
+    // LDS slot (16-byte units) of chunk c of tile row r. The XOR swizzle makes both access
+    // patterns bank-conflict free: the row-major writes, and the fragment reads in which 16
+    // lanes read the same chunk of 16 different rows.
+    __device__ static __forceinline__ int slot(int r, int c) {
+        return (r / RPB) * 16 + (r % RPB) * CPR + (c ^ ((r / RPB) % CPR));
+    }
+};
+
+// Tile (row-major chunks) -> fragment (lane l: candidate l % 16, chunks 4x + l / 16) through the
+// wave's own 16-row LDS staging area. Only this wave touches `stage`, and LDS operations of a
+// wave complete in order, so no barrier is needed.
+template <int DIM, bool FP8>
+__device__ __forceinline__ void tile_to_frag(const KeyTile<DIM, FP8> &t, u32x4 *stage,
+                                             KeyFrag<DIM, FP8> &f) {
+    using T = KeyTile<DIM, FP8>;
+    const int l = lane_id();
+#pragma unroll
+    for (int x = 0; x < T::NL; ++x) stage[T::slot(T::TPL * x + l / T::CPR, l % T::CPR)] = t.v[x];
+#pragma unroll
+    for (int x = 0; x < T::NL; ++x) f.v[x] = stage[T::slot(l & 15, 4 * x + (l >> 4))];
+    f.scale = t.scale;
 }
 
 // Score of the lane's candidate (lane l % 16; every lane of the 4 groups gets the same value).
@@ -192,7 +230,6 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
-constexpr int kPre = 4;  // key tiles in flight per wave
 
 struct SelShared {
     uint32_t hist[kHistBins];
@@ -228,6 +265,16 @@ struct ChunkRows {
     }
 };
 
+// Row of the first candidate of a 16-aligned tile when all 16 rows are contiguous (pages of at
+// least 16 tokens, modes kTokens / kCandidates); a tile of a dropped block reads rows 0..15.
+template <int MODE>
+__device__ __forceinline__ int64_t tile_base_row(const ChunkRows<MODE> &cr, int i0, int lp) {
+    const int P = 1 << lp;
+    const int j = (i0 >> lp) - cr.first;
+    if (MODE == kCandidates && cr.blk[j] < 0) return 0;
+    return (int64_t)cr.row[j] + (i0 & (P - 1));
+}
+
 __host__ __device__ inline int chunk_table_entries(int mode, int chunk, int lp) {
     return mode == kBlocks ? chunk : (chunk >> lp) + 2;
 }
@@ -236,6 +283,7 @@ template <int DIM, int HT, bool FP8, int MODE>
 __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
     extern __shared__ uint32_t s_key[];  // [chunk] keys, then the chunk address table
     __shared__ SelShared sh;
+    __shared__ u32x4 s_stage[kSelWaves][256];  // per-wave key-tile transpose area (4 KiB)
     const int tid = threadIdx.x, l = lane_id();
 
     // ---- locate this workgroup's (sequence, chunk): chunk counts prefix over sequences
@@ -315,17 +363,35 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int ntiles = (cnt + 15) >> 4;
         const int w = wave_id();
         const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
-        KeyFrag<DIM, FP8> f[kPre];
-        int64_t rows[kPre];
-        auto issue = [&](int slot, int k) {
-            const int tt = w + k * kSelWaves;
-            int i = c0 + 16 * tt + (l & 15);
-            if (k >= my_tiles || i >= c1) i = c0;
+        using KT = KeyTile<DIM, FP8>;
+        constexpr int kPre = 16 / KT::NL;  // tiles in flight per wave: 16 KiB of keys
+        KT f[kPre];
+        u32x4 *stage = s_stage[w];
+        const bool contiguous = MODE != kBlocks && a.lp >= 4;
+        auto lrow = [&](int i) -> int64_t {  // load row of candidate i (row 0 if invalid)
+            if (i >= c1) i = c0;
             int pos;
-            int64_t row;
-            cr.cand(s, i, c0, a.lp, pos, row);
-            rows[slot] = row;
-            load_key_frag<DIM, FP8>(f[slot], a.keys, a.key_scale, row < 0 ? 0 : row);
+            int64_t r;
+            cr.cand(s, i, c0, a.lp, pos, r);
+            return r < 0 ? 0 : r;
+        };
+        auto issue = [&](int slot, int k) {
+            if (k >= my_tiles) return;
+            const int i0 = c0 + 16 * (w + k * kSelWaves);
+            const int64_t base = contiguous ? tile_base_row(cr, i0, a.lp) : 0;
+#pragma unroll
+            for (int x = 0; x < KT::NL; ++x) {
+                const int tr = KT::TPL * x + l / KT::CPR;
+                const int64_t row = contiguous ? base + tr : lrow(i0 + tr);
+                f[slot].v[x] = ldg16_stream(a.keys + row * KT::RB + 16 * (l % KT::CPR));
+            }
+            if (FP8) {
+                const int i = i0 + (l & 15);
+                int pos;
+                int64_t r;
+                cr.cand(s, i < c1 ? i : c0, c0, a.lp, pos, r);
+                f[slot].scale = r >= 0 ? a.key_scale[r] : 1.f;
+            }
         };
 #pragma unroll
         for (int k = 0; k < kPre; ++k) issue(k, k);
@@ -336,11 +402,21 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 if (k < my_tiles) {
                     const int tt = w + k * kSelWaves;
                     const int li = 16 * tt + (l & 15);
-                    float sc = score_tile<DIM, HT, FP8>(q, f[j]);
-                    if (FP8) sc *= f[j].scale;
-                    const bool ok = (c0 + li < c1) && rows[j] >= 0;
-                    if (l < 16 && c0 + li < c1) s_key[li] = ok ? float_key(sc) : 0u;
+                    KeyFrag<DIM, FP8> fr;
+                    tile_to_frag<DIM, FP8>(f[j], stage, fr);
                     issue(j, k + kPre);
+                    float sc = score_tile<DIM, HT, FP8>(q, fr);
+                    if (FP8) sc *= fr.scale;
+                    if (l < 16 && c0 + li < c1) {
+                        bool ok = true;
+                        if (MODE == kCandidates) {
+                            int pos;
+                            int64_t r;
+                            cr.cand(s, c0 + li, c0, a.lp, pos, r);
+                            ok = r >= 0;
+                        }
+                        s_key[li] = ok ? float_key(sc) : 0u;
+                    }
                 }
             }
         }
