@@ -429,6 +429,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     int pbits = 0;
     uint32_t need = 0, total = 0;
     bool exact = false;  // every candidate in the threshold bin is selected
+    uint32_t listn = 0;  // > 0: the threshold bin of the first pass is resolved through the list
     bool ok = true;
     for (int pass = 0; pass < 3; ++pass) {
         const int bits = pass < 2 ? 11 : 10;
@@ -481,6 +482,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         need -= sh.res[4];
         prefix = (prefix << bits) | T;
         pbits += bits;
+        if (pass == 0 && sh.res[5] <= (uint32_t)kListCap) {
+            listn = sh.res[5];  // resolved below with one more exchange
+            break;
+        }
         if (sh.res[5] == need) {
             exact = true;
             break;
@@ -491,7 +496,124 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     const int K = a.k;
     int32_t *out = a.idx_out + (int64_t)seq * K;
     const uint32_t k_eff = min((uint32_t)K, total);
-    if (k_eff > 0) {
+    if (k_eff > 0 && listn > 0) {
+        // ---- the first pass's threshold bin holds few candidates. Each workgroup publishes
+        //      how many of its candidates lie above the bin and appends its candidates in the
+        //      bin to the sequence's list as composites (key << 32 | ~candidate). Composites are
+        //      distinct, and a larger composite means a larger score or, for equal scores, a
+        //      lower candidate index (= lower position). After one exchange every workgroup
+        //      reads the list and finds the exact threshold composite in LDS.
+        uint32_t above = 0, eq = 0;
+        for (int i = tid; i < cnt; i += kSelThreads) {
+            const uint32_t k = s_key[i];
+            if (k == 0u) continue;
+            const uint32_t p = k >> 21;
+            above += p > prefix;
+            eq += p == prefix;
+        }
+        uint32_t above_tot, eq_tot;
+        block_excl_scan<kSelThreads>(above, sh.scan, &above_tot);
+        const uint32_t eq_base = block_excl_scan<kSelThreads>(eq, sh.scan, &eq_tot);
+        if (tid == 0) {
+            sh.res[6] = eq_tot ? fetch_add_agent(&ss->list_n, eq_tot) : 0u;
+            st_agent(&ss->cnt[chunk][0], above_tot);
+        }
+        __syncthreads();
+        {
+            uint32_t o = sh.res[6] + eq_base;
+            for (int i = tid; i < cnt; i += kSelThreads) {
+                const uint32_t k = s_key[i];
+                if (k != 0u && (k >> 21) == prefix)
+                    st_agent64(&ss->list[o++], ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i));
+            }
+        }
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        uint64_t *Ls = reinterpret_cast<uint64_t *>(&s_stage[0][0]);  // kListCap entries
+        for (int j = tid; j < (int)listn; j += kSelThreads) Ls[j] = ld_agent64(&ss->list[j]);
+        if (chunk == 0 && tid == 0) st_agent(&ss->list_n, 0u);  // only the appends used it
+        const uint32_t Ah = tid < chunk ? ld_agent(&ss->cnt[tid][0]) : 0u;
+        uint32_t a_before;
+        block_excl_scan<kSelThreads>(Ah, sh.scan, &a_before);
+        // exact threshold among the list: radix passes over the composites' remaining bits
+        uint64_t pre = prefix;
+        int pb = 11;
+        uint32_t lneed = need;
+        for (;;) {
+            const int bits = min(11, 64 - pb);
+            const int shift = 64 - pb - bits;
+            const int nb = 1 << bits;
+            for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
+            __syncthreads();
+            for (int j = tid; j < (int)listn; j += kSelThreads) {
+                const uint64_t c = Ls[j];
+                if ((c >> (64 - pb)) == pre)
+                    atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+            }
+            __syncthreads();
+            uint32_t hv[4];
+            uint32_t csum = 0;
+            const int top = nb - 4 * tid - 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int b = top - j;
+                hv[j] = b >= 0 ? sh.hist[b] : 0u;
+                csum += hv[j];
+            }
+            uint32_t tot;
+            const uint32_t abv = block_excl_scan<kSelThreads>(csum, sh.scan, &tot);
+            if (tid == 0) sh.res[3] = 0xFFFFFFFFu;
+            __syncthreads();
+            uint32_t run = abv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < lneed && run + hv[j] >= lneed) {
+                    sh.res[3] = (uint32_t)(top - j);
+                    sh.res[4] = run;
+                    sh.res[5] = hv[j];
+                }
+                run += hv[j];
+            }
+            __syncthreads();
+            lneed -= sh.res[4];
+            pre = (pre << bits) | sh.res[3];
+            pb += bits;
+            const bool whole = sh.res[5] == lneed;  // always true once all 64 bits are used
+            __syncthreads();
+            if (whole) break;
+        }
+        // list candidates of earlier workgroups that are selected
+        uint32_t tb = 0;
+        for (int j = tid; j < (int)listn; j += kSelThreads) {
+            const uint64_t c = Ls[j];
+            const uint32_t ci = ~(uint32_t)c;
+            tb += ((c >> (64 - pb)) >= pre) && ci / (uint32_t)a.chunk < (uint32_t)chunk;
+        }
+        uint32_t taken_before, tmp;
+        block_excl_scan<kSelThreads>(tb, sh.scan, &taken_before);
+        auto take = [&](int i) -> bool {
+            const uint32_t k = s_key[i];
+            if (k == 0u) return false;
+            const uint32_t p = k >> 21;
+            if (p != prefix) return p > prefix;
+            const uint64_t c = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i);
+            return (c >> (64 - pb)) >= pre;
+        };
+        // ordered emission: thread t owns local candidates [t*E, t*E + E)
+        const int E = (cnt + kSelThreads - 1) / kSelThreads;
+        const int i0 = min(cnt, tid * E), i1 = min(cnt, i0 + E);
+        uint32_t my_sel = 0;
+        for (int i = i0; i < i1; ++i) my_sel += take(i);
+        uint32_t dst = a_before + taken_before + block_excl_scan<kSelThreads>(my_sel, sh.scan, &tmp);
+        for (int i = i0; i < i1; ++i) {
+            if (take(i)) {
+                int pos;
+                int64_t row;
+                cr.cand(s, c0 + i, c0, a.lp, pos, row);
+                if (dst < (uint32_t)K) out[dst] = pos;
+                ++dst;
+            }
+        }
+    } else if (k_eff > 0) {
         const int sh_bits = 32 - pbits;
         uint32_t above = 0, eq = 0;
         for (int i = tid; i < cnt; i += kSelThreads) {
@@ -581,8 +703,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         for (int j = (int)k_eff + tid; j < K; j += kSelThreads) out[j] = -1;
 
     // ---- leave the histograms zeroed for the next launch. Every histogram read happens
-    //      before the count-exchange barrier; without that barrier (nothing to select) one
-    //      more barrier separates the last reads from the clearing.
+    //      before the count-exchange (or list) barrier; without that barrier (nothing to
+    //      select) one more barrier separates the last reads from the clearing.
     if (k_eff == 0) ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
     for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
         st_agent(&ss->hist[0][0] + i, 0u);

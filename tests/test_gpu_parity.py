@@ -247,3 +247,43 @@ def test_page_permutation_invariance_gpu():
     torch.cuda.synchronize()
     assert torch.equal(outs[0][1], outs[1][1])
     assert torch.equal(outs[0][0], outs[1][0])
+
+
+def test_decode_all_scores_equal():
+    """Zero indexer queries: every score is 0, so the selection is the lowest positions. The
+    long sequence's threshold bin overflows the candidate list (radix passes); the others are
+    resolved through the list."""
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[9000, 3000, 2053], seed_offset=11)
+    wl.q_idx = torch.zeros_like(wl.q_idx)
+    _say("decode: all scores equal, ctx 9000/3000/2053")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    got = idx.cpu().numpy()
+    for b in range(3):
+        np.testing.assert_array_equal(got[b], np.arange(wl.topk, dtype=np.int32))
+    err = np.abs(out.float().cpu().numpy() - oracle.sparse_attn(wl, got)).max()
+    assert err <= 2e-2
+
+
+def test_decode_exact_integer_scores_with_ties():
+    """Keys and queries in {-1, 0, 1} and w = 1/4: every score is exact in fp32 and fp64, with
+    many ties at the threshold, so the index sets must equal the oracle's exactly (lower
+    positions win ties) on both the list path and the radix-pass path."""
+    wl = inputs.make("decode32k", num_seqs=4, ctx=[70000, 20000, 5000, 3001], seed_offset=12)
+    g = torch.Generator().manual_seed(99)
+    wl.idx_keys = torch.randint(-1, 2, wl.idx_keys.shape, generator=g).to(torch.bfloat16)
+    wl.q_idx = torch.randint(-1, 2, wl.q_idx.shape, generator=g).to(torch.bfloat16)
+    wl.w = torch.full_like(wl.w, 0.25)
+    _say("decode: integer scores with ties, ctx 70000/20000/5000/3001")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    ref = oracle.decode_step(wl)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
+    err = np.abs(out.float().cpu().numpy() - ref["out"]).max()
+    assert err <= 2e-2
