@@ -139,7 +139,7 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
         // the split count only grows as rows shrink; size for the larger of the two
         const int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
         L.part_o = off;
-        off = align256(off + sizeof(float) * (size_t)rmax * s * kv->heads_q * kv->dim_v);
+        off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * kv->heads_q * kv->dim_v);
         L.part_ml = off;
         off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * kv->heads_q);
     }
@@ -280,7 +280,7 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     a.zero_row = ws + L.zero;
     a.scale_log2 = kv->softmax_scale * 1.4426950408889634f;
     a.out = static_cast<uint16_t *>(out);
-    a.part_o = reinterpret_cast<float *>(ws + L.part_o);
+    a.part_o = reinterpret_cast<uint16_t *>(ws + L.part_o);
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
     if (rows == 0) return SA_OK;
     hipError_t e = launch_sparse_attn(a, kv->dim_qk, kv->dim_v, kv->v != nullptr,

@@ -295,15 +295,19 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
                 *reinterpret_cast<u32x2 *>(orow + d) = v;
             }
     } else {
+        // partial of this split, normalised by its own sum, in bf16 (the merge weights carry
+        // the sums); empty splits write zeros and l = 0
         const int64_t ph = ((int64_t)row * a.splits + split) * a.heads_q + head;
-        float *orow = a.part_o + ph * DV;
+        uint16_t *orow = a.part_o + ph * DV;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
         for (int n = 0; n < NDP; ++n)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d = 32 * (part * NDP + n) + 8 * j + 4 * h;
-                *reinterpret_cast<f32x4 *>(orow + d) =
-                    f32x4{o[n][4 * j], o[n][4 * j + 1], o[n][4 * j + 2], o[n][4 * j + 3]};
+                u32x2 v = {pack_bf16x2(o[n][4 * j] * inv, o[n][4 * j + 1] * inv),
+                           pack_bf16x2(o[n][4 * j + 2] * inv, o[n][4 * j + 3] * inv)};
+                *reinterpret_cast<u32x2 *>(orow + d) = v;
             }
         if (h == 0 && part == 0) {
             a.part_ml[2 * ph] = m_run;
@@ -312,11 +316,13 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
     }
 }
 
-// Combine split partials: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// Grid: rows x ceil(heads/4); 256 threads = 4 heads x 64 threads x (DV/64) entries.
+// Combine split partials: o = sum_s w_s o_s / sum_s w_s with w_s = 2^(m_s - M) l_s and o_s the
+// split's own normalised output. Grid: rows x ceil(heads/4); 256 threads = 4 heads x 64
+// threads x (DV/64) entries.
 template <int DV>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     constexpr int PER = DV / 64;
+    static_assert(PER % 2 == 0, "whole bf16 pairs per thread");
     const int row = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (head >= a.heads_q) return;
@@ -331,11 +337,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         const int64_t ph = ((int64_t)row * a.splits + s) * a.heads_q + head;
         const float m = a.part_ml[2 * ph], lv = a.part_ml[2 * ph + 1];
         if (lv == 0.f) continue;
-        const float wgt = exp2f(m - M);
-        L += wgt * lv;
-        const float *po = a.part_o + ph * DV + d0;
+        const float wgt = exp2f(m - M) * lv;
+        L += wgt;
+        const uint16_t *po = a.part_o + ph * DV + d0;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += wgt * po[e];
+        for (int e = 0; e < PER; e += 2) {
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(po + e);
+            acc[e] += wgt * bf16_lo(v);
+            acc[e + 1] += wgt * bf16_hi(v);
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     uint16_t *orow = a.out + ((int64_t)row * a.heads_q + head) * DV + d0;

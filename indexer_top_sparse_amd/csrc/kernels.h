@@ -89,7 +89,7 @@ struct AttnArgs {
     const uint8_t *zero_row;  // >= 1152 zero bytes (source of empty staged rows)
     float scale_log2;   // softmax_scale * log2(e)
     uint16_t *out;      // bf16 [rows][heads_q][dv] (splits == 1)
-    float *part_o;      // [rows][splits][heads_q][dv]   (splits > 1)
+    uint16_t *part_o;   // bf16 [rows][splits][heads_q][dv], normalised per split (splits > 1)
     float *part_ml;     // [rows][splits][heads_q][2]
 };
 
