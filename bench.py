@@ -106,6 +106,83 @@ def write_traffic(workload, csvs, copy_gib):
     print(json.dumps(res, indent=1))
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(wl):
+    """Indexer and attention flops of a prefill batch (causal: row i sees positions 0..p_i)."""
+    pos = wl.q_pos()
+    vis = int((pos + 1).sum())
+    idx = 2 * wl.idx_heads * wl.idx_dim * vis
+    k_eff = int(sum(min(wl.topk, int(p) + 1) for p in pos))
+    attn = 2 * wl.heads_q * (wl.dim_qk + wl.dim_v) * k_eff
+    return idx, attn
+
+
+def run_prefill(args):
+    """Prefill: sa_index_score -> sa_topk -> sa_sparse_attn over every query row. Prints one
+    JSON line with the step time and the indexer's MFMA utilisation."""
+    import torch
+
+    from indexer_top_sparse_amd import binding as B
+    from indexer_top_sparse_amd import device, inputs
+
+    B.load()
+    torch.cuda.set_device(0)
+    wl = inputs.make(args.workload)
+    d = device.to_device(wl, "cuda:0")
+    ws = device.new_workspace(d)
+    ncols = max(wl.ctx_lens)
+    rows = wl.num_queries
+    scores = torch.empty((rows, ncols), dtype=torch.float32, device="cuda")
+    idx = torch.empty((rows, wl.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((rows, wl.heads_q, wl.dim_v), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.index_score(d.batch, d.ix, d.t["q_idx"], d.t["w"], scores)
+        B.topk(d.batch, scores, wl.topk, idx)
+        B.sparse_attn(d.batch, d.kv, d.t["q"], idx, out, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t_s = t_k = t_a = 0.0
+    tot = 0.0
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        B.index_score(d.batch, d.ix, d.t["q_idx"], d.t["w"], scores)
+        ev[1].record(stream)
+        B.topk(d.batch, scores, wl.topk, idx)
+        ev[2].record(stream)
+        B.sparse_attn(d.batch, d.kv, d.t["q"], idx, out, ws)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        t_s += ev[0].elapsed_time(ev[1])
+        t_k += ev[1].elapsed_time(ev[2])
+        t_a += ev[2].elapsed_time(ev[3])
+        tot += ev[0].elapsed_time(ev[3])
+    n = args.steps
+    t_s, t_k, t_a, tot = t_s / n, t_k / n, t_a / n, tot / n
+    fi, fa = prefill_flops(wl)
+    res = {
+        "metric": "prefill query tokens/s (indexer GEMM + row Top-K + sparse attn)",
+        "value": rows / (tot * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": args.warmup, "ms_per_step": tot, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {rows} query rows after a "
+                               f"{max(wl.ctx_lens) - rows}-token prefix, K={wl.topk}"},
+        "kernels_ms": {"index_score": t_s, "topk": t_k, "sparse_attn": t_a},
+        "mfma": {"indexer_tflops": fi / (t_s * 1e-3) / 1e12, "indexer_flops": fi,
+                 "attention_tflops": fa / (t_a * 1e-3) / 1e12, "attention_flops": fa,
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "indexer_frac": fi / (t_s * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "attention_frac": fa / (t_a * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +209,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+
+    if args.workload.startswith("prefill"):
+        run_prefill(args)
+        return
 
     import numpy as np
     import torch

@@ -355,6 +355,10 @@ sa_status sa_index_score(const sa_batch *batch, const sa_indexer *ix, const void
     a.key_scale = ix->key_scale;
     a.scores = scores;
     a.ld = ld;
+    a.row_blocks = 0;
+    if (batch->q_indptr)
+        for (int b = 0; b < batch->num_seqs; ++b)
+            a.row_blocks += (batch->q_indptr_host[b + 1] - batch->q_indptr_host[b] + 7) / 8;
     hipError_t e = launch_index_score(a, ix->dim, ix->heads, ix->key_dtype == SA_FP8_E4M3,
                                       rp.rows, ld, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "index score launch");

@@ -221,6 +221,218 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     }
 }
 
+// ============================================================= prefill scores (dense GEMM)
+// Scores of many query rows of one sequence against all of its keys: a GEMM over
+// (query row, head) x token with d_I as the contraction, followed by ReLU, the head weights and
+// the sum over heads ([CANN] §2.1; [Domestic] §3.3: prefill selects over the whole range at
+// once and is dominated by dense matrix work).
+//
+// Workgroup: 8 query rows of one sequence (one per wave) x a range of kPfTokens tokens. A wave
+// keeps its row's query fragments for all heads in registers (A operand of
+// v_mfma_f32_32x32x16_bf16: 32 heads x 16 dims per fragment) and multiplies them with 64-token
+// key tiles (B operand: 16 dims x 32 tokens) that the workgroup stages in LDS, double
+// buffered: E4M3 keys are widened to bf16 on the way (exact). The epilogue applies ReLU and
+// the weights to the 32x32 (head x token) accumulators, sums over heads in registers and with
+// the partner lane, and stores 64 consecutive scores per tile. Positions past a row's own
+// position get -inf.
+constexpr int kPfRows = 8;
+constexpr int kPfTile = 64;
+constexpr int kPfTokens = 8192;
+
+template <int DIM, int MT, bool FP8>
+__global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
+    constexpr int RB = 2 * DIM;                 // LDS bytes per staged key row (bf16)
+    constexpr int CPR = RB / 16;                // 16-byte chunks per staged row
+    constexpr int RPB = 16 / CPR;               // staged rows per 256-byte LDS line
+    constexpr int KS = DIM / 16;                // k-steps
+    constexpr int GRB = FP8 ? DIM : 2 * DIM;    // global bytes per key row
+    constexpr int GCH = kPfTile * GRB / 16;     // global 16-byte chunks per tile
+    constexpr int GPT = (GCH + 511) / 512;      // chunks per thread
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][kPfTile * RB];
+    __shared__ float s_scale[2][kPfTile];
+    __shared__ int32_t s_page[kPfTokens + 1];  // physical page of each page the range touches
+    __shared__ int s_loc[4];
+    auto slot = [](int r, int c) { return (r / RPB) * 16 + (r % RPB) * CPR + (c ^ ((r / RPB) % CPR)); };
+
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    // ---- (sequence, row block) of this workgroup: row blocks counted per sequence
+    if (tid < 64) {
+        uint32_t base = 0;
+        int fs = -1, fb = 0;
+        for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+            const int b = b0 + l;
+            uint32_t nb = 0;
+            if (b < a.num_seqs) nb = (uint32_t)(a.q_indptr[b + 1] - a.q_indptr[b] + kPfRows - 1) / kPfRows;
+            const uint32_t incl = wave_incl_scan(nb);
+            const uint32_t excl = base + incl - nb;
+            if (b < a.num_seqs && blockIdx.x >= excl && blockIdx.x < excl + nb) {
+                fs = b;
+                fb = blockIdx.x - excl;
+            }
+            base += __shfl(incl, 63, 64);
+        }
+        const uint64_t m = __ballot(fs >= 0);
+        const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+        fs = __shfl(fs, src, 64);
+        fb = __shfl(fb, src, 64);
+        if (tid == 0) {
+            s_loc[0] = m ? fs : -1;
+            s_loc[1] = fb;
+        }
+    }
+    __syncthreads();
+    if (s_loc[0] < 0) return;
+    const int seq = s_loc[0];
+    const int q0 = a.q_indptr[seq], q1 = a.q_indptr[seq + 1];
+    const int ctx = a.ctx_lens[seq];
+    const int row0 = q0 + kPfRows * s_loc[1];
+    const int row = row0 + w;
+    const bool live = row < q1;
+    const int pos0 = ctx - (q1 - q0);                   // position of the sequence's first row
+    const int p_row = live ? pos0 + (row - q0) : -1;    // last visible position of this row
+    const int p_max = pos0 + (min(q1, row0 + kPfRows) - 1 - q0);
+    const int64_t tb0 = (int64_t)blockIdx.y * kPfTokens;
+    const int64_t tb1 = min(a.ld, tb0 + kPfTokens);
+    const int32_t *pt = a.page_table + (int64_t)seq * a.pages_per_seq;
+    const int P = 1 << a.lp;
+    float *out = live ? a.scores + (int64_t)row * a.ld : nullptr;
+
+    // ---- query fragments and head weights of this wave's row
+    u32x4 qa[MT][KS];
+    float wv[MT][4][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int hd = 32 * mt + (l & 31);
+        const uint16_t *qr = a.q_idx + ((int64_t)(live ? row : q0) * a.heads + hd) * DIM + 8 * (l >> 5);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qa[mt][s] = (live && hd < a.heads) ? ldg16(qr + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hh = 32 * mt + 8 * j + 4 * (l >> 5) + i;
+                wv[mt][j][i] = (live && hh < a.heads) ? a.w[(int64_t)row * a.heads + hh] : 0.f;
+            }
+    }
+
+    // ---- tiles with work: [tb0, t_end) where t_end covers the last visible position of the
+    //      workgroup's rows; later columns only get -inf
+    const int64_t t_end = min(tb1, (int64_t)p_max + 1);
+    const int ntiles = t_end > tb0 ? (int)((t_end - tb0 + kPfTile - 1) / kPfTile) : 0;
+    // pages of the tokens [tb0, ctx) that the tiles can touch, so that no key address waits
+    // on a global load
+    const int pfirst = (int)(tb0 >> a.lp);
+    if (ntiles > 0) {
+        const int plast = (int)((min(tb1, (int64_t)ctx) - 1) >> a.lp);
+        for (int j = tid; j <= plast - pfirst; j += 512) s_page[j] = pt[pfirst + j];
+    }
+    // query fragments, weights and the page table complete before the loop, so that inside it
+    // the only vector-memory loads in flight are key tiles
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // key tiles move global -> registers two tiles ahead -> LDS (double buffered); two
+    // register sets alternate so that no copy waits on loads in flight
+    u32x4 stA[GPT], stB[GPT];
+    float scA = 1.f, scB = 1.f;
+    auto krow_of = [&](int64_t tok) -> int64_t {  // past the sequence: its last resident row
+        if (tok >= ctx) tok = ctx - 1;
+        return (int64_t)s_page[(int)(tok >> a.lp) - pfirst] * P + (tok & (P - 1));
+    };
+    // t beyond the last tile reloads the last tile (harmless), so the loads are unconditional
+    auto load = [&](int t, u32x4 (&stg)[GPT], float &scl) {
+        const int64_t t0 = tb0 + (int64_t)min(t, ntiles - 1) * kPfTile;
+#pragma unroll
+        for (int g = 0; g < GPT; ++g) {
+            const int c = min(tid + 512 * g, GCH - 1);
+            stg[g] = ldg16(a.keys + krow_of(t0 + c / (GRB / 16)) * GRB + 16 * (c % (GRB / 16)));
+        }
+        if (FP8) scl = a.key_scale[krow_of(t0 + (tid & (kPfTile - 1)))];
+    };
+    auto store = [&](int buf, const u32x4 (&stg)[GPT], float scl) {
+#pragma unroll
+        for (int g = 0; g < GPT; ++g) {
+            const int c = tid + 512 * g;
+            if (c >= GCH) continue;
+            const int r = c / (GRB / 16), gc = c % (GRB / 16);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(kt[buf]);
+            if (FP8) {  // 16 codes -> 16 bf16 = staged chunks 2 gc, 2 gc + 1
+                const u32x2 lo0 = e4m3x4_to_bf16(stg[g][0]), hi0 = e4m3x4_to_bf16(stg[g][1]);
+                const u32x2 lo1 = e4m3x4_to_bf16(stg[g][2]), hi1 = e4m3x4_to_bf16(stg[g][3]);
+                dst[slot(r, 2 * gc)] = u32x4{lo0[0], lo0[1], hi0[0], hi0[1]};
+                dst[slot(r, 2 * gc + 1)] = u32x4{lo1[0], lo1[1], hi1[0], hi1[1]};
+            } else {
+                dst[slot(r, gc)] = stg[g];
+            }
+        }
+        if (FP8 && tid < kPfTile) s_scale[buf][tid] = scl;
+    };
+    auto compute = [&](int t) {
+        const int buf = t & 1;
+        const int64_t t0 = tb0 + (int64_t)t * kPfTile;
+        if (!live) return;
+        float v[2];
+        if (t0 <= p_row) {
+            const u32x4 *kb = reinterpret_cast<const u32x4 *>(kt[buf]);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16 acc[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const u32x4 b = kb[slot(32 * nt + (l & 31), 2 * s + (l >> 5))];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16(qa[mt][s], b, acc[mt]);
+                }
+                float x = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x = fmaf(wv[mt][j][i], fmaxf(acc[mt][4 * j + i], 0.f), x);
+                x = sum_xor32(x);
+                if (FP8) x *= s_scale[buf][32 * nt + (l & 31)];
+                v[nt] = x;
+            }
+        } else {
+            v[0] = v[1] = 0.f;
+        }
+        // lanes 0..31 store tokens t0 + l, lanes 32..63 tokens t0 + 32 + (l - 32)
+        const int64_t tok = t0 + l;
+        const float x = l < 32 ? v[0] : v[1];
+        if (tok < tb1) out[tok] = tok <= p_row ? x : -__builtin_inff();
+    };
+    // step t: `hold` has tile t + 1 (loaded one step earlier), `next` receives tile t + 2. A
+    // step past the last tile computes nothing visible: its columns are past every row's
+    // position and get -inf.
+    auto step = [&](int t, u32x4 (&hold)[GPT], float &sch, u32x4 (&next)[GPT], float &scn) {
+        load(t + 2, next, scn);
+        compute(t);
+        if (t + 1 < ntiles) store((t + 1) & 1, hold, sch);
+        __syncthreads();
+    };
+
+    const int nt2 = (ntiles + 1) & ~1;
+    if (ntiles > 0) {
+        load(0, stA, scA);
+        store(0, stA, scA);
+        load(1, stA, scA);
+    }
+    __syncthreads();
+    for (int t = 0; t < nt2; t += 2) {
+        step(t, stA, scA, stB, scB);
+        step(t + 1, stB, scB, stA, scA);
+    }
+    // ---- columns past every row of the workgroup
+    if (live)
+        for (int64_t tok = tb0 + (int64_t)nt2 * kPfTile + l; tok < tb1; tok += 64)
+            out[tok] = -__builtin_inff();
+}
+
 // ================================================================ decode selection (fused)
 // One workgroup per chunk of a sequence's candidates; all chunks of all sequences are
 // co-resident (the grid is sized within the device's resident capacity). Scores never leave
@@ -719,8 +931,24 @@ static hipError_t launch_score_t(const ScoreArgs &a, int rows, int64_t max_cols,
     return hipGetLastError();
 }
 
+template <int DIM, int MT, bool FP8>
+static hipError_t launch_prefill_t(const ScoreArgs &a, hipStream_t st) {
+    dim3 grid((unsigned)a.row_blocks, (unsigned)((a.ld + kPfTokens - 1) / kPfTokens));
+    hipLaunchKernelGGL((k_prefill_score<DIM, MT, FP8>), grid, dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, int rows,
                               int64_t max_cols, hipStream_t st) {
+    if (a.q_indptr) {  // query rows grouped per sequence: dense GEMM
+        if (a.row_blocks == 0) return hipSuccess;
+        if (dim == 128) {
+            if (heads <= 32) return fp8 ? launch_prefill_t<128, 1, true>(a, st) : launch_prefill_t<128, 1, false>(a, st);
+            return fp8 ? launch_prefill_t<128, 2, true>(a, st) : launch_prefill_t<128, 2, false>(a, st);
+        }
+        if (heads <= 32) return fp8 ? launch_prefill_t<64, 1, true>(a, st) : launch_prefill_t<64, 1, false>(a, st);
+        return fp8 ? launch_prefill_t<64, 2, true>(a, st) : launch_prefill_t<64, 2, false>(a, st);
+    }
     const bool small = heads <= 16;
     if (dim == 128) {
         if (fp8) return small ? launch_score_t<128, 1, true>(a, rows, max_cols, st)

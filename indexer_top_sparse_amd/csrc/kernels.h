@@ -45,6 +45,7 @@ __device__ __forceinline__ void row_info(const int32_t *q_indptr, int num_seqs, 
 
 struct ScoreArgs {
     int num_seqs, lp, pages_per_seq, heads;
+    int row_blocks;  // prefill GEMM: sum over sequences of ceil(query rows / 8)
     const int32_t *page_table, *ctx_lens, *q_indptr;
     const uint16_t *q_idx;
     const float *w;
