@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
 // the partner lane, and stores 64 consecutive scores per tile. Positions past a row's own
 // position get -inf.
 constexpr int kPfRows = 8;
-constexpr int kPfTile = 64;
+constexpr int kPfTile = 128;
 constexpr int kPfTokens = 8192;
 
 template <int DIM, int MT, bool FP8>
@@ -330,10 +330,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
     // the only vector-memory loads in flight are key tiles
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // key tiles move global -> registers two tiles ahead -> LDS (double buffered); two
-    // register sets alternate so that no copy waits on loads in flight
-    u32x4 stA[GPT], stB[GPT];
-    float scA = 1.f, scB = 1.f;
+    // key tiles move global -> registers one tile ahead -> LDS (double buffered)
+    u32x4 stA[GPT];
+    float scA = 1.f;
     auto krow_of = [&](int64_t tok) -> int64_t {  // past the sequence: its last resident row
         if (tok >= ctx) tok = ctx - 1;
         return (int64_t)s_page[(int)(tok >> a.lp) - pfirst] * P + (tok & (P - 1));
@@ -367,14 +366,15 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
         if (FP8 && tid < kPfTile) s_scale[buf][tid] = scl;
     };
     auto compute = [&](int t) {
+        constexpr int NN = kPfTile / 32;  // 32-token MFMA tiles per key tile
         const int buf = t & 1;
         const int64_t t0 = tb0 + (int64_t)t * kPfTile;
         if (!live) return;
-        float v[2];
+        float v[NN];
         if (t0 <= p_row) {
             const u32x4 *kb = reinterpret_cast<const u32x4 *>(kt[buf]);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
+            for (int nt = 0; nt < NN; ++nt) {
                 f32x16 acc[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
@@ -399,37 +399,34 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
                 v[nt] = x;
             }
         } else {
-            v[0] = v[1] = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NN; ++nt) v[nt] = 0.f;
         }
-        // lanes 0..31 store tokens t0 + l, lanes 32..63 tokens t0 + 32 + (l - 32)
-        const int64_t tok = t0 + l;
-        const float x = l < 32 ? v[0] : v[1];
-        if (tok < tb1) out[tok] = tok <= p_row ? x : -__builtin_inff();
+        // 64 consecutive tokens per store: lanes 0..31 hold MFMA tile 2p, lanes 32..63 tile 2p+1
+#pragma unroll
+        for (int pp = 0; pp < NN / 2; ++pp) {
+            const int64_t tok = t0 + 64 * pp + l;
+            const float x = l < 32 ? v[2 * pp] : v[2 * pp + 1];
+            if (tok < tb1) out[tok] = tok <= p_row ? x : -__builtin_inff();
+        }
     };
-    // step t: `hold` has tile t + 1 (loaded one step earlier), `next` receives tile t + 2. A
-    // step past the last tile computes nothing visible: its columns are past every row's
-    // position and get -inf.
-    auto step = [&](int t, u32x4 (&hold)[GPT], float &sch, u32x4 (&next)[GPT], float &scn) {
-        load(t + 2, next, scn);
-        compute(t);
-        if (t + 1 < ntiles) store((t + 1) & 1, hold, sch);
-        __syncthreads();
-    };
-
-    const int nt2 = (ntiles + 1) & ~1;
+    // step t: tile t + 1 moves global -> registers while tile t is computed, then registers
+    // -> the other LDS buffer. Loads are unconditional (a step past the last tile reloads the
+    // last tile), so the wait before the LDS store covers exactly these loads.
     if (ntiles > 0) {
         load(0, stA, scA);
         store(0, stA, scA);
-        load(1, stA, scA);
     }
     __syncthreads();
-    for (int t = 0; t < nt2; t += 2) {
-        step(t, stA, scA, stB, scB);
-        step(t + 1, stB, scB, stA, scA);
+    for (int t = 0; t < ntiles; ++t) {
+        load(t + 1, stA, scA);
+        compute(t);
+        if (t + 1 < ntiles) store((t + 1) & 1, stA, scA);
+        __syncthreads();
     }
     // ---- columns past every row of the workgroup
     if (live)
-        for (int64_t tok = tb0 + (int64_t)nt2 * kPfTile + l; tok < tb1; tok += 64)
+        for (int64_t tok = tb0 + (int64_t)ntiles * kPfTile + l; tok < tb1; tok += 64)
             out[tok] = -__builtin_inff();
 }
 
