@@ -60,6 +60,13 @@ __device__ __forceinline__ uint32_t float_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// max(x, 0) in one instruction: a float with the sign bit set is a negative int32, so the
+// integer max with 0 maps every negative value (and -0) to +0 and keeps the rest. fmaxf would
+// first canonicalise x (a second v_max), which MFMA results never need.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
 // Combine each lane's value with the one 32 lanes away (v_permlane32_swap with itself yields

@@ -177,7 +177,7 @@ __device__ __forceinline__ float score_tile(const IdxQuery<DIM, HT, FP8> &q,
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(q.w[ht][i], fmaxf(acc[ht][i], 0.f), part);
+        for (int i = 0; i < 4; ++i) part = fmaf(q.w[ht][i], relu(acc[ht][i]), part);
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
     return part;
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            x = fmaf(wv[mt][j][i], fmaxf(acc[mt][4 * j + i], 0.f), x);
+                            x = fmaf(wv[mt][j][i], relu(acc[mt][4 * j + i]), x);
                 x = sum_xor32(x);
                 if (FP8) x *= s_scale[buf][32 * nt + (l & 31)];
                 v[nt] = x;
