@@ -67,10 +67,12 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[S::BUF];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // dynamic lds: [NWV][32][kPartRow] fp32 partial scores | [split_len] int32 slots |
-    //              [split_len] fp32 row flags (scale or 1; < 0 empty)
+    //              [split_len] fp32 logit bias (0, or -inf for an empty row) |
+    //              [split_len] fp32 E4M3 row scale (0 for an empty row; E4M3 caches only)
     float *s_part = reinterpret_cast<float *>(lds);
     int32_t *s_slot = reinterpret_cast<int32_t *>(lds + NWV * 32 * kPartRow * 4);
-    float *s_sig = reinterpret_cast<float *>(s_slot + a.split_len);
+    float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
+    float *s_sig = s_bias + a.split_len;
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int h = l >> 5, lm = l & 31;
@@ -98,7 +100,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
             if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
         }
         s_slot[j] = slot;
-        s_sig[j] = slot < 0 ? -1.f : (FP8 ? a.kv_scale[slot] : 1.f);
+        s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
+        if (FP8) s_sig[j] = slot < 0 ? 0.f : a.kv_scale[slot];
     }
 
     // query fragments (B operand of S^T = K Q^T): head `head`, d = 16 s + 8 h + e for this
@@ -120,18 +123,21 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
     // ---- gather: global chunk i of the tile -> registers -> swizzled LDS chunk(s)
     u32x4 stg[PER];
     const int srow = tid / TPR, sj = tid % TPR;
+    // An empty slot (or a tile past the end) stages the workspace's zero row: its logit gets
+    // the -inf bias and its V row contributes 0 * 0. Loads are unconditional wherever a row
+    // divides evenly among its threads.
     auto load = [&](int t, u32x4 (&v)[PER]) {
         const int32_t slot = t < ntiles ? s_slot[t * kTile + srow] : -1;
-        const uint8_t *kr = a.kc + (int64_t)(slot < 0 ? 0 : slot) * S::KROW_G;
-        const uint8_t *vr = SEPV ? a.vc + (int64_t)(slot < 0 ? 0 : slot) * S::VROW_G : nullptr;
+        const uint8_t *kr = slot < 0 ? a.zero_row : a.kc + (int64_t)slot * S::KROW_G;
+        const uint8_t *vr = SEPV ? (slot < 0 ? a.zero_row : a.vc + (int64_t)slot * S::VROW_G)
+                                 : nullptr;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const bool isv = i >= PER_K;
             const int col = sj + TPR * (isv ? i - PER_K : i);
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (slot >= 0 && col < (isv ? S::GCH_V : S::GCH_K))
-                x = ldg16((isv ? vr : kr) + 16 * col);
-            v[i] = x;
+            const int gch = isv ? S::GCH_V : S::GCH_K;
+            const bool even = (isv ? S::GCH_V : S::GCH_K) % TPR == 0;
+            v[i] = (even || col < gch) ? ldg16((isv ? vr : kr) + 16 * col) : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto store = [&](const u32x4 (&v)[PER], uint8_t *buf) {
@@ -196,27 +202,27 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
             *reinterpret_cast<f32x4 *>(mine_s + 4 * q4) =
                 f32x4{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
         lds_barrier();
-        // ---- full scores: the quad's four partials summed in the same order by every wave;
-        //      logits in the log2 domain, -inf for empty rows
+        // ---- full scores: the quad's four partials, all read back from LDS and summed in
+        //      the same order by every wave (identical scores in all four); logits in the log2
+        //      domain as one FMA with the row's bias (-inf for an empty row, whose staged K
+        //      row is zero)
         const float *sig = s_sig + t * kTile;
+        const float *bia = s_bias + t * kTile;
         float m_tile = -__builtin_inff();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+            f32x4 sum = *reinterpret_cast<const f32x4 *>(s_part + ((quad * 4) * 32 + lm) * kPartRow + 16 * h + 4 * j);
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const f32x4 v =
-                    p == part ? f32x4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]}
-                              : *reinterpret_cast<const f32x4 *>(
-                                    s_part + ((quad * 4 + p) * 32 + lm) * kPartRow + 16 * h + 4 * j);
-                sum = p == 0 ? v : sum + v;
-            }
-            const f32x4 sv = *reinterpret_cast<const f32x4 *>(sig + 8 * j + 4 * h);
+            for (int p = 1; p < 4; ++p)
+                sum += *reinterpret_cast<const f32x4 *>(
+                    s_part + ((quad * 4 + p) * 32 + lm) * kPartRow + 16 * h + 4 * j);
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bia + 8 * j + 4 * h);
+            f32x4 sv = {1.f, 1.f, 1.f, 1.f};
+            if (FP8) sv = *reinterpret_cast<const f32x4 *>(sig + 8 * j + 4 * h);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * j + i;
-                const float x = sum[i] * a.scale_log2 * (FP8 ? sv[i] : 1.f);
-                sacc[r] = sv[i] < 0.f ? -__builtin_inff() : x;
+                sacc[r] = fmaf(sum[i], FP8 ? a.scale_log2 * sv[i] : a.scale_log2, bv[i]);
                 m_tile = fmaxf(m_tile, sacc[r]);
             }
         }
@@ -233,8 +239,8 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
                 for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
             m_run = m_new;
         }
-        // while m_run is -inf every logit seen so far was -inf: p = 0
-        const bool none = m_run == -__builtin_inff();
+        // while m_run is -inf every logit seen so far was -inf: subtracting 0 keeps p = 0
+        const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
         u32x4 pb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -245,9 +251,9 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
 #pragma unroll
                 for (int e1 = 0; e1 < 2; ++e1) {
                     const int r = 8 * u + 2 * e2 + e1;
-                    const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[r] - m_run);
+                    const float p = __builtin_amdgcn_exp2f(sacc[r] - m_use);
                     l_run += p;
-                    pp[e1] = FP8 ? p * fmaxf(sig[8 * (r >> 2) + 4 * h + (r & 3)], 0.f) : p;
+                    pp[e1] = FP8 ? p * sig[8 * (r >> 2) + 4 * h + (r & 3)] : p;
                 }
                 pk[e2] = pack_bf16x2(pp[0], pp[1]);
             }
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 template <int DQK, int DV, bool SEPV, bool FP8>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)4 * 32 * kPartRow * 4 + (size_t)a.split_len * 8;
+    const size_t lds = (size_t)4 * 32 * kPartRow * 4 + (size_t)a.split_len * (FP8 ? 12 : 8);
     auto kern = k_sparse_attn<DQK, DV, SEPV, FP8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
