@@ -110,7 +110,9 @@ int attn_splits(int rows, int k, int heads_q) {
     const int target = 512;  // workgroups: two per CU (about 60 KB of LDS each)
     const int per_split = std::max(rows, 1) * attn_hgroups(heads_q);
     int s = std::max(1, (target + per_split - 1) / per_split);
-    s = std::min(s, std::max(1, (k + 31) / 32));
+    // at least 8 tiles of 32 rows per split: below that the merge costs more than the extra
+    // workgroups save
+    s = std::min(s, std::max(1, (k + 255) / 256));
     return s;
 }
 int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }
@@ -192,68 +194,77 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
     return std::min(block_k, nblk) * page_size;
 }
 
-// Launch of the fused selection for one candidate mode.
+// Launches of the fused selection for one candidate mode. All workgroups of a launch must be
+// resident at once (they wait for each other), so a launch holds at most the device's resident
+// capacity of workgroups; batches with more sequences than half that capacity are split into
+// consecutive launches.
 sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
                      int mode, int k, int block_k, const int32_t *blocks, int32_t *idx_out,
                      uint8_t *ws, const WsLayout &L, hipStream_t st) {
     const bool fp8 = mode != 1 && ix->key_dtype == SA_FP8_E4M3;
     void *kern = decode_select_kernel(ix->dim, ix->heads, fp8, mode);
     const int threads = 512;
-    const int64_t total = [&] {
-        int64_t t = 0;
-        for (int s = 0; s < b->num_seqs; ++s)
-            t += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
-        return t;
-    }();
+    const int lp = log2i(b->page_size);
     const int cus = device_cus();
-    const char *env = getenv("SA_SELECT_CHUNK");
-    int chunk = env ? std::max(64, atoi(env) / 64 * 64)
-                    : std::max<int>(64, (int)((total / ((int64_t)cus * 4) + 63) / 64 * 64));
-    for (;;) {
-        if (chunk > 32768) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
-        const size_t lds = decode_select_dynamic_lds(mode, chunk, log2i(b->page_size));
-        const int occ = occupancy(kern, threads, lds);
-        if (occ < 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
-        const int64_t cap = (int64_t)occ * cus;
+    const int occ0 = occupancy(kern, threads, decode_select_dynamic_lds(mode, 64, lp));
+    if (occ0 <= 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
+    const int per_launch = std::max(1, occ0 * cus / 2);
+    for (int s0 = 0; s0 < b->num_seqs; s0 += per_launch) {
+        const int nb = std::min(per_launch, b->num_seqs - s0);
+        int64_t total = 0;
+        for (int s = s0; s < s0 + nb; ++s)
+            total += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+        // capacity -> chunks -> LDS -> capacity, until the plan fits what it assumed
+        int occ = occ0, chunk_max = 64;
         int64_t groups = 0;
-        int gmax = 0;
-        for (int s = 0; s < b->num_seqs; ++s) {
-            const int nc = ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
-            const int g = std::max(1, (nc + chunk - 1) / chunk);
-            groups += g;
-            gmax = std::max(gmax, g);
+        size_t lds = 0;
+        for (int iter = 0;; ++iter) {
+            const int spare = occ * cus - nb;
+            if (spare < 0 || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
+            chunk_max = 64;
+            groups = 0;
+            for (int s = s0; s < s0 + nb; ++s) {
+                const int nc = ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+                const int c = sel_chunk(nc, spare, total);
+                chunk_max = std::max(chunk_max, c);
+                groups += sel_groups(nc, c);
+            }
+            lds = decode_select_dynamic_lds(mode, chunk_max, lp);
+            const int o = occupancy(kern, threads, lds);
+            if (o <= 0) return fail(SA_ERR_UNSUPPORTED, "selection chunk exceeds the LDS of a CU");
+            if (o >= occ) break;
+            occ = o;
         }
-        if (occ > 0 && groups <= cap && gmax <= kMaxGroupsPerSeq) {
-            SelectArgs a;
-            a.num_seqs = b->num_seqs;
-            a.lp = log2i(b->page_size);
-            a.pages_per_seq = b->pages_per_seq;
-            a.heads = ix->heads;
-            a.chunk = chunk;
-            a.k = k;
-            a.block_k = block_k;
-            a.page_table = b->page_table;
-            a.ctx_lens = b->ctx_lens;
-            a.blocks = blocks;
-            a.q_idx = static_cast<const uint16_t *>(q_idx);
-            a.w = w;
-            a.keys = static_cast<const uint8_t *>(mode == 1 ? ix->pooled : ix->keys);
-            a.key_scale = ix->key_scale;
-            a.idx_out = idx_out;
-            a.sync = reinterpret_cast<SelSync *>(ws + L.sync);
-            a.err = reinterpret_cast<uint32_t *>(ws + L.err);
-            // The grid never exceeds what the device holds at once (checked above), so every
-            // workgroup becomes resident once the work queued before it has drained and the
-            // waits between workgroups of a sequence end; the waits are also spin-bounded.
-            // A plain launch is used: the cooperative launch API adds a device-wide
-            // synchronisation that costs more than the whole selection at small batch sizes.
-            void *args[] = {&a};
-            hipError_t e = hipLaunchKernel(kern, dim3((unsigned)groups), dim3(threads), args, lds, st);
-            if (e != hipSuccess) return hip_fail(e, "selection launch");
-            return SA_OK;
-        }
-        chunk = std::max(chunk + 64, (chunk + chunk / 8 + 63) / 64 * 64);
+        SelectArgs a;
+        a.num_seqs = nb;
+        a.lp = lp;
+        a.pages_per_seq = b->pages_per_seq;
+        a.heads = ix->heads;
+        a.chunk = chunk_max;
+        a.spare = occ * cus - nb;
+        a.total = total;
+        a.k = k;
+        a.block_k = block_k;
+        a.page_table = b->page_table + (int64_t)s0 * b->pages_per_seq;
+        a.ctx_lens = b->ctx_lens + s0;
+        a.blocks = blocks ? blocks + (int64_t)s0 * block_k : nullptr;
+        a.q_idx = static_cast<const uint16_t *>(q_idx) + (int64_t)s0 * ix->heads * ix->dim;
+        a.w = w + (int64_t)s0 * ix->heads;
+        a.keys = static_cast<const uint8_t *>(mode == 1 ? ix->pooled : ix->keys);
+        a.key_scale = ix->key_scale;
+        a.idx_out = idx_out + (int64_t)s0 * k;
+        a.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
+        a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+        // The grid never exceeds what the device holds at once, so every workgroup becomes
+        // resident once the work queued before it has drained, and the waits between
+        // workgroups of a sequence end; the waits are also spin-bounded. A plain launch is
+        // used: the cooperative launch API adds a device-wide synchronisation that costs more
+        // than the whole selection at small batch sizes.
+        void *args[] = {&a};
+        hipError_t e = hipLaunchKernel(kern, dim3((unsigned)groups), dim3(threads), args, lds, st);
+        if (e != hipSuccess) return hip_fail(e, "selection launch");
     }
+    return SA_OK;
 }
 
 sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,

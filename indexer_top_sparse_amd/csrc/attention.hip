@@ -327,30 +327,47 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
 // threads x (DV/64) entries.
 template <int DV>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-    constexpr int PER = DV / 64;
+    constexpr int PER = DV / 64;      // output entries per thread
+    constexpr int WPS = PER / 2;      // 32-bit words (bf16 pairs) per split and thread
+    constexpr int BATCH = 8;          // splits whose loads are in flight together
     static_assert(PER % 2 == 0, "whole bf16 pairs per thread");
     const int row = blockIdx.x;
     const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (head >= a.heads_q) return;
     const int d0 = (threadIdx.x & 63) * PER;
-    float M = -__builtin_inff();
-    for (int s = 0; s < a.splits; ++s)
-        M = fmaxf(M, a.part_ml[2 * (((int64_t)row * a.splits + s) * a.heads_q + head)]);
-    float L = 0.f, acc[PER];
+    const int64_t ph0 = (int64_t)row * a.splits * a.heads_q + head;  // split s: ph0 + s * heads_q
+    // online combination in split order: running max M, sum L and output (rescaled when M
+    // grows); splits without selected rows (l = 0) are skipped
+    float M = -__builtin_inff(), L = 0.f, acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-        const int64_t ph = ((int64_t)row * a.splits + s) * a.heads_q + head;
-        const float m = a.part_ml[2 * ph], lv = a.part_ml[2 * ph + 1];
-        if (lv == 0.f) continue;
-        const float wgt = exp2f(m - M) * lv;
-        L += wgt;
-        const uint16_t *po = a.part_o + ph * DV + d0;
+    for (int s0 = 0; s0 < a.splits; s0 += BATCH) {
+        float2 ml[BATCH];
+        uint32_t v[BATCH][WPS];
 #pragma unroll
-        for (int e = 0; e < PER; e += 2) {
-            const uint32_t v = *reinterpret_cast<const uint32_t *>(po + e);
-            acc[e] += wgt * bf16_lo(v);
-            acc[e + 1] += wgt * bf16_hi(v);
+        for (int u = 0; u < BATCH; ++u) {
+            ml[u] = float2{-__builtin_inff(), 0.f};
+            if (s0 + u < a.splits) {
+                const int64_t ph = ph0 + (int64_t)(s0 + u) * a.heads_q;
+                ml[u] = *reinterpret_cast<const float2 *>(a.part_ml + 2 * ph);
+                const uint32_t *po = reinterpret_cast<const uint32_t *>(a.part_o + ph * DV + d0);
+#pragma unroll
+                for (int x = 0; x < WPS; ++x) v[u][x] = po[x];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            if (!(ml[u].y > 0.f)) continue;
+            const float mn = fmaxf(M, ml[u].x);
+            const float c = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is accumulated
+            const float wgt = __builtin_amdgcn_exp2f(ml[u].x - mn) * ml[u].y;
+            L = fmaf(L, c, wgt);
+#pragma unroll
+            for (int x = 0; x < WPS; ++x) {
+                acc[2 * x] = fmaf(acc[2 * x], c, wgt * bf16_lo(v[u][x]));
+                acc[2 * x + 1] = fmaf(acc[2 * x + 1], c, wgt * bf16_hi(v[u][x]));
+            }
+            M = mn;
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;

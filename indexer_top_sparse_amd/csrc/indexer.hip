@@ -498,13 +498,15 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- locate this workgroup's (sequence, chunk): chunk counts prefix over sequences
     if (tid < 64) {
         uint32_t base = 0;
-        int found_seq = -1, found_chunk = 0, found_G = 0;
+        int found_seq = -1, found_chunk = 0, found_G = 0, found_len = 64;
         for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
             const int b = b0 + l;
             uint32_t nchunks = 0;
+            int len = 64;
             if (b < a.num_seqs) {
                 const int nc = ncand_of(MODE, a.ctx_lens[b], a.lp, a.block_k);
-                nchunks = max(1, (nc + a.chunk - 1) / a.chunk);
+                len = sel_chunk(nc, a.spare, a.total);
+                nchunks = sel_groups(nc, len);
             }
             const uint32_t incl = wave_incl_scan(nchunks);
             const uint32_t excl = base + incl - nchunks;
@@ -512,6 +514,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 found_seq = b;
                 found_chunk = blockIdx.x - excl;
                 found_G = nchunks;
+                found_len = len;
             }
             base += __shfl(incl, 63, 64);
         }
@@ -521,23 +524,26 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int fs = __shfl(found_seq, src, 64);
         const int fc = __shfl(found_chunk, src, 64);
         const int fg = __shfl(found_G, src, 64);
+        const int fl = __shfl(found_len, src, 64);
         if (tid == 0) {
             sh.res[0] = m ? fs : 0xFFFFFFFFu;
             sh.res[1] = fc;
             sh.res[2] = fg;
+            sh.res[3] = fl;
         }
     }
     __syncthreads();
     if (sh.res[0] == 0xFFFFFFFFu) return;  // grid padding (never co-waited on)
-    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2];
+    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], clen = sh.res[3];
+    __syncthreads();  // sh.res is reused below
     SeqCtx s;
     s.seq = seq;
     s.ctx = a.ctx_lens[seq];
     s.ncand = ncand_of(MODE, s.ctx, a.lp, a.block_k);
     s.pt = a.page_table + (int64_t)seq * a.pages_per_seq;
     s.blocks = MODE == kCandidates ? a.blocks + (int64_t)seq * a.block_k : nullptr;
-    const int c0 = chunk * a.chunk;
-    const int c1 = min(c0 + a.chunk, s.ncand);
+    const int c0 = chunk * clen;
+    const int c1 = min(c0 + clen, s.ncand);
     const int cnt = max(0, c1 - c0);
 
     // ---- address table of the chunk
@@ -795,7 +801,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         for (int j = tid; j < (int)listn; j += kSelThreads) {
             const uint64_t c = Ls[j];
             const uint32_t ci = ~(uint32_t)c;
-            tb += ((c >> (64 - pb)) >= pre) && ci / (uint32_t)a.chunk < (uint32_t)chunk;
+            tb += ((c >> (64 - pb)) >= pre) && ci / (uint32_t)clen < (uint32_t)chunk;
         }
         uint32_t taken_before, tmp;
         block_excl_scan<kSelThreads>(tb, sh.scan, &taken_before);

@@ -287,3 +287,20 @@ def test_decode_exact_integer_scores_with_ties():
     np.testing.assert_array_equal(idx.cpu().numpy(), ref["idx"])
     err = np.abs(out.float().cpu().numpy() - ref["out"]).max()
     assert err <= 2e-2
+
+
+def test_decode_batch_larger_than_one_selection_launch():
+    """300 sequences (more than half the resident capacity of the selection kernel, so the
+    batch runs as several launches) with mixed short lengths, including empty ones."""
+    rng = np.random.default_rng(5)
+    ctx = [int(x) for x in rng.integers(1, 3000, 300)]
+    ctx[7] = 0
+    ctx[150] = 2048
+    wl = inputs.make("decode32k", num_seqs=300, ctx=ctx, seed_offset=13)
+    _say("decode: B=300, ctx 0..3000")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2)
