@@ -107,12 +107,12 @@ sa_status check_kv(const sa_kv *kv) {
 }
 
 int attn_splits(int rows, int k, int heads_q) {
-    const int target = 512;  // workgroups: two per CU (about 60 KB of LDS each)
+    const int target = 256;  // workgroups: one per CU (8 waves, about 100 KB of LDS)
     const int per_split = std::max(rows, 1) * attn_hgroups(heads_q);
     int s = std::max(1, (target + per_split - 1) / per_split);
-    // at least 8 tiles of 32 rows per split: below that the merge costs more than the extra
+    // at least 4 tiles of 32 rows per split: below that the merge costs more than the extra
     // workgroups save
-    s = std::min(s, std::max(1, (k + 255) / 256));
+    s = std::min(s, std::max(1, (k + 127) / 128));
     return s;
 }
 int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }

@@ -1,32 +1,25 @@
 // Sparse attention over the gathered rows of the selected positions, gfx950.
 //
 // "Day0 Inference Support and Performance Optimization for Next-Gen Large Models on Huawei
-// Ascend CANN Architecture" §1 and §2.1 (the attention reads the KV precisely according to the
-// selected indices); "Engineering Path for Day-0 Adaptation of Trillion-Scale Sparse Models on
-// Domestic AI Accelerators" §3.1-§3.2 (non-contiguous access by index; block number + offset).
+// Ascend CANN Architecture" §1 and §2.1 (the attention reads only the KV rows the index set
+// names); "Engineering Path for Day-0 Adaptation of Trillion-Scale Sparse Models on Domestic
+// AI Accelerators" §3.1-§3.2 (non-contiguous access by index; block number + offset).
 //
-// One workgroup = one query row x one head group x one split of its index list. All heads
-// share one KV row (MQA / MLA latent rows), so each gathered row is staged once in LDS and
-// used by every wave:
-//   S^T[tok][head] = K[tok][:] . Q[head][:]          (32x32x16 bf16 MFMA, K from LDS)
-//   online softmax per head (lazy rescaling; a lane holds 16 tokens of one head)
-//   O^T[d][head]  += V^T[d][tok] . P^T[tok][head]    (V^T fragments by transposing LDS reads)
-// Splits write unnormalised partials that k_attn_merge combines.
+// All query heads share one KV row (MQA / MLA latent rows), so each gathered row is staged
+// once in LDS and used by every wave of the workgroup (see k_sparse_attn_pairs). Index sets
+// split over several workgroups publish normalised partials that k_attn_merge combines.
 #include "common.h"
 #include "kernels.h"
 
 namespace sa {
 
 constexpr int kTile = 32;          // gathered rows per iteration
-// floats per lane row of the partial-score exchange: 32 scores + 4 padding, so that the
-// 16-byte accesses of 16 consecutive lanes fall on distinct LDS banks
-constexpr int kPartRow = 36;
 constexpr float kRescale = 8.f;    // log2 growth tolerated before O is rescaled
 
 // LDS row swizzle: 16-byte chunk c of staged row r lives at chunk c ^ swz(r). The XOR only
-// touches the low three chunk bits, so a chunk stays inside its aligned group of 8. This
-// choice keeps both the K-fragment reads (rows 0..31, one chunk each) and the transposing
-// V reads (8 rows x 64 bytes) free of LDS bank conflicts with 1152-byte rows.
+// touches the low three chunk bits, so a chunk stays inside its aligned group of 8. With
+// 1152-byte rows it keeps the K-fragment reads (16 rows, one chunk each) and each 16-lane group
+// of the transposing V reads (4 rows x 32 bytes) free of LDS bank conflicts.
 __device__ __forceinline__ int swz(int r) { return ((r << 1) & 6) ^ ((r >> 2) & 3); }
 
 template <int DQK, int DV, bool SEPV, bool FP8>
@@ -42,43 +35,41 @@ struct AttnShape {
     static constexpr int GCH = kTile * (GCH_K + GCH_V);  // global chunks per tile
 };
 
-// One workgroup = one quad of waves for one head group of 32 query heads. The four waves
-// split the QK^T contraction over d (each adds a quarter of the k-steps; the partial scores are
-// exchanged through LDS and summed in the same order by all four) and split the PV output
-// over d_v (a quarter each). Each wave therefore holds a quarter of the query fragments and
-// of the output accumulator, and two workgroups share a CU (two waves per SIMD) with about
-// 60 KB of LDS each; running unsynchronised, the two overlap each other's MFMA, LDS and VALU
-// phases. Gathered rows go global -> registers (one tile ahead) -> the single LDS tile.
+// One workgroup = 8 waves for one query row, a group of 64 query heads and one split of its
+// index list; one workgroup per CU. Wave w forms pair w / 2 (16 heads) with its partner w ^ 1:
+//   S^T[row][head] = K[row][:] . Q[head][:]   (16x16x32 bf16 MFMA; each wave of a pair adds one
+//                                              half of d, the halves are exchanged through LDS)
+//   online softmax per head (a lane holds 8 rows of one head)
+//   O^T[d][head] += V^T[d][row] . P^T[row][head]  (each wave of a pair owns one half of d_v;
+//                                                  V^T fragments by transposing LDS reads)
+// Gathered rows go global -> registers (one tile ahead) -> one of two LDS tiles, so the store
+// of the next tile overlaps nothing but is covered by a whole tile of loads.
+constexpr int kPairHeads = 64;
+
 template <int DQK, int DV, bool SEPV, bool FP8>
-__global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
     using S = AttnShape<DQK, DV, SEPV, FP8>;
-    constexpr int NT = 256;
-    constexpr int NWV = 4;
-    constexpr int NQ = 1;
-    constexpr int KSP = DQK / 16 / 4;  // k-steps per wave
-    constexpr int NDP = DV / 32 / 4;   // 32-wide d_v tiles per wave
-    // staging: TPR threads per gathered row; thread (row, j) moves chunks j, j + TPR, ...
-    constexpr int TPR = NT / kTile;
+    constexpr int NT = 512;
+    constexpr int KH = DQK / 32 / 2;    // k-steps per wave (half of d)
+    constexpr int DT = DV / 16 / 2;     // 16-wide d_v tiles per wave (half of d_v)
+    static_assert(KH * 64 == DQK && DT * 32 == DV, "halves of d and d_v");
+    constexpr int TPR = NT / kTile;     // staging threads per gathered row
     constexpr int PER_K = (S::GCH_K + TPR - 1) / TPR;
     constexpr int PER_V = (S::GCH_V + TPR - 1) / TPR;
     constexpr int PER = PER_K + PER_V;
-    static_assert(KSP * 64 == DQK && NDP * 128 == DV, "quarters of d and d_v");
+    constexpr int VROWB = SEPV ? S::ROWB_V : S::ROWB_K;
 
-    __shared__ __attribute__((aligned(16))) uint8_t stage[S::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[2][S::BUF];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // dynamic lds: [NWV][32][kPartRow] fp32 partial scores | [split_len] int32 slots |
-    //              [split_len] fp32 logit bias (0, or -inf for an empty row) |
-    //              [split_len] fp32 E4M3 row scale (0 for an empty row; E4M3 caches only)
-    float *s_part = reinterpret_cast<float *>(lds);
-    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + NWV * 32 * kPartRow * 4);
+    // dynamic lds: [4 pairs][2 halves][2][64 lanes] f32x4 partial scores | [split_len] int32
+    // slots | [split_len] fp32 logit bias (0 or -inf) | [split_len] fp32 E4M3 scale (E4M3 only)
+    f32x4 *s_x = reinterpret_cast<f32x4 *>(lds);
+    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + 4 * 2 * 2 * 64 * 16);
     float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
     float *s_sig = s_bias + a.split_len;
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-    const int h = l >> 5, lm = l & 31;
-    const int quad = 0, part = w;
-    // block -> (row, head group, split); rows vary fastest so that with rows % 8 == 0 all
-    // workgroups of one row land on the same XCD (blocks are dealt round-robin over XCDs)
+    const int pair = w >> 1, half = w & 1, g = l >> 4, L = l & 15;
     const int row = blockIdx.x % a.rows;
     const int hg = (blockIdx.x / a.rows) % a.hgroups;
     const int split = blockIdx.x / (a.rows * a.hgroups);
@@ -91,8 +82,7 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
     const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
     const int P = 1 << a.lp;
 
-    // ---- slot and flag of every selected row of this split (the loop below then issues no
-    //      dependent global loads)
+    // ---- slot, bias and scale of every selected row of this split
     for (int j = tid; j < ntiles * kTile; j += NT) {
         int32_t slot = -1;
         if (j0 + j < j1) {
@@ -103,30 +93,26 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
         s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
         if (FP8) s_sig[j] = slot < 0 ? 0.f : a.kv_scale[slot];
     }
-
-    // query fragments (B operand of S^T = K Q^T): head `head`, d = 16 s + 8 h + e for this
-    // wave's k-steps s in [part * KSP, part * KSP + KSP)
-    const int head = 32 * (NQ * hg + quad) + lm;
-    u32x4 qf[KSP];
+    // query fragments (B operand of S^T = K Q^T): head L of the pair, d = 32 s + 8 g + e for
+    // this wave's half of the k-steps
+    const int head = kPairHeads * hg + 16 * pair + L;
+    const bool live = head < a.heads_q;
+    u32x4 qf[KH];
     {
-        const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + head) * DQK + 8 * h;
+        const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + (live ? head : 0)) * DQK + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KSP; ++s)
-            qf[s] = head < a.heads_q ? ldg16(qr + 16 * (part * KSP + s)) : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < KH; ++s)
+            qf[s] = live ? ldg16(qr + 32 * (half * KH + s)) : u32x4{0u, 0u, 0u, 0u};
     }
-    // Query fragments and the slot table complete here, so that inside the tile loop the only
-    // vector-memory loads in flight are the staging loads of the next tile, which nothing in
-    // the loop body before the staging store waits for.
+    // query fragments and the slot table complete here, so that inside the loop the only
+    // vector-memory loads in flight are gathered rows
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // slot table ready
+    __syncthreads();
 
-    // ---- gather: global chunk i of the tile -> registers -> swizzled LDS chunk(s)
+    // ---- gather: thread (row srow, j = sj) moves global chunks j, j + TPR, ... of its row
     u32x4 stg[PER];
     const int srow = tid / TPR, sj = tid % TPR;
-    // An empty slot (or a tile past the end) stages the workspace's zero row: its logit gets
-    // the -inf bias and its V row contributes 0 * 0. Loads are unconditional wherever a row
-    // divides evenly among its threads.
-    auto load = [&](int t, u32x4 (&v)[PER]) {
+    auto load = [&](int t) {
         const int32_t slot = t < ntiles ? s_slot[t * kTile + srow] : -1;
         const uint8_t *kr = slot < 0 ? a.zero_row : a.kc + (int64_t)slot * S::KROW_G;
         const uint8_t *vr = SEPV ? (slot < 0 ? a.zero_row : a.vc + (int64_t)slot * S::VROW_G)
@@ -137,10 +123,10 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
             const int col = sj + TPR * (isv ? i - PER_K : i);
             const int gch = isv ? S::GCH_V : S::GCH_K;
             const bool even = (isv ? S::GCH_V : S::GCH_K) % TPR == 0;
-            v[i] = (even || col < gch) ? ldg16((isv ? vr : kr) + 16 * col) : u32x4{0u, 0u, 0u, 0u};
+            stg[i] = (even || col < gch) ? ldg16((isv ? vr : kr) + 16 * col) : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    auto store = [&](const u32x4 (&v)[PER], uint8_t *buf) {
+    auto store = [&](uint8_t *buf) {
         const int r = srow, sw = swz(srow);
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -150,172 +136,146 @@ __global__ __launch_bounds__(256, 2) void k_sparse_attn(AttnArgs a) {
                 uint8_t *rowp = isv ? buf + S::KBUF + r * S::ROWB_V : buf + r * S::ROWB_K;
                 if (FP8) {
                     // 16 codes -> 16 bf16 (exact); the row scale is applied to logits and P
-                    const u32x2 q0 = e4m3x4_to_bf16(v[i][0]), q1 = e4m3x4_to_bf16(v[i][1]);
-                    const u32x2 q2 = e4m3x4_to_bf16(v[i][2]), q3 = e4m3x4_to_bf16(v[i][3]);
+                    const u32x2 q0 = e4m3x4_to_bf16(stg[i][0]), q1 = e4m3x4_to_bf16(stg[i][1]);
+                    const u32x2 q2 = e4m3x4_to_bf16(stg[i][2]), q3 = e4m3x4_to_bf16(stg[i][3]);
                     *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col) ^ sw)) =
                         u32x4{q0[0], q0[1], q1[0], q1[1]};
                     *reinterpret_cast<u32x4 *>(rowp + 16 * ((2 * col + 1) ^ sw)) =
                         u32x4{q2[0], q2[1], q3[0], q3[1]};
                 } else {
-                    *reinterpret_cast<u32x4 *>(rowp + 16 * (col ^ sw)) = v[i];
+                    *reinterpret_cast<u32x4 *>(rowp + 16 * (col ^ sw)) = stg[i];
                 }
             }
         }
     };
 
-    f32x16 o[NDP];
+    f32x4 o[DT];
 #pragma unroll
-    for (int n = 0; n < NDP; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[n][r] = 0.f;
+    for (int n = 0; n < DT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    // prologue: tile 0 into LDS, tile 1 into registers
     if (ntiles > 0) {
-        load(0, stg);
-        store(stg, stage);
-        load(1, stg);
-        lds_barrier();
+        load(0);
+        store(stage[0]);
+        load(1);
     }
-    const int g = l >> 4, jj = l & 15;
-    // tile t is in `stage`; the registers hold tile t+1, written into `stage` once every wave
-    // is done with tile t, and then receive the loads of tile t+2
+    __syncthreads();
+
     for (int t = 0; t < ntiles; ++t) {
-        const uint8_t *cur = stage;
-        const uint8_t *vb = SEPV ? cur + S::KBUF : cur;
-        constexpr int VROWB = SEPV ? S::ROWB_V : S::ROWB_K;
-        // ---- partial S^T = K Q^T over this wave's quarter of d
-        f32x16 sacc;
+        const uint8_t *kb = stage[t & 1];
+        const uint8_t *vb = SEPV ? kb + S::KBUF : kb;
+        // the other buffer held tile t - 1, whose reads ended before the last barrier
+        if (t + 1 < ntiles) store(stage[(t + 1) & 1]);
+        load(t + 2);
+        // ---- partial S^T over this wave's half of d: two 16-row M tiles
+        f32x4 sa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        const uint8_t *krow = cur + lm * S::ROWB_K;
-        const int sw = swz(lm);
+        for (int s = 0; s < KH; ++s)
 #pragma unroll
-        for (int s = 0; s < KSP; ++s) {
-            const int c = 2 * (part * KSP + s) + h;
-            const u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + 16 * (c ^ sw));
-            sacc = mfma32x32x16(kf, qf[s], sacc);
-        }
-        float *mine_s = s_part + (w * 32 + lm) * kPartRow + 16 * h;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            *reinterpret_cast<f32x4 *>(mine_s + 4 * q4) =
-                f32x4{sacc[4 * q4], sacc[4 * q4 + 1], sacc[4 * q4 + 2], sacc[4 * q4 + 3]};
-        lds_barrier();
-        // ---- full scores: the quad's four partials, all read back from LDS and summed in
-        //      the same order by every wave (identical scores in all four); logits in the log2
-        //      domain as one FMA with the row's bias (-inf for an empty row, whose staged K
-        //      row is zero)
-        const float *sig = s_sig + t * kTile;
-        const float *bia = s_bias + t * kTile;
-        float m_tile = -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f32x4 sum = *reinterpret_cast<const f32x4 *>(s_part + ((quad * 4) * 32 + lm) * kPartRow + 16 * h + 4 * j);
-#pragma unroll
-            for (int p = 1; p < 4; ++p)
-                sum += *reinterpret_cast<const f32x4 *>(
-                    s_part + ((quad * 4 + p) * 32 + lm) * kPartRow + 16 * h + 4 * j);
-            const f32x4 bv = *reinterpret_cast<const f32x4 *>(bia + 8 * j + 4 * h);
-            f32x4 sv = {1.f, 1.f, 1.f, 1.f};
-            if (FP8) sv = *reinterpret_cast<const f32x4 *>(sig + 8 * j + 4 * h);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * j + i;
-                sacc[r] = fmaf(sum[i], FP8 ? a.scale_log2 * sv[i] : a.scale_log2, bv[i]);
-                m_tile = fmaxf(m_tile, sacc[r]);
+            for (int mt = 0; mt < 2; ++mt) {
+                const int r = 16 * mt + L;
+                const u32x4 kf = *reinterpret_cast<const u32x4 *>(
+                    kb + r * S::ROWB_K + 16 * ((4 * (half * KH + s) + g) ^ swz(r)));
+                sa[mt] = mfma16x16x32(kf, qf[s], sa[mt]);
             }
+        // ---- exchange halves with the partner wave (float addition commutes, so both waves
+        //      obtain the same sums)
+        f32x4 *xo = s_x + ((pair * 2 + half) * 2) * 64 + l;
+        xo[0] = sa[0];
+        xo[64] = sa[1];
+        lds_barrier();
+        const f32x4 *xp = s_x + ((pair * 2 + (half ^ 1)) * 2) * 64 + l;
+        const f32x4 sum0 = sa[0] + xp[0], sum1 = sa[1] + xp[64];
+        // ---- logits in the log2 domain: rows 16 mt + 4 g + i of head L
+        const float *bia = s_bias + t * kTile + 4 * g;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bia);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bia + 16);
+        f32x4 sg0 = {1.f, 1.f, 1.f, 1.f}, sg1 = {1.f, 1.f, 1.f, 1.f};
+        if (FP8) {
+            sg0 = *reinterpret_cast<const f32x4 *>(s_sig + t * kTile + 4 * g);
+            sg1 = *reinterpret_cast<const f32x4 *>(s_sig + t * kTile + 4 * g + 16);
         }
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = fmaf(sum0[i], FP8 ? a.scale_log2 * sg0[i] : a.scale_log2, b0[i]);
+            x[4 + i] = fmaf(sum1[i], FP8 ? a.scale_log2 * sg1[i] : a.scale_log2, b1[i]);
+        }
+        float m_tile = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        m_tile = fmaxf(m_tile, __shfl_xor(m_tile, 16, 64));
         m_tile = max_xor32(m_tile);
         const bool grow = m_tile > m_run + kRescale;
         if (__any(grow)) {
             const float m_new = grow ? m_tile : m_run;
-            // alpha = 0 when m_run = -inf (nothing accumulated yet)
             const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
             l_run *= alpha;
 #pragma unroll
-            for (int n = 0; n < NDP; ++n)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[n][r] *= alpha;
+            for (int n = 0; n < DT; ++n) o[n] *= alpha;
             m_run = m_new;
         }
-        // while m_run is -inf every logit seen so far was -inf: subtracting 0 keeps p = 0
         const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
-        u32x4 pb[2];
+        float p[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float pp[2];
-#pragma unroll
-                for (int e1 = 0; e1 < 2; ++e1) {
-                    const int r = 8 * u + 2 * e2 + e1;
-                    const float p = __builtin_amdgcn_exp2f(sacc[r] - m_use);
-                    l_run += p;
-                    pp[e1] = FP8 ? p * sig[8 * (r >> 2) + 4 * h + (r & 3)] : p;
-                }
-                pk[e2] = pack_bf16x2(pp[0], pp[1]);
-            }
-            pb[u] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+            l_run += p[e];
         }
-        // ---- O^T += V^T P^T over this wave's quarter of d_v: two 16-token k-steps
+        if (FP8) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int ra = 16 * u + 4 * (g >> 1) + (jj >> 2), rb = ra + 8;
-            const uint8_t *va = vb + ra * VROWB, *vbp = vb + rb * VROWB;
-            const int swa = swz(ra), swb = swz(rb);
-            const int byte_in = 8 * (jj & 1);
-#pragma unroll
-            for (int n = 0; n < NDP; ++n) {
-                const int c = 4 * (part * NDP + n) + 2 * (g & 1) + ((jj & 3) >> 1);
-                const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (SA_LDS i16x4 *)(va + 16 * (c ^ swa) + byte_in));
-                const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (SA_LDS i16x4 *)(vbp + 16 * (c ^ swb) + byte_in));
-                const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
-                const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-                o[n] = mfma32x32x16(u32x4{w0[0], w0[1], w1[0], w1[1]}, pb[u], o[n]);
+            for (int i = 0; i < 4; ++i) {
+                p[i] *= sg0[i];
+                p[4 + i] *= sg1[i];
             }
         }
-        // ---- stage tile t+1 (loaded during this tile) and start the loads of tile t+2
-        lds_barrier();  // every wave is done reading tile t
-        if (t + 1 < ntiles) store(stg, stage);
-        load(t + 2, stg);
-        lds_barrier();
+        // P^T B operand: k = 8 g + e <-> row 4 g + (e % 4) + 16 (e / 4), the lane's own rows
+        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        // ---- O^T += V^T P^T over this wave's half of d_v. Transposing reads: input lane j of
+        //      group g loads columns [4 (j % 4), +4) of row base + j / 4; output lane L then
+        //      holds column L of rows base .. base + 3.
+        const int vr1 = 4 * g + (L >> 2), vr2 = 16 + vr1;
+        const uint8_t *va = vb + vr1 * VROWB, *vbp = vb + vr2 * VROWB;
+        const int sw1 = swz(vr1), sw2 = swz(vr2);
+        const int byte_in = 8 * ((L & 3) & 1);
+#pragma unroll
+        for (int n = 0; n < DT; ++n) {
+            const int c = (half * (DV / 2) + 16 * n) / 8 + ((L & 3) >> 1);
+            const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SA_LDS i16x4 *)(va + 16 * (c ^ sw1) + byte_in));
+            const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (SA_LDS i16x4 *)(vbp + 16 * (c ^ sw2) + byte_in));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
+            o[n] = mfma16x16x32(u32x4{w0[0], w0[1], w1[0], w1[1]}, pb, o[n]);
+        }
+        lds_barrier();  // tile t fully read; tile t + 1 stored
     }
 
-    // ---- epilogue: this wave owns d_v tiles [part * NDP, part * NDP + NDP) of head `head`
-    const float l_tot = sum_xor32(l_run);
-    if (head >= a.heads_q) return;
+    // ---- epilogue: lane L of group g holds d_v = half * DV / 2 + 16 n + 4 g + i of head L
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot = sum_xor32(l_tot);
+    if (!live) return;
     if (a.splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t *orow = a.out + ((int64_t)row * a.heads_q + head) * DV;
 #pragma unroll
-        for (int n = 0; n < NDP; ++n)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = 32 * (part * NDP + n) + 8 * j + 4 * h;
-                u32x2 v = {pack_bf16x2(o[n][4 * j] * inv, o[n][4 * j + 1] * inv),
-                           pack_bf16x2(o[n][4 * j + 2] * inv, o[n][4 * j + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + d) = v;
-            }
+        for (int n = 0; n < DT; ++n) {
+            const int d = half * (DV / 2) + 16 * n + 4 * g;
+            *reinterpret_cast<u32x2 *>(orow + d) =
+                u32x2{pack_bf16x2(o[n][0] * inv, o[n][1] * inv), pack_bf16x2(o[n][2] * inv, o[n][3] * inv)};
+        }
     } else {
-        // partial of this split, normalised by its own sum, in bf16 (the merge weights carry
-        // the sums); empty splits write zeros and l = 0
         const int64_t ph = ((int64_t)row * a.splits + split) * a.heads_q + head;
         uint16_t *orow = a.part_o + ph * DV;
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-        for (int n = 0; n < NDP; ++n)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = 32 * (part * NDP + n) + 8 * j + 4 * h;
-                u32x2 v = {pack_bf16x2(o[n][4 * j] * inv, o[n][4 * j + 1] * inv),
-                           pack_bf16x2(o[n][4 * j + 2] * inv, o[n][4 * j + 3] * inv)};
-                *reinterpret_cast<u32x2 *>(orow + d) = v;
-            }
-        if (h == 0 && part == 0) {
+        for (int n = 0; n < DT; ++n) {
+            const int d = half * (DV / 2) + 16 * n + 4 * g;
+            *reinterpret_cast<u32x2 *>(orow + d) =
+                u32x2{pack_bf16x2(o[n][0] * inv, o[n][1] * inv), pack_bf16x2(o[n][2] * inv, o[n][3] * inv)};
+        }
+        if (g == 0 && half == 0) {
             a.part_ml[2 * ph] = m_run;
             a.part_ml[2 * ph + 1] = l_tot;
         }
@@ -379,12 +339,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 
 template <int DQK, int DV, bool SEPV, bool FP8>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)4 * 32 * kPartRow * 4 + (size_t)a.split_len * (FP8 ? 12 : 8);
-    auto kern = k_sparse_attn<DQK, DV, SEPV, FP8>;
+    const size_t lds = (size_t)4 * 2 * 2 * 64 * 16 + (size_t)a.split_len * (FP8 ? 12 : 8);
+    auto kern = k_sparse_attn_pairs<DQK, DV, SEPV, FP8>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(a.rows * a.splits * a.hgroups)), dim3(256), lds, st,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.rows * a.splits * a.hgroups)), dim3(512), lds, st,
                        a);
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;

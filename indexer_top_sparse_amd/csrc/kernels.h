@@ -95,7 +95,7 @@ struct TopkArgs {
 };
 
 // Head groups per query row: one attention workgroup per 32 query heads.
-inline int attn_hgroups(int heads_q) { return (heads_q + 31) / 32; }
+inline int attn_hgroups(int heads_q) { return (heads_q + 63) / 64; }
 
 struct AttnArgs {
     int num_seqs, lp, pages_per_seq, heads_q, k, splits, split_len, rows, hgroups;
