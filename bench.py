@@ -53,8 +53,12 @@ def algorithmic_bytes(wl):
     for n in wl.ctx_lens:
         npg = math.ceil(n / P)
         k_eff = min(K, n)
-        sel += (n * key_row + wl.idx_heads * wl.idx_dim * 2 + wl.idx_heads * 4 + npg * 4 + 4
-                + K * 4)
+        if wl.block_topk:
+            # two-level: one pooled summary row per block, then the keys of the kept blocks
+            keys = npg * wl.idx_dim * 2 + min(n, min(wl.block_topk, npg) * P) * key_row
+        else:
+            keys = n * key_row
+        sel += (keys + wl.idx_heads * wl.idx_dim * 2 + wl.idx_heads * 4 + npg * 4 + 4 + K * 4)
         attn += (k_eff * kv_row + wl.heads_q * wl.dim_qk * 2 + wl.heads_q * wl.dim_v * 2
                  + K * 4 + npg * 4)
     # the fused step: everything above except the index set, which never has to leave the op
