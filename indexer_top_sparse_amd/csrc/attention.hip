@@ -18,9 +18,11 @@ constexpr float kRescale = 8.f;    // log2 growth tolerated before O is rescaled
 
 // LDS row swizzle: 16-byte chunk c of staged row r lives at chunk c ^ swz(r). The XOR only
 // touches the low three chunk bits, so a chunk stays inside its aligned group of 8. With
-// 1152-byte rows it keeps the K-fragment reads (16 rows, one chunk each) and each 16-lane group
-// of the transposing V reads (4 rows x 32 bytes) free of LDS bank conflicts.
-__device__ __forceinline__ int swz(int r) { return ((r << 1) & 6) ^ ((r >> 2) & 3); }
+// 1152-byte rows it keeps three access patterns free of LDS bank conflicts: the staging stores
+// (16 consecutive chunks of a row), the K-fragment reads (16 rows, one chunk each) and the
+// transposing V reads, where 32 lanes read rows {4g, 4g+1, 16+4g, 16+4g+1} (or the other four
+// of the group) x 32 bytes for two lane groups g at once.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r >> 2) & 4); }
 
 template <int DQK, int DV, bool SEPV, bool FP8>
 struct AttnShape {
@@ -228,13 +230,16 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
                 p[4 + i] *= sg1[i];
             }
         }
-        // P^T B operand: k = 8 g + e <-> row 4 g + (e % 4) + 16 (e / 4), the lane's own rows
-        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        // P^T B operand: k = 8 g + e <-> the lane's own rows, in the order of the V reads below:
+        // e = 0..3 rows 4g, 4g+1, 16+4g, 16+4g+1; e = 4..7 the same plus 2
+        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[2], p[3]), pack_bf16x2(p[6], p[7])};
         // ---- O^T += V^T P^T over this wave's half of d_v. Transposing reads: input lane j of
-        //      group g loads columns [4 (j % 4), +4) of row base + j / 4; output lane L then
-        //      holds column L of rows base .. base + 3.
-        const int vr1 = 4 * g + (L >> 2), vr2 = 16 + vr1;
+        //      group g loads columns [4 (j % 4), +4) of row R(j / 4), with R(q) = 4 g + (q & 1)
+        //      + 16 (q >> 1) (+ 2 for the second read); output lane L then holds column L of
+        //      rows R(0) .. R(3).
+        const int q = L >> 2;
+        const int vr1 = 4 * g + (q & 1) + 16 * (q >> 1), vr2 = vr1 + 2;
         const uint8_t *va = vb + vr1 * VROWB, *vbp = vb + vr2 * VROWB;
         const int sw1 = swz(vr1), sw2 = swz(vr2);
         const int byte_in = 8 * ((L & 3) & 1);
