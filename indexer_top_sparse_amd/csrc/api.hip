@@ -113,6 +113,8 @@ int attn_splits(int rows, int k, int heads_q) {
     // at least 4 tiles of 32 rows per split: below that the merge costs more than the extra
     // workgroups save
     s = std::min(s, std::max(1, (k + 127) / 128));
+    // at most 2048 rows per split: the per-row slot, bias and scale tables live in LDS
+    s = std::max(s, (k + kMaxSplitRows - 1) / kMaxSplitRows);
     return s;
 }
 int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }

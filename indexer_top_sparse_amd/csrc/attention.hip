@@ -8,6 +8,8 @@
 // All query heads share one KV row (MQA / MLA latent rows), so each gathered row is staged
 // once in LDS and used by every wave of the workgroup (see k_sparse_attn_pairs). Index sets
 // split over several workgroups publish normalised partials that k_attn_merge combines.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -346,9 +348,15 @@ template <int DQK, int DV, bool SEPV, bool FP8>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
     const size_t lds = (size_t)4 * 2 * 2 * 64 * 16 + (size_t)a.split_len * (FP8 ? 12 : 8);
     auto kern = k_sparse_attn_pairs<DQK, DV, SEPV, FP8>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    // raise the kernel's dynamic-LDS limit only when a launch needs more than already granted
+    static std::atomic<int> granted{-1};
+    hipError_t e = hipSuccess;
+    if ((int)lds > granted.load(std::memory_order_relaxed)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        granted.store((int)lds, std::memory_order_relaxed);
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)(a.rows * a.splits * a.hgroups)), dim3(512), lds, st,
                        a);
     e = hipGetLastError();

@@ -96,6 +96,7 @@ struct TopkArgs {
 
 // Head groups per query row: one attention workgroup per 32 query heads.
 inline int attn_hgroups(int heads_q) { return (heads_q + 63) / 64; }
+constexpr int kMaxSplitRows = 2048;  // selected rows per attention workgroup
 
 struct AttnArgs {
     int num_seqs, lp, pages_per_seq, heads_q, k, splits, split_len, rows, hgroups;

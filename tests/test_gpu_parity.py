@@ -304,3 +304,22 @@ def test_decode_batch_larger_than_one_selection_launch():
     torch.cuda.synchronize()
     assert binding.workspace_error(ws) == 0
     _check_decode(wl, out, idx, 2e-2)
+
+
+def test_prefill_large_k_splits_rows():
+    """K = 4096 over 300 prefill rows: many rows fill the device, yet each row's index set is
+    split (at most 2048 selected rows per attention workgroup), exercising the merge."""
+    wl = inputs.make("prefill64k", ctx=6000, q_len=300, topk=4096, seed_offset=14)
+    _say("prefill: ctx 6000, 300 rows, K=4096")
+    dw = device.to_device(wl)
+    s = device.index_score(dw)
+    idx = device.topk(dw, s)
+    ws = device.new_workspace(dw)
+    out = device.sparse_attn(dw, idx, ws).float().cpu().numpy()
+    got = idx.cpu().numpy()
+    pos = wl.q_pos().numpy()
+    ref_idx = oracle.topk(s.cpu().numpy().astype(np.float64), pos + 1, wl.topk)
+    np.testing.assert_array_equal(got, ref_idx)
+    err = np.abs(out - oracle.sparse_attn(wl, got)).max()
+    _say(f"  max abs output error {err:.3e}")
+    assert err <= 2e-2
