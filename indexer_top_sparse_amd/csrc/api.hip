@@ -122,7 +122,8 @@ int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, part_o = 0, part_ml = 0, total = 0;
+    size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, slots = 0, part_o = 0, part_ml = 0,
+           total = 0;
 };
 
 WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int block_k) {
@@ -139,6 +140,8 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
     L.idx = off;
     off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(k, 0));
     if (kv) {
+        L.slots = off;  // physical rows of the fused step's index set
+        off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(k, 0));
         const int rmax = std::max(rows, b->num_seqs);
         // the split count only grows as rows shrink; size for the larger of the two
         const int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
@@ -202,7 +205,7 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
 // consecutive launches.
 sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
                      int mode, int k, int block_k, const int32_t *blocks, int32_t *idx_out,
-                     uint8_t *ws, const WsLayout &L, hipStream_t st) {
+                     int32_t *slots_out, uint8_t *ws, const WsLayout &L, hipStream_t st) {
     const bool fp8 = mode != 1 && ix->key_dtype == SA_FP8_E4M3;
     void *kern = decode_select_kernel(ix->dim, ix->heads, fp8, mode);
     const int threads = 512;
@@ -211,16 +214,20 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
     const int occ0 = occupancy(kern, threads, decode_select_dynamic_lds(mode, 64, lp));
     if (occ0 <= 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
     const int per_launch = std::max(1, occ0 * cus / 2);
-    for (int s0 = 0; s0 < b->num_seqs; s0 += per_launch) {
-        const int nb = std::min(per_launch, b->num_seqs - s0);
-        int64_t total = 0;
-        for (int s = s0; s < s0 + nb; ++s)
-            total += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
-        // capacity -> chunks -> LDS -> capacity, until the plan fits what it assumed
+    for (int s0 = 0, nb = 0; s0 < b->num_seqs; s0 += nb) {
+        nb = std::min(per_launch, b->num_seqs - s0);
+        // capacity -> chunks -> LDS -> capacity, until the plan fits what it assumed. A chunk
+        // that does not fit (LDS, or more candidates than the emission's ballot groups cover)
+        // halves the sequences of this launch, which gives each one more workgroups.
         int occ = occ0, chunk_max = 64;
-        int64_t groups = 0;
+        int64_t groups = 0, total = 0;
         size_t lds = 0;
         for (int iter = 0;; ++iter) {
+            if (iter == 0) {
+                total = 0;
+                for (int s = s0; s < s0 + nb; ++s)
+                    total += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+            }
             const int spare = occ * cus - nb;
             if (spare < 0 || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
             chunk_max = 64;
@@ -232,8 +239,14 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
                 groups += sel_groups(nc, c);
             }
             lds = decode_select_dynamic_lds(mode, chunk_max, lp);
-            const int o = occupancy(kern, threads, lds);
-            if (o <= 0) return fail(SA_ERR_UNSUPPORTED, "selection chunk exceeds the LDS of a CU");
+            const int o = chunk_max <= kSelMaxChunk ? occupancy(kern, threads, lds) : 0;
+            if (o <= 0) {
+                if (nb == 1) return fail(SA_ERR_UNSUPPORTED, "selection chunk exceeds the LDS of a CU");
+                nb = (nb + 1) / 2;
+                occ = occ0;
+                iter = -1;
+                continue;
+            }
             if (o >= occ) break;
             occ = o;
         }
@@ -255,6 +268,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         a.keys = static_cast<const uint8_t *>(mode == 1 ? ix->pooled : ix->keys);
         a.key_scale = ix->key_scale;
         a.idx_out = idx_out + (int64_t)s0 * k;
+        a.slots_out = slots_out ? slots_out + (int64_t)s0 * k : nullptr;
         a.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
         a.err = reinterpret_cast<uint32_t *>(ws + L.err);
         // The grid never exceeds what the device holds at once, so every workgroup becomes
@@ -270,8 +284,8 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
 }
 
 sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
-                   const int32_t *idx, int k, void *out, uint8_t *ws, const WsLayout &L,
-                   hipStream_t st) {
+                   const int32_t *idx, const int32_t *slots, int k, void *out, uint8_t *ws,
+                   const WsLayout &L, hipStream_t st) {
     AttnArgs a;
     a.num_seqs = b->num_seqs;
     a.lp = log2i(b->page_size);
@@ -287,6 +301,7 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     a.q_indptr = b->q_indptr;
     a.q = static_cast<const uint16_t *>(q);
     a.idx = idx;
+    a.slots = slots;
     a.kc = static_cast<const uint8_t *>(kv->k);
     a.vc = static_cast<const uint8_t *>(kv->v);
     a.kv_scale = kv->scale;
@@ -414,23 +429,24 @@ sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
     if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
     const WsLayout L = ws_layout(batch, rp.rows, kv, k, 0);
     if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
-    return run_attn(batch, rp.rows, kv, q, idx, k, out, static_cast<uint8_t *>(ws), L,
+    return run_attn(batch, rp.rows, kv, q, idx, nullptr, k, out, static_cast<uint8_t *>(ws), L,
                     static_cast<hipStream_t>(stream));
 }
 
 static sa_status select_impl(const sa_batch *batch, const RowPlan &rp, const sa_indexer *ix,
                              const void *q_idx, const float *w, int32_t k, int32_t block_k,
-                             int32_t *idx, uint8_t *wsb, const WsLayout &L, hipStream_t hs) {
+                             int32_t *idx, int32_t *slots, uint8_t *wsb, const WsLayout &L,
+                             hipStream_t hs) {
     (void)rp;
     sa_status st;
     if (block_k > 0) {
         int32_t *blocks = reinterpret_cast<int32_t *>(wsb + L.blocks);
-        if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks, wsb, L,
+        if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks, nullptr, wsb, L,
                              hs)) != SA_OK)
             return st;
-        return run_select(batch, ix, q_idx, w, 2, k, block_k, blocks, idx, wsb, L, hs);
+        return run_select(batch, ix, q_idx, w, 2, k, block_k, blocks, idx, slots, wsb, L, hs);
     }
-    return run_select(batch, ix, q_idx, w, 0, k, 0, nullptr, idx, wsb, L, hs);
+    return run_select(batch, ix, q_idx, w, 0, k, 0, nullptr, idx, slots, wsb, L, hs);
 }
 
 static sa_status check_select(const sa_batch *batch, RowPlan *rp, const sa_indexer *ix,
@@ -456,7 +472,8 @@ sa_status sa_index_select(const sa_batch *batch, const sa_indexer *ix, const voi
     if (!idx_out) return fail(SA_ERR_INVALID, "idx_out is required");
     const WsLayout L = ws_layout(batch, rp.rows, nullptr, k, block_k);
     if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
-    return select_impl(batch, rp, ix, q_idx, w, k, block_k, idx_out, static_cast<uint8_t *>(ws),
+    return select_impl(batch, rp, ix, q_idx, w, k, block_k, idx_out, nullptr,
+                       static_cast<uint8_t *>(ws),
                        L, static_cast<hipStream_t>(stream));
 }
 
@@ -470,7 +487,7 @@ sa_status sa_block_select(const sa_batch *batch, const sa_indexer *ix, const voi
     if (!blocks_out) return fail(SA_ERR_INVALID, "blocks_out is required");
     const WsLayout L = ws_layout(batch, rp.rows, nullptr, block_k, block_k);
     if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
-    return run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks_out,
+    return run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks_out, nullptr,
                       static_cast<uint8_t *>(ws), L, static_cast<hipStream_t>(stream));
 }
 
@@ -489,9 +506,12 @@ sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_k
     uint8_t *wsb = static_cast<uint8_t *>(ws);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
-    if ((st = select_impl(batch, rp, ix, q_idx, w, k, block_k, idx, wsb, L, hs)) != SA_OK)
+    // the selection also writes the physical rows of the index set, so the attention reads
+    // them directly instead of translating positions through the page table
+    int32_t *slots = reinterpret_cast<int32_t *>(wsb + L.slots);
+    if ((st = select_impl(batch, rp, ix, q_idx, w, k, block_k, idx, slots, wsb, L, hs)) != SA_OK)
         return st;
-    return run_attn(batch, rp.rows, kv, q, idx, k, out, wsb, L, hs);
+    return run_attn(batch, rp.rows, kv, q, idx, slots, k, out, wsb, L, hs);
 }
 
 }  // extern "C"

@@ -90,8 +90,12 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
     for (int j = tid; j < ntiles * kTile; j += NT) {
         int32_t slot = -1;
         if (j0 + j < j1) {
-            const int e = idx[j0 + j];
-            if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
+            if (a.slots) {
+                slot = a.slots[(int64_t)row * a.k + j0 + j];
+            } else {
+                const int e = idx[j0 + j];
+                if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
+            }
         }
         s_slot[j] = slot;
         s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;

@@ -440,7 +440,7 @@ constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
 
-struct SelShared {
+struct alignas(16) SelShared {
     uint32_t hist[kHistBins];
     uint32_t scan[kSelWaves + 1];
     uint32_t res[8];
@@ -710,6 +710,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- per-workgroup counts -> global offsets
     const int K = a.k;
     int32_t *out = a.idx_out + (int64_t)seq * K;
+    int32_t *slots = a.slots_out ? a.slots_out + (int64_t)seq * K : nullptr;
     const uint32_t k_eff = min((uint32_t)K, total);
     if (k_eff > 0 && listn > 0) {
         // ---- the first pass's threshold bin holds few candidates. Each workgroup publishes
@@ -813,19 +814,36 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             const uint64_t c = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i);
             return (c >> (64 - pb)) >= pre;
         };
-        // ordered emission: thread t owns local candidates [t*E, t*E + E)
-        const int E = (cnt + kSelThreads - 1) / kSelThreads;
-        const int i0 = min(cnt, tid * E), i1 = min(cnt, i0 + E);
-        uint32_t my_sel = 0;
-        for (int i = i0; i < i1; ++i) my_sel += take(i);
-        uint32_t dst = a_before + taken_before + block_excl_scan<kSelThreads>(my_sel, sh.scan, &tmp);
-        for (int i = i0; i < i1; ++i) {
-            if (take(i)) {
+        // ordered emission, wave-parallel: groups of 64 consecutive candidates, one lane per
+        // candidate; a ballot per group, one scan over the group counts, then each selected
+        // lane writes at base + group offset + selected lanes below it
+        uint64_t *gmask = reinterpret_cast<uint64_t *>(&sh.hist[0]);  // [<= 512] groups
+        uint32_t *gofs = &sh.hist[1024];                               // [<= 512]
+        const int ng = (cnt + 63) >> 6;
+        for (int gi = wave_id(); gi < ng; gi += kSelWaves) {
+            const int i = 64 * gi + l;
+            const uint64_t m = __ballot(i < cnt && take(i));
+            if (l == 0) gmask[gi] = m;
+        }
+        __syncthreads();
+        const uint32_t gc = tid < ng ? (uint32_t)__popcll(gmask[tid]) : 0u;
+        const uint32_t gex = block_excl_scan<kSelThreads>(gc, sh.scan, &tmp);
+        if (tid < ng) gofs[tid] = gex;
+        __syncthreads();
+        const uint32_t base = a_before + taken_before;
+        for (int gi = wave_id(); gi < ng; gi += kSelThreads / 64) {
+            const uint64_t m = gmask[gi];
+            if ((m >> l) & 1u) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                const uint32_t dst = base + gofs[gi] + below;
                 int pos;
                 int64_t row;
-                cr.cand(s, c0 + i, c0, a.lp, pos, row);
-                if (dst < (uint32_t)K) out[dst] = pos;
-                ++dst;
+                cr.cand(s, c0 + 64 * gi + l, c0, a.lp, pos, row);
+                if (dst < (uint32_t)K) {
+                    out[dst] = pos;
+                    if (slots) slots[dst] = (int32_t)row;
+                }
             }
         }
     } else if (k_eff > 0) {
@@ -908,14 +926,20 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                     int pos;
                     int64_t row;
                     cr.cand(s, c0 + i, c0, a.lp, pos, row);
-                    if (dst < (uint32_t)K) out[dst] = pos;
+                    if (dst < (uint32_t)K) {
+                        out[dst] = pos;
+                        if (slots) slots[dst] = (int32_t)row;
+                    }
                     ++dst;
                 }
             }
         }
     }
     if (chunk == G - 1)
-        for (int j = (int)k_eff + tid; j < K; j += kSelThreads) out[j] = -1;
+        for (int j = (int)k_eff + tid; j < K; j += kSelThreads) {
+            out[j] = -1;
+            if (slots) slots[j] = -1;
+        }
 
     // ---- leave the histograms zeroed for the next launch. Every histogram read happens
     //      before the count-exchange (or list) barrier; without that barrier (nothing to

@@ -8,6 +8,7 @@
 namespace sa {
 
 constexpr int kMaxGroupsPerSeq = 512;  // workgroups sharing one sequence in a selection
+constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup (512 ballot groups)
 
 // Per-sequence record in the workspace used by the cross-workgroup selection. `count` and the
 // histograms return to zero at the end of every launch; `gen` only grows.
@@ -81,7 +82,8 @@ struct SelectArgs {
     const float *w;
     const uint8_t *keys;
     const float *key_scale;
-    int32_t *idx_out;  // [num_seqs][k]
+    int32_t *idx_out;    // [num_seqs][k]
+    int32_t *slots_out;  // [num_seqs][k] physical rows of the selected positions, or null
     SelSync *sync;
     uint32_t *err;
 };
@@ -103,6 +105,7 @@ struct AttnArgs {
     const int32_t *page_table, *ctx_lens, *q_indptr;
     const uint16_t *q;
     const int32_t *idx;
+    const int32_t *slots;  // [rows][k] physical rows of idx (-1 unused), or null: translate idx
     const uint8_t *kc;  // K rows (or latent rows)
     const uint8_t *vc;  // V rows, or null when V is the head of each K row
     const float *kv_scale;

@@ -323,3 +323,18 @@ def test_prefill_large_k_splits_rows():
     err = np.abs(out - oracle.sparse_attn(wl, got)).max()
     _say(f"  max abs output error {err:.3e}")
     assert err <= 2e-2
+
+
+def test_decode_long_contexts_fill_a_selection_launch():
+    """128 sequences of 64000 tokens: with one workgroup per sequence plus the spare ones, a
+    workgroup's share would not fit the LDS of a CU, so the batch runs as smaller launches
+    with more workgroups per sequence. Small head shapes keep the inputs at a few GB."""
+    _say("decode: B=128, ctx 64000, 4 indexer heads, 8 query heads, K=256")
+    wl = inputs.make("decode32k", num_seqs=128, ctx=64000, idx_heads=4, idx_dim=64, topk=256,
+                     heads_q=8, dim_qk=128, dim_v=128, seed_offset=15)
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2, rows=[0, 1, 63, 64, 127])
