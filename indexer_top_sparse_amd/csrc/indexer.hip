@@ -437,6 +437,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
 // with per-pass global histograms and a barrier per pass. Selected candidates are written in
 // ascending position order; ties at the threshold go to the lower positions.
 constexpr int kSelThreads = 512;
+static_assert(kListCap % kSelThreads == 0, "whole list entries per thread");
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistBins = 2048;
 
@@ -733,19 +734,43 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         if (tid == 0) {
             sh.res[6] = eq_tot ? fetch_add_agent(&ss->list_n, eq_tot) : 0u;
             st_agent(&ss->cnt[chunk][0], above_tot);
+            sh.grp[0] = 0u;
         }
         __syncthreads();
         {
-            uint32_t o = sh.res[6] + eq_base;
-            for (int i = tid; i < cnt; i += kSelThreads) {
-                const uint32_t k = s_key[i];
-                if (k != 0u && (k >> 21) == prefix)
-                    st_agent64(&ss->list[o++], ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i));
+            // the list's order is irrelevant (every reader takes all of it), so each wave
+            // appends the bin's candidates of one round at consecutive slots: a wave-level
+            // ballot and one LDS atomic per wave and round keep the stores coalesced
+            (void)eq_base;
+            const uint32_t lbase = sh.res[6];
+            for (int i0 = 0; i0 < cnt; i0 += kSelThreads) {
+                const int i = i0 + tid;
+                const uint32_t k = i < cnt ? s_key[i] : 0u;
+                const bool in_bin = k != 0u && (k >> 21) == prefix;
+                const uint64_t m = __ballot(in_bin);
+                if (m == 0) continue;
+                uint32_t woff = 0;
+                if (l == 0) woff = atomicAdd(&sh.grp[0], (uint32_t)__popcll(m));
+                woff = __shfl(woff, 0, 64);
+                if (in_bin) {
+                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    st_agent64(&ss->list[lbase + woff + below],
+                               ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i));
+                }
             }
         }
         ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
-        uint64_t *Ls = reinterpret_cast<uint64_t *>(&s_stage[0][0]);  // kListCap entries
-        for (int j = tid; j < (int)listn; j += kSelThreads) Ls[j] = ld_agent64(&ss->list[j]);
+        // the list (at most kListCap entries) stays in registers: thread tid holds entries
+        // tid + kSelThreads r; 0 marks an empty slot (list keys are never 0). All loads are
+        // issued before the first is used.
+        constexpr int LPT = kListCap / kSelThreads;
+        uint64_t lc[LPT];
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) {
+            const int j = tid + kSelThreads * r;
+            lc[r] = j < (int)listn ? ld_agent64(&ss->list[j]) : 0ull;
+        }
         if (chunk == 0 && tid == 0) st_agent(&ss->list_n, 0u);  // only the appends used it
         const uint32_t Ah = tid < chunk ? ld_agent(&ss->cnt[tid][0]) : 0u;
         uint32_t a_before;
@@ -760,9 +785,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             const int nb = 1 << bits;
             for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
             __syncthreads();
-            for (int j = tid; j < (int)listn; j += kSelThreads) {
-                const uint64_t c = Ls[j];
-                if ((c >> (64 - pb)) == pre)
+#pragma unroll
+            for (int r = 0; r < LPT; ++r) {
+                const uint64_t c = lc[r];
+                if (c != 0ull && (c >> (64 - pb)) == pre)
                     atomicAdd(&sh.hist[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
             }
             __syncthreads();
@@ -799,51 +825,72 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         }
         // list candidates of earlier workgroups that are selected
         uint32_t tb = 0;
-        for (int j = tid; j < (int)listn; j += kSelThreads) {
-            const uint64_t c = Ls[j];
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) {
+            const uint64_t c = lc[r];
             const uint32_t ci = ~(uint32_t)c;
-            tb += ((c >> (64 - pb)) >= pre) && ci / (uint32_t)clen < (uint32_t)chunk;
+            // candidates of earlier workgroups: below this chunk's first candidate c0
+            tb += c != 0ull && ((c >> (64 - pb)) >= pre) && ci < (uint32_t)c0;
         }
-        uint32_t taken_before, tmp;
+        uint32_t taken_before;
         block_excl_scan<kSelThreads>(tb, sh.scan, &taken_before);
-        auto take = [&](int i) -> bool {
-            const uint32_t k = s_key[i];
+        auto take = [&](uint32_t k, int i) -> bool {  // k = s_key[i]
             if (k == 0u) return false;
             const uint32_t p = k >> 21;
             if (p != prefix) return p > prefix;
             const uint64_t c = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i);
             return (c >> (64 - pb)) >= pre;
         };
-        // ordered emission, wave-parallel: groups of 64 consecutive candidates, one lane per
-        // candidate; a ballot per group, one scan over the group counts, then each selected
-        // lane writes at base + group offset + selected lanes below it
-        uint64_t *gmask = reinterpret_cast<uint64_t *>(&sh.hist[0]);  // [<= 512] groups
-        uint32_t *gofs = &sh.hist[1024];                               // [<= 512]
+        // ordered emission: wave w owns the consecutive groups [g0, g1) of 64 candidates (one
+        // lane per candidate). A first pass counts the wave's selected candidates with one
+        // ballot per group; the wave totals, in wave order, give each wave its first slot; a
+        // second pass repeats the ballots and every selected lane writes at that slot plus the
+        // selected candidates before it.
         const int ng = (cnt + 63) >> 6;
-        for (int gi = wave_id(); gi < ng; gi += kSelWaves) {
-            const int i = 64 * gi + l;
-            const uint64_t m = __ballot(i < cnt && take(i));
-            if (l == 0) gmask[gi] = m;
+        const int gpw = (ng + kSelWaves - 1) / kSelWaves;
+        const int g0 = wave_id() * gpw, g1 = min(ng, g0 + gpw);
+        // keys of EB groups are read before any is used
+        constexpr int EB = 8;
+        auto keys = [&](int gb, uint32_t *kk) {
+#pragma unroll
+            for (int u = 0; u < EB; ++u) {
+                const int i = 64 * (gb + u) + l;
+                kk[u] = (gb + u < g1 && i < cnt) ? s_key[i] : 0u;
+            }
+        };
+        uint32_t wcount = 0;
+        for (int gb = g0; gb < g1; gb += EB) {
+            uint32_t kk[EB];
+            keys(gb, kk);
+#pragma unroll
+            for (int u = 0; u < EB; ++u)
+                wcount += (uint32_t)__popcll(__ballot(take(kk[u], 64 * (gb + u) + l)));
         }
+        // sh.hist is free here: its last reads ended before the radix loop's last barrier
+        if (l == 0) sh.hist[wave_id()] = wcount;
         __syncthreads();
-        const uint32_t gc = tid < ng ? (uint32_t)__popcll(gmask[tid]) : 0u;
-        const uint32_t gex = block_excl_scan<kSelThreads>(gc, sh.scan, &tmp);
-        if (tid < ng) gofs[tid] = gex;
-        __syncthreads();
-        const uint32_t base = a_before + taken_before;
-        for (int gi = wave_id(); gi < ng; gi += kSelThreads / 64) {
-            const uint64_t m = gmask[gi];
-            if ((m >> l) & 1u) {
-                const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                    (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                const uint32_t dst = base + gofs[gi] + below;
-                int pos;
-                int64_t row;
-                cr.cand(s, c0 + 64 * gi + l, c0, a.lp, pos, row);
-                if (dst < (uint32_t)K) {
-                    out[dst] = pos;
-                    if (slots) slots[dst] = (int32_t)row;
+        uint32_t run = a_before + taken_before;
+        for (int v = 0; v < wave_id(); ++v) run += sh.hist[v];
+        for (int gb = g0; gb < g1; gb += EB) {
+            uint32_t kk[EB];
+            keys(gb, kk);
+#pragma unroll
+            for (int u = 0; u < EB; ++u) {
+                const int i = 64 * (gb + u) + l;
+                const bool sel = take(kk[u], i);
+                const uint64_t m = __ballot(sel);
+                if (sel) {
+                    const uint32_t dst = run + __builtin_amdgcn_mbcnt_hi(
+                                                   (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    int pos;
+                    int64_t row;
+                    cr.cand(s, c0 + i, c0, a.lp, pos, row);
+                    if (dst < (uint32_t)K) {
+                        out[dst] = pos;
+                        if (slots) slots[dst] = (int32_t)row;
+                    }
                 }
+                run += (uint32_t)__popcll(m);
             }
         }
     } else if (k_eff > 0) {
