@@ -216,30 +216,38 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
     const int per_launch = std::max(1, occ0 * cus / 2);
     for (int s0 = 0, nb = 0; s0 < b->num_seqs; s0 += nb) {
         nb = std::min(per_launch, b->num_seqs - s0);
-        // capacity -> chunks -> LDS -> capacity, until the plan fits what it assumed. A chunk
-        // that does not fit (LDS, or more candidates than the emission's ballot groups cover)
-        // halves the sequences of this launch, which gives each one more workgroups.
-        int occ = occ0, chunk_max = 64;
-        int64_t groups = 0, total = 0;
+        // capacity -> chunk -> LDS -> capacity, until the plan fits what it assumed. The chunk
+        // is the smallest multiple of 64 whose workgroups (sel_groups per sequence, at most
+        // kMaxGroupsPerSeq) all fit in the capacity. A chunk that does not fit (LDS, or more
+        // candidates than the emission's ballot groups cover) halves the sequences of this
+        // launch.
+        int occ = occ0, chunk = 64;
+        int64_t groups = 0;
         size_t lds = 0;
         for (int iter = 0;; ++iter) {
-            if (iter == 0) {
-                total = 0;
+            const int cap = occ * cus;
+            if (nb > cap || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
+            int nc_max = 0;
+            for (int s = s0; s < s0 + nb; ++s)
+                nc_max = std::max(nc_max, ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k));
+            auto total_groups = [&](int c) {
+                int64_t gsum = 0;
                 for (int s = s0; s < s0 + nb; ++s)
-                    total += ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
+                    gsum += sel_groups(ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k), c);
+                return gsum;
+            };
+            int lo = std::max(1, (nc_max + kMaxGroupsPerSeq - 1) / kMaxGroupsPerSeq);
+            lo = (lo + 63) / 64;
+            int hi = std::max(lo, (nc_max + 63) / 64);  // in units of 64; hi always fits (nb <= cap)
+            while (lo < hi) {
+                const int mid = (lo + hi) / 2;
+                if (total_groups(64 * mid) <= cap) hi = mid;
+                else lo = mid + 1;
             }
-            const int spare = occ * cus - nb;
-            if (spare < 0 || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
-            chunk_max = 64;
-            groups = 0;
-            for (int s = s0; s < s0 + nb; ++s) {
-                const int nc = ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k);
-                const int c = sel_chunk(nc, spare, total);
-                chunk_max = std::max(chunk_max, c);
-                groups += sel_groups(nc, c);
-            }
-            lds = decode_select_dynamic_lds(mode, chunk_max, lp);
-            const int o = chunk_max <= kSelMaxChunk ? occupancy(kern, threads, lds) : 0;
+            chunk = 64 * lo;
+            groups = total_groups(chunk);
+            lds = decode_select_dynamic_lds(mode, chunk, lp);
+            const int o = chunk <= kSelMaxChunk ? occupancy(kern, threads, lds) : 0;
             if (o <= 0) {
                 if (nb == 1) return fail(SA_ERR_UNSUPPORTED, "selection chunk exceeds the LDS of a CU");
                 nb = (nb + 1) / 2;
@@ -255,9 +263,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         a.lp = lp;
         a.pages_per_seq = b->pages_per_seq;
         a.heads = ix->heads;
-        a.chunk = chunk_max;
-        a.spare = occ * cus - nb;
-        a.total = total;
+        a.chunk = chunk;
         a.k = k;
         a.block_k = block_k;
         a.page_table = b->page_table + (int64_t)s0 * b->pages_per_seq;

@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             int len = 64;
             if (b < a.num_seqs) {
                 const int nc = ncand_of(MODE, a.ctx_lens[b], a.lp, a.block_k);
-                len = sel_chunk(nc, a.spare, a.total);
+                len = a.chunk;
                 nchunks = sel_groups(nc, len);
             }
             const uint32_t incl = wave_incl_scan(nchunks);

@@ -56,26 +56,19 @@ struct ScoreArgs {
     int64_t ld;
 };
 
-// Work split of the fused selection. A launch holds `spare` more workgroups than sequences;
-// sequence b with nc candidates gets 1 + floor(nc * spare / total) of them (at most
-// kMaxGroupsPerSeq), so every workgroup streams about total / (sequences + spare) candidates
-// whatever the length mix. A workgroup covers `sel_chunk` consecutive candidates (a multiple of
-// 64). Host and device evaluate the same integer expressions.
-__host__ __device__ inline int sel_chunk(int nc, int spare, long long total) {
-    long long g = 1 + (total > 0 ? (long long)nc * spare / total : 0);
-    if (g > kMaxGroupsPerSeq) g = kMaxGroupsPerSeq;
-    const long long per = ((nc + g - 1) / g + 63) / 64 * 64;
-    return per < 64 ? 64 : (int)per;
-}
+// Work split of the fused selection: every workgroup of a launch covers `chunk` consecutive
+// candidates of one sequence (the last one of a sequence fewer); a sequence with nc candidates
+// gets sel_groups(nc, chunk) workgroups. The host picks the smallest chunk (a multiple of 64)
+// whose workgroups all fit on the device at once, so the longest stream per workgroup is as
+// short as the device allows whatever the length mix. Host and device evaluate the same
+// expression.
 __host__ __device__ inline int sel_groups(int nc, int chunk) {
     return nc > 0 ? (nc + chunk - 1) / chunk : 1;
 }
 
 struct SelectArgs {
-    int num_seqs, lp, pages_per_seq, heads, chunk, k, block_k;
-    int spare;        // workgroups beyond one per sequence (see sel_chunk)
-    long long total;  // candidates of all sequences of the launch
-    // chunk: the largest per-workgroup candidate count of the launch (LDS layout)
+    int num_seqs, lp, pages_per_seq, heads, k, block_k;
+    int chunk;  // candidates per workgroup (see sel_groups)
     const int32_t *page_table, *ctx_lens;
     const int32_t *blocks;  // [num_seqs][block_k] for the fine stage, else null
     const uint16_t *q_idx;
