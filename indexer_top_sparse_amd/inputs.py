@@ -37,7 +37,7 @@ class Workload:
     # indexer
     idx_heads: int
     idx_dim: int
-    idx_dtype: str            # "bf16" | "fp8"
+    idx_dtype: str            # "bf16" | "fp8" | "mxfp8"
     q_idx: torch.Tensor       # bf16 [nq, idx_heads, idx_dim]
     w: torch.Tensor           # fp32 [nq, idx_heads]
     idx_keys: torch.Tensor    # bf16 [num_pages, page_size, idx_dim] or uint8 codes
@@ -57,6 +57,8 @@ class Workload:
     kv_scale: Optional[torch.Tensor]  # fp32 [num_pages, page_size] (fp8) else None
     softmax_scale: float
     seeds: dict = field(default_factory=dict)
+    # uint8 E8M0 bytes [num_pages, page_size, idx_dim / 32] (mxfp8 indexer keys) else None
+    idx_mx_scale: Optional[torch.Tensor] = None
 
     # ---- derived views --------------------------------------------------------------
     @property
@@ -114,6 +116,22 @@ def quantize_rows_e4m3(x: torch.Tensor):
     return codes.view(torch.uint8), sigma.to(torch.float32)
 
 
+def quantize_rows_mxfp8(x: torch.Tensor):
+    """Quantize fp32 ``x`` [..., n] (n a multiple of 32) to MXFP8: every 32 consecutive
+    elements share one power-of-two scale 2^X, X = floor(log2(amax)) - 8 clamped to
+    [-127, 127] (-127 for an all-zero block), stored as the E8M0 byte X + 127; elements are
+    code = RNE(clamp(v / 2^X, -448, 448)) in OCP E4M3. Returns (uint8 codes [..., n],
+    uint8 E8M0 [..., n / 32])."""
+    n = x.shape[-1]
+    blocks = x.reshape(*x.shape[:-1], n // 32, 32)
+    amax = blocks.abs().amax(dim=-1)
+    _, e = torch.frexp(amax)  # amax = f * 2^e, f in [0.5, 1)
+    xexp = torch.where(amax > 0, e - 1 - 8, torch.full_like(e, -127)).clamp(-127, 127)
+    scaled = blocks * torch.pow(2.0, -xexp.to(torch.float64)).to(torch.float32).unsqueeze(-1)
+    codes = scaled.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.reshape(x.shape), (xexp + 127).to(torch.uint8)
+
+
 def _page_table(num_seqs, ctx_lens, page_size, g):
     pages = [math.ceil(n / page_size) for n in ctx_lens]
     pages_per_seq = max(1, max(pages))
@@ -166,6 +184,11 @@ PRESETS = {
                           page_size=64, idx_heads=64, idx_dim=128, weights="scaled", topk=2048,
                           heads_q=128, heads_kv=1, dim_qk=576, dim_v=512, mla=True, dtype="fp8",
                           q_len=1, block_topk=0)),
+    # the ragged E4M3 batch with the indexer in MXFP8 (groups of 32, E8M0 scales)
+    "mxfp8ragged": (6, dict(num_seqs=64, ctx="loguniform", ctx_lo=4096, ctx_hi=131072,
+                            page_size=64, idx_heads=64, idx_dim=128, weights="scaled", topk=2048,
+                            heads_q=128, heads_kv=1, dim_qk=576, dim_v=512, mla=True,
+                            dtype="fp8", idx_dtype="mxfp8", q_len=1, block_topk=0)),
 }
 
 
@@ -211,7 +234,12 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
         w = torch.randn((nq, H_I), generator=gw, dtype=torch.float32) / 8.0
 
     dtype = p["dtype"]
-    if dtype == "fp8":
+    idx_dtype = p.get("idx_dtype", dtype)
+    idx_mx_scale = None
+    if idx_dtype == "mxfp8":
+        idx_keys, idx_mx_scale = quantize_rows_mxfp8(kf)
+        idx_scale, keys_bf16_for_pool = None, None
+    elif idx_dtype == "fp8":
         idx_keys, idx_scale = quantize_rows_e4m3(kf)
         keys_bf16_for_pool = None
     else:
@@ -221,7 +249,7 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
 
     pooled = None
     if p["block_topk"]:
-        assert dtype == "bf16", "block summaries are defined over bf16 indexer keys"
+        assert idx_dtype == "bf16", "block summaries are defined over bf16 indexer keys"
         pooled = _pooled_keys(keys_bf16_for_pool, pt, ctx_lens, P)
 
     Hq, Hkv, dqk, dv = p["heads_q"], p["heads_kv"], p["dim_qk"], p["dim_v"]
@@ -245,9 +273,9 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
     return Workload(
         name=preset, config_id=config_id, num_seqs=B, ctx_lens=ctx_lens, page_size=P,
         pages_per_seq=pages_per_seq, num_pages=num_pages, page_table=pt, q_lens=q_lens,
-        idx_heads=H_I, idx_dim=d_I, idx_dtype=dtype, q_idx=q_idx, w=w, idx_keys=idx_keys,
+        idx_heads=H_I, idx_dim=d_I, idx_dtype=idx_dtype, q_idx=q_idx, w=w, idx_keys=idx_keys,
         idx_scale=idx_scale, pooled=pooled, topk=p["topk"], block_topk=p["block_topk"],
         heads_q=Hq, heads_kv=Hkv, dim_qk=dqk, dim_v=dv, kv_dtype=dtype, q=q, k_cache=k_cache,
         v_cache=v_cache, kv_scale=kv_scale, softmax_scale=float(scale),
-        seeds={"config_id": config_id, "seed_offset": off},
+        seeds={"config_id": config_id, "seed_offset": off}, idx_mx_scale=idx_mx_scale,
     )

@@ -56,6 +56,14 @@ def load(real: str = "f64"):
     lib.ora_bf16.argtypes = [C.c_uint16]
     lib.ora_e4m3.restype = C.c_double if real == "f64" else C.c_float
     lib.ora_e4m3.argtypes = [C.c_uint8]
+    lib.ora_e4m3_encode.restype = C.c_uint8
+    lib.ora_e4m3_encode.argtypes = [C.c_double]
+    lib.ora_mx_exponent.restype = C.c_int
+    lib.ora_mx_exponent.argtypes = [C.c_double]
+    lib.ora_mx_quantize_bf16.restype = None
+    lib.ora_mx_quantize_bf16.argtypes = [P, i32, P, P]
+    lib.ora_index_scores_mx.argtypes = [i32, P, P, i32, i32, P, P, P, P, P, i32, i32, i64, P]
+    lib.ora_index_scores_mx.restype = C.c_int
     for fn in ("ora_index_scores", "ora_block_scores", "ora_topk", "ora_topk_in_blocks",
                "ora_sparse_attn"):
         getattr(lib, fn).restype = C.c_int
@@ -103,6 +111,31 @@ def bf16_decode(bits: np.ndarray, real: str = "f64") -> np.ndarray:
                     dtype=lib.real_dtype).reshape(np.shape(bits))
 
 
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest E4M3 codes (ties to even mantissa, saturating at +-448)."""
+    lib = load("f64")
+    v = np.asarray(values, dtype=np.float64)
+    return np.array([lib.ora_e4m3_encode(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def mx_exponent(amax: float) -> int:
+    """Shared exponent X of an MXFP8 block with largest magnitude ``amax``."""
+    return int(load("f64").ora_mx_exponent(float(amax)))
+
+
+def mx_quantize_bf16(bits: np.ndarray):
+    """bf16 bit patterns [..., n] (n a multiple of 32) -> (E4M3 codes [..., n], E8M0 [..., n/32])."""
+    lib = load("f64")
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    n = b.shape[-1]
+    flat = b.reshape(-1, n)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    e8m0 = np.empty((flat.shape[0], n // 32), dtype=np.uint8)
+    for r in range(flat.shape[0]):
+        lib.ora_mx_quantize_bf16(_p(flat[r]), n, _p(codes[r]), _p(e8m0[r]))
+    return codes.reshape(b.shape), e8m0.reshape(b.shape[:-1] + (n // 32,))
+
+
 def e4m3_decode(codes: np.ndarray, real: str = "f64") -> np.ndarray:
     lib = load(real)
     return np.array([lib.ora_e4m3(int(c)) for c in np.asarray(codes).ravel()],
@@ -120,9 +153,16 @@ def index_scores(wl, rows=None, ncols=None, real: str = "f64") -> np.ndarray:
     q_idx = _np(wl.q_idx)[rows].copy()
     w = _np(wl.w, np.float32)[rows].copy()
     keys = _np(wl.idx_keys)
-    scale = None if wl.idx_scale is None else _np(wl.idx_scale, np.float32)
     pt = _np(wl.page_table, np.int32)
     out = np.empty((len(rows), ncols), dtype=lib.real_dtype)
+    if wl.idx_dtype == "mxfp8":
+        e8m0 = _np(wl.idx_mx_scale, np.uint8)
+        rc = lib.ora_index_scores_mx(len(rows), _p(q_seq), _p(q_pos), wl.idx_heads, wl.idx_dim,
+                                     _p(q_idx), _p(w), _p(keys), _p(e8m0), _p(pt),
+                                     wl.pages_per_seq, wl.page_size, ncols, _p(out))
+        assert rc == 0, "oracle index_scores_mx rejected its inputs"
+        return out
+    scale = None if wl.idx_scale is None else _np(wl.idx_scale, np.float32)
     rc = lib.ora_index_scores(len(rows), _p(q_seq), _p(q_pos), wl.idx_heads, wl.idx_dim,
                               _p(q_idx), _p(w), _fmt(wl.idx_dtype), _p(keys), _p(scale), _p(pt),
                               wl.pages_per_seq, wl.page_size, ncols, _p(out))
@@ -163,6 +203,7 @@ def topk(scores: np.ndarray, n_valid, k: int, real: str = "f64") -> np.ndarray:
 def topk_in_blocks(wl, blocks: np.ndarray, rows=None, k=None, real: str = "f64") -> np.ndarray:
     """Fine stage: Top-k among the visible tokens of the given blocks (one row per query)."""
     lib = load(real)
+    assert wl.idx_dtype != "mxfp8", "two-level selection is defined over bf16 / E4M3 keys"
     rows, q_seq, q_pos = _rows(wl, rows)
     k = wl.topk if k is None else k
     blocks = np.ascontiguousarray(blocks, dtype=np.int32)

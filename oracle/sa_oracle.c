@@ -65,6 +65,59 @@ REAL ora_e4m3(uint8_t code) {
     return sign ? -mag : mag;
 }
 
+/* Nearest E4M3 code to y, ties to the code with an even mantissa, saturating at +-448 (the
+ * largest finite magnitude; the format has no infinities). The sign bit is y's sign bit, so
+ * -0.0 and negative values that round to zero give 0x80. The search simply visits every
+ * finite non-negative code. */
+uint8_t ora_e4m3_encode(double y) {
+    double a = fabs(y);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        double err = fabs((double)ora_e4m3((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    if (a > 448.0) best = 0x7E;
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* MXFP8 (the OCP microscaling format with E4M3 elements): a block of 32 consecutive elements
+ * shares one power-of-two scale 2^X, stored as the E8M0 byte X + 127. The shared exponent is
+ *     X = floor(log2(amax)) - 8        (8 = the exponent of E4M3's largest power of two)
+ * clamped to [-127, 127], with X = -127 for an all-zero block; each element is encoded as
+ * E4M3(v / 2^X) with saturation. The indexer runs in this format, with per-group dynamic
+ * quantization and a group of 32: [CANN] §3. */
+int ora_mx_exponent(double amax) {
+    if (!(amax > 0)) return -127;
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2(amax)) = e - 1 */
+    int x = (e - 1) - 8;
+    return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+/* Quantize n bf16 values (n a multiple of 32) to MXFP8: codes[n], e8m0[n / 32]. */
+void ora_mx_quantize_bf16(const uint16_t *in, int n, uint8_t *codes, uint8_t *e8m0) {
+    for (int b = 0; b < n / 32; b++) {
+        double amax = 0;
+        for (int i = 0; i < 32; i++) {
+            double v = fabs((double)ora_bf16(in[32 * b + i]));
+            if (v > amax) amax = v;
+        }
+        int x = ora_mx_exponent(amax);
+        e8m0[b] = (uint8_t)(x + 127);
+        for (int i = 0; i < 32; i++)
+            codes[32 * b + i] = ora_e4m3_encode((double)ora_bf16(in[32 * b + i]) * ldexp(1.0, -x));
+    }
+}
+
+/* Value of element i of an MXFP8 vector: E4M3 code times 2^(E8M0 byte of its block - 127). */
+static REAL mx_elem(const uint8_t *codes, const uint8_t *e8m0, int i) {
+    return ora_e4m3(codes[i]) * (REAL)ldexp(1.0, (int)e8m0[i / 32] - 127);
+}
+
 /* ---------------------------------------------------------------- paged addressing */
 
 /* Blocked KV layout: a logical position maps to (block number, offset inside the block) and
@@ -107,6 +160,66 @@ static REAL score_one(int heads, int dim, const uint16_t *qrow /* [heads, dim] *
         s += (REAL)wrow[h] * (d > 0 ? d : 0);
     }
     return s;
+}
+
+/*
+ * The same score with the indexer in MXFP8 ([CANN] §3): the query row of each head is quantized
+ * (per-group dynamic quantization, groups of 32) exactly as ora_mx_quantize_bf16 states, the
+ * stored key row is MXFP8 (codes [slot, dim], E8M0 bytes [slot, dim / 32]), and the dot
+ * products, ReLU and head weighting are those of score_one.
+ */
+static REAL score_one_mx(int heads, int dim, const uint8_t *qcodes, const uint8_t *qe8m0,
+                         const float *wrow, const uint8_t *keys, const uint8_t *key_e8m0,
+                         int64_t slot) {
+    REAL s = 0;
+    const uint8_t *kc = keys + slot * dim, *ke = key_e8m0 + slot * (dim / 32);
+    for (int h = 0; h < heads; h++) {
+        REAL d = 0;
+        for (int i = 0; i < dim; i++)
+            d += mx_elem(qcodes + (int64_t)h * dim, qe8m0 + (int64_t)h * (dim / 32), i) *
+                 mx_elem(kc, ke, i);
+        s += (REAL)wrow[h] * (d > 0 ? d : 0);
+    }
+    return s;
+}
+
+/* ora_index_scores for MXFP8 keys (see score_one_mx); dim must be a multiple of 32. */
+int ora_index_scores_mx(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads, int dim,
+                        const uint16_t *q_idx, const float *w, const uint8_t *keys,
+                        const uint8_t *key_e8m0, const int32_t *page_table, int pages_per_seq,
+                        int page_size, int64_t ncols, REAL *out) {
+    if (dim % 32) return 1;
+    for (int r = 0; r < nq; r++)
+        if (q_pos[r] >= ncols || q_pos[r] >= (int64_t)pages_per_seq * page_size) return 1;
+    uint8_t *qc = malloc((size_t)nq * heads * dim);
+    uint8_t *qe = malloc((size_t)nq * heads * (dim / 32));
+    if (!qc || !qe) {
+        free(qc);
+        free(qe);
+        return 1;
+    }
+    for (int r = 0; r < nq; r++)
+        for (int h = 0; h < heads; h++)
+            ora_mx_quantize_bf16(q_idx + ((int64_t)r * heads + h) * dim, dim,
+                                 qc + ((int64_t)r * heads + h) * dim,
+                                 qe + ((int64_t)r * heads + h) * (dim / 32));
+    int64_t total = (int64_t)nq * ncols;
+#pragma omp parallel for schedule(dynamic, 512)
+    for (int64_t f = 0; f < total; f++) {
+        int r = (int)(f / ncols);
+        int64_t t = f % ncols;
+        if (t > q_pos[r]) {
+            out[f] = -(REAL)INFINITY;
+            continue;
+        }
+        int64_t slot = slot_of(page_table, pages_per_seq, page_size, q_seq[r], t);
+        out[f] = score_one_mx(heads, dim, qc + (int64_t)r * heads * dim,
+                              qe + (int64_t)r * heads * (dim / 32), w + (int64_t)r * heads, keys,
+                              key_e8m0, slot);
+    }
+    free(qc);
+    free(qe);
+    return 0;
 }
 
 /*
