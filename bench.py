@@ -47,7 +47,8 @@ def kernel_source_hash() -> str:
 def algorithmic_bytes(wl):
     """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
     P, K = wl.page_size, wl.topk
-    key_row = wl.idx_dim * (1 if wl.idx_dtype == "fp8" else 2) + (4 if wl.idx_dtype == "fp8" else 0)
+    key_row = {"bf16": 2 * wl.idx_dim, "fp8": wl.idx_dim + 4,            # codes + fp32 row scale
+               "mxfp8": wl.idx_dim + wl.idx_dim // 32}[wl.idx_dtype]    # codes + E8M0 per 32
     kv_row = wl.k_row * (1 if wl.kv_dtype == "fp8" else 2) + (4 if wl.kv_dtype == "fp8" else 0)
     sel = attn = 0
     for n in wl.ctx_lens:
@@ -350,7 +351,7 @@ def main():
                 f"{args.replicas} rotating replicas resident in HBM",
         "config": {
             "workload": f"{args.workload}: decode B={wl.num_seqs} ctx={max(wl.ctx_lens)} "
-                        f"page={wl.page_size} indexer {wl.idx_heads}x{wl.idx_dim} "
+                        f"page={wl.page_size} indexer {wl.idx_heads}x{wl.idx_dim} {wl.idx_dtype} "
                         f"K={wl.topk} heads_q={wl.heads_q} qk/v={wl.dim_qk}/{wl.dim_v} "
                         f"{wl.kv_dtype}",
             "global_batch": wl.num_seqs, "seq_len": max(wl.ctx_lens), "parallelism": "none",

@@ -59,7 +59,9 @@ typedef enum sa_status {
 
 typedef enum sa_dtype {
     SA_BF16 = 0,     /* bfloat16 */
-    SA_FP8_E4M3 = 1  /* OCP E4M3 codes (max 448) times one fp32 scale per stored row */
+    SA_FP8_E4M3 = 1, /* OCP E4M3 codes (max 448) times one fp32 scale per stored row */
+    SA_MXFP8 = 2     /* OCP microscaling: E4M3 codes, and for every 32 consecutive entries of a
+                        row one E8M0 byte e giving the scale 2^(e - 127) (indexer keys only) */
 } sa_dtype;
 
 /* Sequences, their lengths and the page table of the blocked KV layout ([Domestic] §3.2;
@@ -82,16 +84,26 @@ typedef struct sa_batch {
  * q_I[heads][dim] and head weights w[heads] (fp32 accumulation):
  *     s[t] = sum_h w[h] * max(q_I[h] . k_I[t], 0)
  * (relevance scoring with head-weight weighting; the pages leave the formula open and this
- * library fixes it as written). For E4M3 keys, k_I[t] = code * key_scale[t]. */
+ * library fixes it as written). For E4M3 keys, k_I[t] = code * key_scale[t].
+ *
+ * MXFP8 keys: the indexer runs in MXFP8 with per-group dynamic quantization and groups of 32
+ * ([CANN] §3). Entry i of a stored key row is code[i] * 2^(key_mx_scale[i / 32] - 127), and the
+ * library quantizes each head's bf16 query row the same way before the dot products: for every
+ * 32 consecutive entries, X = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 when all are
+ * zero), code = E4M3(v / 2^X) rounded to nearest with ties to even and saturated at +-448. The
+ * dot products then use the decoded values (fp32 accumulation). Two-level selection with MXFP8
+ * keys is not supported (SA_ERR_UNSUPPORTED). */
 typedef struct sa_indexer {
     int32_t heads;            /* H_I: 1..64 */
     int32_t dim;              /* d_I: 64 or 128 */
-    sa_dtype key_dtype;       /* SA_BF16 or SA_FP8_E4M3 */
+    sa_dtype key_dtype;       /* SA_BF16, SA_FP8_E4M3 or SA_MXFP8 */
     const void *keys;         /* device [num_pages][page_size][dim] */
     const float *key_scale;   /* device [num_pages][page_size] for E4M3 keys, else NULL */
     const void *pooled;       /* device bf16 [num_pages][dim]: one summary key per page for
                                  two-level selection ([SameDay] §3.1: coarse filtering over
                                  summaries already held in the cache), or NULL */
+    const uint8_t *key_mx_scale; /* device [num_pages][page_size][dim / 32] E8M0 bytes for
+                                    SA_MXFP8 keys (4-byte aligned), else NULL */
 } sa_indexer;
 
 /* The attention KV cache. One KV head (MQA/MLA style: every query head reads the same row).

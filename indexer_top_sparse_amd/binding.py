@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
-SA_BF16, SA_FP8_E4M3 = 0, 1
+SA_BF16, SA_FP8_E4M3, SA_MXFP8 = 0, 1, 2
 
 
 class SaError(RuntimeError):
@@ -34,7 +34,8 @@ class sa_batch(C.Structure):
 
 class sa_indexer(C.Structure):
     _fields_ = [("heads", C.c_int32), ("dim", C.c_int32), ("key_dtype", C.c_int),
-                ("keys", C.c_void_p), ("key_scale", C.c_void_p), ("pooled", C.c_void_p)]
+                ("keys", C.c_void_p), ("key_scale", C.c_void_p), ("pooled", C.c_void_p),
+                ("key_mx_scale", C.c_void_p)]
 
 
 class sa_kv(C.Structure):
@@ -120,11 +121,15 @@ class Batch:
                           else None)
 
 
-def indexer_desc(heads, dim, keys, key_scale=None, pooled=None):
-    dt = SA_FP8_E4M3 if key_scale is not None else SA_BF16
+def indexer_desc(heads, dim, keys, key_scale=None, pooled=None, key_mx_scale=None):
+    if key_mx_scale is not None:
+        dt = SA_MXFP8
+    else:
+        dt = SA_FP8_E4M3 if key_scale is not None else SA_BF16
     return sa_indexer(heads, dim, dt, keys.data_ptr(),
                       key_scale.data_ptr() if key_scale is not None else None,
-                      pooled.data_ptr() if pooled is not None else None)
+                      pooled.data_ptr() if pooled is not None else None,
+                      key_mx_scale.data_ptr() if key_mx_scale is not None else None)
 
 
 def kv_desc(heads_q, dim_qk, dim_v, k, v=None, scale=None, softmax_scale=1.0, heads_kv=1):

@@ -79,11 +79,15 @@ sa_status check_indexer(const sa_indexer *ix) {
     if (!ix) return fail(SA_ERR_INVALID, "indexer descriptor is NULL");
     if (ix->heads < 1 || ix->heads > 64) return fail(SA_ERR_UNSUPPORTED, "indexer heads must be 1..64");
     if (ix->dim != 64 && ix->dim != 128) return fail(SA_ERR_UNSUPPORTED, "indexer dim must be 64 or 128");
-    if (ix->key_dtype != SA_BF16 && ix->key_dtype != SA_FP8_E4M3)
+    if (ix->key_dtype != SA_BF16 && ix->key_dtype != SA_FP8_E4M3 && ix->key_dtype != SA_MXFP8)
         return fail(SA_ERR_INVALID, "unknown indexer key dtype");
     if (!ix->keys || !aligned16(ix->keys)) return fail(SA_ERR_INVALID, "indexer keys NULL or not 16-byte aligned");
     if ((ix->key_dtype == SA_FP8_E4M3) != (ix->key_scale != nullptr))
         return fail(SA_ERR_INVALID, "key_scale must be given exactly for E4M3 keys");
+    if ((ix->key_dtype == SA_MXFP8) != (ix->key_mx_scale != nullptr))
+        return fail(SA_ERR_INVALID, "key_mx_scale must be given exactly for MXFP8 keys");
+    if (ix->key_mx_scale && (reinterpret_cast<uintptr_t>(ix->key_mx_scale) & 3u))
+        return fail(SA_ERR_INVALID, "key_mx_scale not 4-byte aligned");
     if (ix->pooled && !aligned16(ix->pooled)) return fail(SA_ERR_INVALID, "pooled not 16-byte aligned");
     return SA_OK;
 }
@@ -206,8 +210,8 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
 sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
                      int mode, int k, int block_k, const int32_t *blocks, int32_t *idx_out,
                      int32_t *slots_out, uint8_t *ws, const WsLayout &L, hipStream_t st) {
-    const bool fp8 = mode != 1 && ix->key_dtype == SA_FP8_E4M3;
-    void *kern = decode_select_kernel(ix->dim, ix->heads, fp8, mode);
+    void *kern = decode_select_kernel(ix->dim, ix->heads, (int)ix->key_dtype, mode);
+    if (!kern) return fail(SA_ERR_UNSUPPORTED, "no selection kernel for this key dtype and mode");
     const int threads = 512;
     const int lp = log2i(b->page_size);
     const int cus = device_cus();
@@ -273,6 +277,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         a.w = w + (int64_t)s0 * ix->heads;
         a.keys = static_cast<const uint8_t *>(mode == 1 ? ix->pooled : ix->keys);
         a.key_scale = ix->key_scale;
+        a.key_mx = ix->key_mx_scale;
         a.idx_out = idx_out + (int64_t)s0 * k;
         a.slots_out = slots_out ? slots_out + (int64_t)s0 * k : nullptr;
         a.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
@@ -387,14 +392,15 @@ sa_status sa_index_score(const sa_batch *batch, const sa_indexer *ix, const void
     a.w = w;
     a.keys = static_cast<const uint8_t *>(ix->keys);
     a.key_scale = ix->key_scale;
+    a.key_mx = ix->key_mx_scale;
     a.scores = scores;
     a.ld = ld;
     a.row_blocks = 0;
     if (batch->q_indptr)
         for (int b = 0; b < batch->num_seqs; ++b)
             a.row_blocks += (batch->q_indptr_host[b + 1] - batch->q_indptr_host[b] + 7) / 8;
-    hipError_t e = launch_index_score(a, ix->dim, ix->heads, ix->key_dtype == SA_FP8_E4M3,
-                                      rp.rows, ld, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_index_score(a, ix->dim, ix->heads, (int)ix->key_dtype, rp.rows, ld,
+                                      static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "index score launch");
     return SA_OK;
 }
@@ -465,6 +471,8 @@ static sa_status check_select(const sa_batch *batch, RowPlan *rp, const sa_index
     if (!q_idx || !aligned16(q_idx) || !w) return fail(SA_ERR_INVALID, "q_idx (16-byte aligned) and w are required");
     if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
     if (block_k < 0 || block_k > 65536) return fail(SA_ERR_INVALID, "block_k must be in [0, 65536]");
+    if (block_k > 0 && ix->key_dtype == SA_MXFP8)
+        return fail(SA_ERR_UNSUPPORTED, "two-level selection with MXFP8 keys");
     if (block_k > 0 && !ix->pooled) return fail(SA_ERR_INVALID, "two-level selection needs ix->pooled");
     return SA_OK;
 }

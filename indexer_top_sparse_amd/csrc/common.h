@@ -31,6 +31,41 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D(16x16) += A(16x128) * B(128x16) on E4M3 codes with one E8M0 scale per row (A) or column
+// (B) and 32-entry block of k (v_mfma_scale_f32_16x16x128_f8f6f4). Lane l holds row / column
+// l%16: its first 16 code bytes (lo) are k = 16*(l/16) + j, the next 16 (hi) are
+// k = 64 + 16*(l/16) + j. The low byte of a lane's scale word is the E8M0 exponent of
+// (row / column l%16, block l/16). D is laid out as for mfma16x16x32.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_mx16x16x128(u32x4 alo, u32x4 ahi, uint32_t sa, u32x4 blo,
+                                                  u32x4 bhi, uint32_t sb, f32x4 c) {
+    const i32x8 a = {(int)alo[0], (int)alo[1], (int)alo[2], (int)alo[3],
+                     (int)ahi[0], (int)ahi[1], (int)ahi[2], (int)ahi[3]};
+    const i32x8 b = {(int)blo[0], (int)blo[1], (int)blo[2], (int)blo[3],
+                     (int)bhi[0], (int)bhi[1], (int)bhi[2], (int)bhi[3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+}
+
+// fp32 -> OCP E4M3 code: round to nearest, ties to even, saturating at +-448; the sign bit
+// follows the sign of y (so -0 and negatives that round to zero give 0x80). Magnitudes below
+// the smallest normal (2^-6) are multiples of 2^-9; above it the fp32 mantissa is rounded to 3
+// bits and a carry moves to the next binade by itself.
+__device__ __forceinline__ uint32_t e4m3_rne(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fminf(fabsf(y), 448.f);
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t cn = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);  // normal
+    const uint32_t cs = (uint32_t)rintf(a * 512.f);                                // subnormal
+    return (a < 0.015625f ? cs : cn) | sign;
+}
+
+// MX block exponent from the bit pattern of the block's largest magnitude (bf16, sign cleared):
+// floor(log2) of a normal value minus 8 (the exponent of E4M3's largest power of two), clamped
+// to [-127, 127]. Zero and subnormal maxima give -127.
+__device__ __forceinline__ int mx_block_exp(uint32_t amax_bf16) {
+    return max(-127, min(127, (int)(amax_bf16 >> 7) - 127 - 8));
+}
+
 // two fp32 -> two bf16 in one word (v_cvt_pk_bf16_f32: round to nearest even), lo first
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));

@@ -20,6 +20,10 @@ namespace sa {
 //   kCandidates: candidate i is token (blocks[i / P] * P + i % P) of a kept block (fine stage).
 enum { kTokens = 0, kBlocks = 1, kCandidates = 2 };
 
+// Indexer key formats: bf16, E4M3 with one fp32 scale per row, MXFP8 (E4M3 with one E8M0
+// exponent per 32 entries).
+enum { kKeyBf16 = 0, kKeyE4M3 = 1, kKeyMx = 2 };
+
 struct SeqCtx {
     int seq;
     int ctx;
@@ -94,9 +98,10 @@ template <int DIM, bool FP8>
 struct KeyFrag {
     u32x4 v[FP8 ? DIM / 64 : DIM / 32];
     float scale;  // E4M3 row scale (loaded with the codes so that no later load waits on it)
+    uint32_t mx;  // MXFP8: E8M0 exponent of the lane's block (see key_mx_scale)
 };
 
-template <int DIM, bool FP8>
+template <int DIM, bool FP8, bool ROWSCALE = FP8>
 __device__ __forceinline__ void load_key_frag(KeyFrag<DIM, FP8> &f, const uint8_t *keys,
                                               const float *key_scale, int64_t row) {
     const int g = lane_id() >> 4;
@@ -105,7 +110,7 @@ __device__ __forceinline__ void load_key_frag(KeyFrag<DIM, FP8> &f, const uint8_
     if (FP8) {
 #pragma unroll
         for (int c = 0; c < DIM / 64; ++c) f.v[c] = ldg16_stream(p + 64 * c + 16 * g);
-        f.scale = key_scale[row];
+        if (ROWSCALE) f.scale = key_scale[row];
     } else {
 #pragma unroll
         for (int s = 0; s < DIM / 32; ++s) f.v[s] = ldg16_stream(p + 64 * s + 16 * g);
@@ -126,6 +131,7 @@ struct KeyTile {
     static constexpr int RPB = 16 / CPR;            // tile rows per 256-byte LDS line
     u32x4 v[NL];
     float scale;  // E4M3 scale of the lane's own candidate (lane l % 16)
+    uint32_t mx;  // MXFP8: E8M0 exponent of block l / 16 of the lane's own candidate
 
     // LDS slot (16-byte units) of chunk c of tile row r. The XOR swizzle makes both access
     // patterns bank-conflict free: the row-major writes, and the fragment reads in which 16
@@ -148,6 +154,7 @@ __device__ __forceinline__ void tile_to_frag(const KeyTile<DIM, FP8> &t, u32x4 *
 #pragma unroll
     for (int x = 0; x < T::NL; ++x) f.v[x] = stage[T::slot(l & 15, 4 * x + (l >> 4))];
     f.scale = t.scale;
+    f.mx = t.mx;
 }
 
 // Score of the lane's candidate (lane l % 16; every lane of the 4 groups gets the same value).
@@ -183,12 +190,119 @@ __device__ __forceinline__ float score_tile(const IdxQuery<DIM, HT, FP8> &q,
     return part;
 }
 
+// ------------------------------------------------------------------ MXFP8 indexer
+// [CANN] §3: the indexer runs in MXFP8, with per-group dynamic quantization (groups of 32) of
+// the query and keys stored with one E8M0 exponent per 32 entries. On gfx950 one block-scaled
+// MFMA (16x16x128, E4M3 x E4M3, E8M0 scales per 32-entry block) takes a 16-head x 16-token
+// tile over the whole 128-entry head dimension: no conversion of key codes and no per-token
+// scale multiply. The query is quantized once per workgroup, in registers.
+//
+// Lane l of head tile ht holds head h = 16 ht + l%16 and the entries 16 g .. 16 g + 15 (lo) and
+// 64 + 16 g .. 64 + 16 g + 15 (hi) of its row, g = l / 16: these lie in blocks g/2 and 2 + g/2,
+// so the block maxima come from the lane and its partner l ^ 16. The MFMA wants, in lane l, the
+// exponent of block g, which lanes of group 2 (block 1) or 0 (block 2) computed. d_I = 64 keeps
+// hi zero and blocks 2, 3 at scale 1.
+template <int DIM, int HT>
+struct MxQuery {
+    u32x4 lo[HT], hi[HT];
+    uint32_t sc[HT];
+    float w[HT][4];
+
+    // 16 bf16 (two 16-byte words) -> 16 E4M3 codes of v / 2^x
+    __device__ static __forceinline__ u32x4 encode16(u32x4 a, u32x4 b, int x) {
+        u32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t w0 = j < 2 ? a[2 * j] : b[2 * j - 4];
+            const uint32_t w1 = j < 2 ? a[2 * j + 1] : b[2 * j - 3];
+            r[j] = e4m3_rne(ldexpf(bf16_lo(w0), -x)) | (e4m3_rne(ldexpf(bf16_hi(w0), -x)) << 8) |
+                   (e4m3_rne(ldexpf(bf16_lo(w1), -x)) << 16) |
+                   (e4m3_rne(ldexpf(bf16_hi(w1), -x)) << 24);
+        }
+        return r;
+    }
+    // largest magnitude of 16 bf16, as a bit pattern with the sign cleared (monotone in value)
+    __device__ static __forceinline__ uint32_t amax16(u32x4 a, u32x4 b) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m = max(m, max(a[j] & 0x7FFFu, (a[j] >> 16) & 0x7FFFu));
+            m = max(m, max(b[j] & 0x7FFFu, (b[j] >> 16) & 0x7FFFu));
+        }
+        return m;
+    }
+
+    __device__ __forceinline__ void load(const uint16_t *q_row, const float *w_row, int heads) {
+        const int l = lane_id(), g = l >> 4;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int h = 16 * ht + (l & 15);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const uint16_t *p = q_row + (size_t)h * DIM + 16 * g;
+            const bool ok = h < heads;
+            const u32x4 a0 = ok ? ldg16(p) : z, a1 = ok ? ldg16(p + 8) : z;
+            u32x4 b0 = z, b1 = z;
+            if (DIM == 128 && ok) {
+                b0 = ldg16(p + 64);
+                b1 = ldg16(p + 72);
+            }
+            uint32_t m0 = amax16(a0, a1), m1 = amax16(b0, b1);
+            m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16, 64));
+            m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16, 64));
+            const int x0 = mx_block_exp(m0);  // block g / 2
+            const int x1 = mx_block_exp(m1);  // block 2 + g / 2
+            lo[ht] = encode16(a0, a1, x0);
+            hi[ht] = DIM == 128 ? encode16(b0, b1, x1) : z;
+            const int from2 = __shfl(x0, (l & 15) + 32, 64);  // block 1
+            const int from0 = __shfl(x1, l & 15, 64);         // block 2
+            int x;
+            if (DIM == 128) x = g == 0 ? x0 : g == 1 ? from2 : g == 2 ? from0 : x1;
+            else x = g == 0 ? x0 : g == 1 ? from2 : 0;
+            sc[ht] = (uint32_t)(x + 127);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int hh = 16 * ht + 4 * g + i;
+                w[ht][i] = hh < heads ? w_row[hh] : 0.f;
+            }
+        }
+    }
+};
+
+// E8M0 exponent that lane l supplies for its token's key row: block l / 16 (1.0 for the absent
+// blocks 2, 3 of d_I = 64).
+template <int DIM>
+__device__ __forceinline__ uint32_t key_mx_scale(const uint8_t *key_mx, int64_t row) {
+    const int g = lane_id() >> 4;
+    return g < DIM / 32 ? (uint32_t)key_mx[row * (DIM / 32) + g] : 127u;
+}
+
+// MXFP8 score of the lane's candidate (lane l % 16; every lane of the 4 groups gets the same
+// value). The fragment holds the token's codes in the E4M3 layout of KeyFrag (chunk g, and for
+// d_I = 128 chunk 4 + g) and its block exponent in mx.
+template <int DIM, int HT>
+__device__ __forceinline__ float score_tile_mx(const MxQuery<DIM, HT> &q, const u32x4 *kv,
+                                               uint32_t mx) {
+    const u32x4 khi = DIM == 128 ? kv[1] : u32x4{0u, 0u, 0u, 0u};
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const f32x4 acc = mfma_mx16x16x128(q.lo[ht], q.hi[ht], q.sc[ht], kv[0], khi, mx,
+                                           f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(q.w[ht][i], relu(acc[i]), part);
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    return part;
+}
+
 // ============================================================== scores to HBM (sa_index_score)
 // Grid: (row, chunk of 1024 candidates). 4 waves; each wave walks 16-token tiles.
 constexpr int kScoreChunk = 1024;
 
-template <int DIM, int HT, bool FP8>
+template <int DIM, int HT, int KF>
 __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
+    constexpr bool FP8 = KF != kKeyBf16, MX = KF == kKeyMx;
     const int row = blockIdx.y;
     int seq, qoff, qlen;
     row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
@@ -202,7 +316,9 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
     if (c1 <= c0) return;
 
     IdxQuery<DIM, HT, FP8> q;
-    q.load(a.q_idx + (size_t)row * a.heads * DIM, a.w + (size_t)row * a.heads, a.heads);
+    MxQuery<DIM, HT> qm;
+    if constexpr (MX) qm.load(a.q_idx + (size_t)row * a.heads * DIM, a.w + (size_t)row * a.heads, a.heads);
+    else q.load(a.q_idx + (size_t)row * a.heads * DIM, a.w + (size_t)row * a.heads, a.heads);
     SeqCtx s{seq, ctx, ctx, a.page_table + (int64_t)seq * a.pages_per_seq, nullptr};
     const int l = lane_id();
     const int ntiles = (c1 - (int)c0 + 15) >> 4;
@@ -214,9 +330,15 @@ __global__ __launch_bounds__(256) void k_index_score(ScoreArgs a) {
         int64_t krow;
         cand_row<kTokens>(s, i, a.lp, pos, krow);
         KeyFrag<DIM, FP8> f;
-        load_key_frag<DIM, FP8>(f, a.keys, a.key_scale, krow);
-        float sc = score_tile<DIM, HT, FP8>(q, f);
-        if (FP8) sc *= f.scale;
+        float sc;
+        if constexpr (MX) {
+            load_key_frag<DIM, true, false>(f, a.keys, nullptr, krow);
+            sc = score_tile_mx<DIM, HT>(qm, f.v, key_mx_scale<DIM>(a.key_mx, krow));
+        } else {
+            load_key_frag<DIM, FP8>(f, a.keys, a.key_scale, krow);
+            sc = score_tile<DIM, HT, FP8>(q, f);
+            if (FP8) sc *= f.scale;
+        }
         if (valid && l < 16) out[i] = sc;
     }
 }
@@ -489,8 +611,9 @@ __host__ __device__ inline int chunk_table_entries(int mode, int chunk, int lp) 
     return mode == kBlocks ? chunk : (chunk >> lp) + 2;
 }
 
-template <int DIM, int HT, bool FP8, int MODE>
+template <int DIM, int HT, int KF, int MODE>
 __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
+    constexpr bool FP8 = KF != kKeyBf16, MX = KF == kKeyMx;
     extern __shared__ uint32_t s_key[];  // [chunk] keys, then the chunk address table
     __shared__ SelShared sh;
     __shared__ u32x4 s_stage[kSelWaves][256];  // per-wave key-tile transpose area (4 KiB)
@@ -575,7 +698,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- scores of this chunk -> LDS keys (0 = not a candidate)
     if (cnt > 0) {
         IdxQuery<DIM, HT, FP8> q;
-        q.load(a.q_idx + (size_t)seq * a.heads * DIM, a.w + (size_t)seq * a.heads, a.heads);
+        MxQuery<DIM, HT> qm;
+        if constexpr (MX) qm.load(a.q_idx + (size_t)seq * a.heads * DIM, a.w + (size_t)seq * a.heads, a.heads);
+        else q.load(a.q_idx + (size_t)seq * a.heads * DIM, a.w + (size_t)seq * a.heads, a.heads);
         const int ntiles = (cnt + 15) >> 4;
         const int w = wave_id();
         const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
@@ -606,7 +731,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 int pos;
                 int64_t r;
                 cr.cand(s, i < c1 ? i : c0, c0, a.lp, pos, r);
-                f[slot].scale = r >= 0 ? a.key_scale[r] : 1.f;
+                if (MX) f[slot].mx = r >= 0 ? key_mx_scale<DIM>(a.key_mx, r) : 127u;
+                else f[slot].scale = r >= 0 ? a.key_scale[r] : 1.f;
             }
         };
 #pragma unroll
@@ -621,8 +747,13 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                     KeyFrag<DIM, FP8> fr;
                     tile_to_frag<DIM, FP8>(f[j], stage, fr);
                     issue(j, k + kPre);
-                    float sc = score_tile<DIM, HT, FP8>(q, fr);
-                    if (FP8) sc *= fr.scale;
+                    float sc;
+                    if constexpr (MX) {
+                        sc = score_tile_mx<DIM, HT>(qm, fr.v, fr.mx);
+                    } else {
+                        sc = score_tile<DIM, HT, FP8>(q, fr);
+                        if (FP8) sc *= fr.scale;
+                    }
                     if (l < 16 && c0 + li < c1) {
                         bool ok = true;
                         if (MODE == kCandidates) {
@@ -998,10 +1129,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
 }
 
 // ------------------------------------------------------------------ launchers
-template <int DIM, int HT, bool FP8>
+template <int DIM, int HT, int KF>
 static hipError_t launch_score_t(const ScoreArgs &a, int rows, int64_t max_cols, hipStream_t st) {
     dim3 grid((unsigned)((max_cols + kScoreChunk - 1) / kScoreChunk), (unsigned)rows);
-    hipLaunchKernelGGL((k_index_score<DIM, HT, FP8>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_index_score<DIM, HT, KF>), grid, dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
@@ -1012,9 +1143,26 @@ static hipError_t launch_prefill_t(const ScoreArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, int rows,
+template <int DIM, int KF>
+static hipError_t launch_score_heads(const ScoreArgs &a, int heads, int rows, int64_t max_cols,
+                                     hipStream_t st) {
+    return heads <= 16 ? launch_score_t<DIM, 1, KF>(a, rows, max_cols, st)
+                       : launch_score_t<DIM, 4, KF>(a, rows, max_cols, st);
+}
+
+template <int KF>
+static hipError_t launch_score_kf(const ScoreArgs &a, int dim, int heads, int rows,
+                                  int64_t max_cols, hipStream_t st) {
+    return dim == 128 ? launch_score_heads<128, KF>(a, heads, rows, max_cols, st)
+                      : launch_score_heads<64, KF>(a, heads, rows, max_cols, st);
+}
+
+hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, int key_fmt, int rows,
                               int64_t max_cols, hipStream_t st) {
-    if (a.q_indptr) {  // query rows grouped per sequence: dense GEMM
+    const bool fp8 = key_fmt == kKeyE4M3;
+    // query rows grouped per sequence: dense GEMM (MXFP8 keys take the row-wise kernel, which
+    // handles grouped rows too)
+    if (a.q_indptr && key_fmt != kKeyMx) {
         if (a.row_blocks == 0) return hipSuccess;
         if (dim == 128) {
             if (heads <= 32) return fp8 ? launch_prefill_t<128, 1, true>(a, st) : launch_prefill_t<128, 1, false>(a, st);
@@ -1023,42 +1171,32 @@ hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, 
         if (heads <= 32) return fp8 ? launch_prefill_t<64, 1, true>(a, st) : launch_prefill_t<64, 1, false>(a, st);
         return fp8 ? launch_prefill_t<64, 2, true>(a, st) : launch_prefill_t<64, 2, false>(a, st);
     }
-    const bool small = heads <= 16;
-    if (dim == 128) {
-        if (fp8) return small ? launch_score_t<128, 1, true>(a, rows, max_cols, st)
-                              : launch_score_t<128, 4, true>(a, rows, max_cols, st);
-        return small ? launch_score_t<128, 1, false>(a, rows, max_cols, st)
-                     : launch_score_t<128, 4, false>(a, rows, max_cols, st);
-    }
-    if (fp8) return small ? launch_score_t<64, 1, true>(a, rows, max_cols, st)
-                          : launch_score_t<64, 4, true>(a, rows, max_cols, st);
-    return small ? launch_score_t<64, 1, false>(a, rows, max_cols, st)
-                 : launch_score_t<64, 4, false>(a, rows, max_cols, st);
+    if (key_fmt == kKeyMx) return launch_score_kf<kKeyMx>(a, dim, heads, rows, max_cols, st);
+    if (fp8) return launch_score_kf<kKeyE4M3>(a, dim, heads, rows, max_cols, st);
+    return launch_score_kf<kKeyBf16>(a, dim, heads, rows, max_cols, st);
 }
 
-template <int DIM, int HT, bool FP8, int MODE>
+template <int DIM, int HT, int KF, int MODE>
 static void *select_kernel_ptr() {
-    return reinterpret_cast<void *>(&k_decode_select<DIM, HT, FP8, MODE>);
+    return reinterpret_cast<void *>(&k_decode_select<DIM, HT, KF, MODE>);
 }
 
-template <int DIM, int HT, bool FP8>
-static void *select_kernel_mode(int mode) {
-    if (mode == kTokens) return select_kernel_ptr<DIM, HT, FP8, kTokens>();
-    if (mode == kBlocks) return select_kernel_ptr<DIM, HT, false, kBlocks>();
-    return select_kernel_ptr<DIM, HT, FP8, kCandidates>();
+// pooled summaries (kBlocks) are bf16 whatever the key format; MXFP8 keys only take kTokens
+template <int DIM, int HT>
+static void *select_kernel_mode(int key_fmt, int mode) {
+    if (mode == kBlocks) return select_kernel_ptr<DIM, HT, kKeyBf16, kBlocks>();
+    if (key_fmt == kKeyMx) return mode == kTokens ? select_kernel_ptr<DIM, HT, kKeyMx, kTokens>() : nullptr;
+    if (key_fmt == kKeyE4M3)
+        return mode == kTokens ? select_kernel_ptr<DIM, HT, kKeyE4M3, kTokens>()
+                               : select_kernel_ptr<DIM, HT, kKeyE4M3, kCandidates>();
+    return mode == kTokens ? select_kernel_ptr<DIM, HT, kKeyBf16, kTokens>()
+                           : select_kernel_ptr<DIM, HT, kKeyBf16, kCandidates>();
 }
 
-void *decode_select_kernel(int dim, int heads, bool fp8, int mode) {
+void *decode_select_kernel(int dim, int heads, int key_fmt, int mode) {
     const bool small = heads <= 16;
-    if (dim == 128) {
-        if (fp8) return small ? select_kernel_mode<128, 1, true>(mode)
-                              : select_kernel_mode<128, 4, true>(mode);
-        return small ? select_kernel_mode<128, 1, false>(mode)
-                     : select_kernel_mode<128, 4, false>(mode);
-    }
-    if (fp8) return small ? select_kernel_mode<64, 1, true>(mode)
-                          : select_kernel_mode<64, 4, true>(mode);
-    return small ? select_kernel_mode<64, 1, false>(mode) : select_kernel_mode<64, 4, false>(mode);
+    if (dim == 128) return small ? select_kernel_mode<128, 1>(key_fmt, mode) : select_kernel_mode<128, 4>(key_fmt, mode);
+    return small ? select_kernel_mode<64, 1>(key_fmt, mode) : select_kernel_mode<64, 4>(key_fmt, mode);
 }
 
 size_t decode_select_static_lds() { return sizeof(SelShared); }

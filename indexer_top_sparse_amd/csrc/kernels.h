@@ -52,6 +52,7 @@ struct ScoreArgs {
     const float *w;
     const uint8_t *keys;
     const float *key_scale;
+    const uint8_t *key_mx;  // MXFP8 keys: E8M0 exponents [rows][dim / 32], else null
     float *scores;
     int64_t ld;
 };
@@ -75,6 +76,7 @@ struct SelectArgs {
     const float *w;
     const uint8_t *keys;
     const float *key_scale;
+    const uint8_t *key_mx;  // MXFP8 keys: E8M0 exponents [rows][dim / 32], else null
     int32_t *idx_out;    // [num_seqs][k]
     int32_t *slots_out;  // [num_seqs][k] physical rows of the selected positions, or null
     SelSync *sync;
@@ -109,9 +111,10 @@ struct AttnArgs {
     float *part_ml;     // [rows][splits][heads_q][2]
 };
 
-hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, bool fp8, int rows,
+// key_fmt: 0 bf16, 1 E4M3 with a row scale, 2 MXFP8 (the values of sa_dtype)
+hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, int key_fmt, int rows,
                               int64_t max_cols, hipStream_t st);
-void *decode_select_kernel(int dim, int heads, bool fp8, int mode);
+void *decode_select_kernel(int dim, int heads, int key_fmt, int mode);  // null: unsupported
 size_t decode_select_static_lds();
 size_t decode_select_dynamic_lds(int mode, int chunk, int lp);
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);

@@ -37,6 +37,7 @@ def to_device(wl, device="cuda", prefill: bool | None = None) -> DeviceWorkload:
     put("w", wl.w)
     put("idx_keys", wl.idx_keys)
     put("idx_scale", wl.idx_scale)
+    put("idx_mx_scale", getattr(wl, "idx_mx_scale", None))
     put("pooled", wl.pooled)
     put("q", wl.q)
     put("k_cache", wl.k_cache)
@@ -45,7 +46,7 @@ def to_device(wl, device="cuda", prefill: bool | None = None) -> DeviceWorkload:
     batch = B.Batch(t["page_table"], t["ctx_lens"], wl.ctx_lens, wl.page_size, wl.num_pages,
                     t.get("q_indptr"), wl.q_indptr().tolist() if prefill else None)
     ix = B.indexer_desc(wl.idx_heads, wl.idx_dim, t["idx_keys"], t.get("idx_scale"),
-                        t.get("pooled"))
+                        t.get("pooled"), t.get("idx_mx_scale"))
     kv = B.kv_desc(wl.heads_q, wl.dim_qk, wl.dim_v, t["k_cache"], t.get("v_cache"),
                    t.get("kv_scale"), wl.softmax_scale, wl.heads_kv)
     return DeviceWorkload(wl, batch, ix, kv, t)

@@ -56,6 +56,28 @@ def test_mx_quantize_exact_block():
     np.testing.assert_array_equal(oracle.e4m3_decode(codes) * 2.0 ** -6, vals)
 
 
+def test_mx_quantize_corner_block():
+    """A block whose largest magnitude is 464 (X = floor(log2 464) - 8 = 0, so the elements are
+    encoded as they are): 464 lies above E4M3's largest value and saturates to 448 (0x7E);
+    1.0625, 17, 19 and -1.1875 sit exactly between two E4M3 neighbours and go to the one with
+    the even mantissa (1.0, 16, 20, -1.25); in the subnormal range (steps of 2^-9) 1.5 steps
+    rounds to 2 steps, half a step to 0, and minus half a step to -0 (0x80). Codes derived by
+    hand from the E4M3 layout (sign, 4 exponent bits with bias 7, 3 mantissa bits)."""
+    vals = [464.0, 1.0625, 17.0, 19.0, -1.1875, 3 * 2.0 ** -10, 2.0 ** -10, -2.0 ** -10,
+            -300.0, 255.0, 0.5, -0.03125]
+    want = [0x7E, 0x38, 0x58, 0x5A, 0xBA, 0x02, 0x00, 0x80,
+            0xF9,         # -300: between -288 (1.125 x 2^8) and -320 (1.25 x 2^8), nearer -288
+            0x78,         # 255 -> 256 = 1.0 x 2^8
+            0x30,         # 0.5 = 2^-1: exponent field 6
+            0x90]         # -0.03125 = -2^-5: exponent field 2
+    blk = vals + [0.0] * (32 - len(vals))
+    bits = to_bf16(blk).view(torch.int16).numpy().view(np.uint16)
+    codes, e8m0 = oracle.mx_quantize_bf16(bits)
+    assert e8m0.tolist() == [127]
+    assert [int(c) for c in codes[:len(vals)]] == want
+    assert not np.any(codes[len(vals):])
+
+
 def test_mx_quantize_rounding_bound():
     """Random bf16 blocks: every element is within half an E4M3 step of its value (relative
     2^-4 in the normal range, 2^(X-10) absolute in the subnormal range), except elements whose
