@@ -76,15 +76,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Four E4M3 codes (one 32-bit word, byte 0 first) -> four bf16 (two words). E4M3 values are
-// exact in fp32 and in bf16, so the conversion through fp32 is exact.
+// Four E4M3 codes (one 32-bit word, byte 0 first) -> four bf16 (two words), two codes per
+// instruction (v_cvt_scalef32_pk_bf16_fp8 with scale 1). Every E4M3 value, subnormals included,
+// is exact in bf16.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t codes) {
-    f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
-    f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
-    u32x2 r;
-    r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xFFFF0000u);
-    r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xFFFF0000u);
-    return r;
+    const bf16x2v lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.f, false);
+    const bf16x2v hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
 // Order-preserving map float -> uint32 (larger float <=> larger key). -0 maps like +0. Key 0

@@ -77,16 +77,17 @@ struct IdxQuery {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int h = 16 * ht + (l & 15);
+            const int hc = min(h, heads - 1);  // loads stay unconditional; padding heads are zeroed
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (h < heads) v = ldg16(q_row + (size_t)h * DIM + d_of(s, g));
-                a[ht][s] = v;
+                const u32x4 v = ldg16(q_row + (size_t)hc * DIM + d_of(s, g));
+                a[ht][s] = h < heads ? v : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int hh = 16 * ht + 4 * g + i;
-                w[ht][i] = hh < heads ? w_row[hh] : 0.f;
+                const float x = w_row[min(hh, heads - 1)];
+                w[ht][i] = hh < heads ? x : 0.f;
             }
         }
     }
@@ -234,18 +235,27 @@ struct MxQuery {
 
     __device__ __forceinline__ void load(const uint16_t *q_row, const float *w_row, int heads) {
         const int l = lane_id(), g = l >> 4;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        // all loads first (unconditional, padding heads read a valid row and are zeroed), so
+        // that one wait covers them
+        u32x4 raw[HT][4];
+        float wr[HT][4];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int h = 16 * ht + (l & 15);
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            const uint16_t *p = q_row + (size_t)h * DIM + 16 * g;
+            const uint16_t *p = q_row + (size_t)min(h, heads - 1) * DIM + 16 * g;
+#pragma unroll
+            for (int c = 0; c < (DIM == 128 ? 4 : 2); ++c) raw[ht][c] = ldg16(p + (c >> 1) * 64 + (c & 1) * 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wr[ht][i] = w_row[min(16 * ht + 4 * g + i, heads - 1)];
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int h = 16 * ht + (l & 15);
             const bool ok = h < heads;
-            const u32x4 a0 = ok ? ldg16(p) : z, a1 = ok ? ldg16(p + 8) : z;
-            u32x4 b0 = z, b1 = z;
-            if (DIM == 128 && ok) {
-                b0 = ldg16(p + 64);
-                b1 = ldg16(p + 72);
-            }
+            const u32x4 a0 = ok ? raw[ht][0] : z, a1 = ok ? raw[ht][1] : z;
+            const u32x4 b0 = (DIM == 128 && ok) ? raw[ht][2] : z;
+            const u32x4 b1 = (DIM == 128 && ok) ? raw[ht][3] : z;
             uint32_t m0 = amax16(a0, a1), m1 = amax16(b0, b1);
             m0 = max(m0, (uint32_t)__shfl_xor((int)m0, 16, 64));
             m1 = max(m1, (uint32_t)__shfl_xor((int)m1, 16, 64));
@@ -260,20 +270,19 @@ struct MxQuery {
             else x = g == 0 ? x0 : g == 1 ? from2 : 0;
             sc[ht] = (uint32_t)(x + 127);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int hh = 16 * ht + 4 * g + i;
-                w[ht][i] = hh < heads ? w_row[hh] : 0.f;
-            }
+            for (int i = 0; i < 4; ++i) w[ht][i] = 16 * ht + 4 * g + i < heads ? wr[ht][i] : 0.f;
         }
     }
 };
 
-// E8M0 exponent that lane l supplies for its token's key row: block l / 16 (1.0 for the absent
-// blocks 2, 3 of d_I = 64).
+// E8M0 exponent that lane l supplies for its token's key row: block l / 16. For d_I = 64 the
+// blocks 2, 3 hold zero codes, and lanes 32..63 repeat the exponents of blocks 0, 1 (any finite
+// scale of a zero block adds nothing). No select follows the load, so nothing that consumes it
+// is forced to wait where it would be placed.
 template <int DIM>
 __device__ __forceinline__ uint32_t key_mx_scale(const uint8_t *key_mx, int64_t row) {
     const int g = lane_id() >> 4;
-    return g < DIM / 32 ? (uint32_t)key_mx[row * (DIM / 32) + g] : 127u;
+    return key_mx[row * (DIM / 32) + (g % (DIM / 32))];
 }
 
 // MXFP8 score of the lane's candidate (lane l % 16; every lane of the 4 groups gets the same
@@ -716,8 +725,13 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             cr.cand(s, i, c0, a.lp, pos, r);
             return r < 0 ? 0 : r;
         };
+        // Every step issues the same loads: a step past the wave's last tile reloads that tile
+        // (an L2 hit), and loads whose value is not needed read a valid row and are discarded
+        // by the consumer. The number of loads issued after a tile's own is then the same on every
+        // path, so the wait before each tile is exact and kPre tiles stay in flight; a load
+        // behind a branch would make the compiler wait for every outstanding load instead.
         auto issue = [&](int slot, int k) {
-            if (k >= my_tiles) return;
+            k = min(k, my_tiles - 1);
             const int i0 = c0 + 16 * (w + k * kSelWaves);
             const int64_t base = contiguous ? tile_base_row(cr, i0, a.lp) : 0;
 #pragma unroll
@@ -731,38 +745,47 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 int pos;
                 int64_t r;
                 cr.cand(s, i < c1 ? i : c0, c0, a.lp, pos, r);
-                if (MX) f[slot].mx = r >= 0 ? key_mx_scale<DIM>(a.key_mx, r) : 127u;
-                else f[slot].scale = r >= 0 ? a.key_scale[r] : 1.f;
+                // a candidate without a row (a dropped block) reads row 0; its key is discarded
+                const int64_t rr = r >= 0 ? r : 0;
+                if (MX) f[slot].mx = key_mx_scale<DIM>(a.key_mx, rr);
+                else f[slot].scale = a.key_scale[rr];
             }
         };
+        if (my_tiles > 0) {
 #pragma unroll
-        for (int k = 0; k < kPre; ++k) issue(k, k);
-        for (int k0 = 0; k0 < my_tiles; k0 += kPre) {
+            for (int k = 0; k < kPre; ++k) issue(k, k);
+            for (int k0 = 0; k0 < my_tiles; k0 += kPre) {
 #pragma unroll
-            for (int j = 0; j < kPre; ++j) {
-                const int k = k0 + j;
-                if (k < my_tiles) {
-                    const int tt = w + k * kSelWaves;
-                    const int li = 16 * tt + (l & 15);
+                for (int j = 0; j < kPre; ++j) {
+                    const int k = k0 + j;
                     KeyFrag<DIM, FP8> fr;
                     tile_to_frag<DIM, FP8>(f[j], stage, fr);
+                    // take the tile's scale word here, before the next load into its slot: a
+                    // plain copy would be placed after that load is issued, and the register
+                    // rotation it causes waits for every outstanding load
+                    if constexpr (MX) asm volatile("v_mov_b32 %0, %1" : "=v"(fr.mx) : "v"(f[j].mx));
+                    else if constexpr (FP8) asm volatile("v_mov_b32 %0, %1" : "=v"(fr.scale) : "v"(f[j].scale));
                     issue(j, k + kPre);
-                    float sc;
-                    if constexpr (MX) {
-                        sc = score_tile_mx<DIM, HT>(qm, fr.v, fr.mx);
-                    } else {
-                        sc = score_tile<DIM, HT, FP8>(q, fr);
-                        if (FP8) sc *= fr.scale;
-                    }
-                    if (l < 16 && c0 + li < c1) {
-                        bool ok = true;
-                        if (MODE == kCandidates) {
-                            int pos;
-                            int64_t r;
-                            cr.cand(s, c0 + li, c0, a.lp, pos, r);
-                            ok = r >= 0;
+                    if (k < my_tiles) {
+                        const int tt = w + k * kSelWaves;
+                        const int li = 16 * tt + (l & 15);
+                        float sc;
+                        if constexpr (MX) {
+                            sc = score_tile_mx<DIM, HT>(qm, fr.v, fr.mx);
+                        } else {
+                            sc = score_tile<DIM, HT, FP8>(q, fr);
+                            if (FP8) sc *= fr.scale;
                         }
-                        s_key[li] = ok ? float_key(sc) : 0u;
+                        if (l < 16 && c0 + li < c1) {
+                            bool ok = true;
+                            if (MODE == kCandidates) {
+                                int pos;
+                                int64_t r;
+                                cr.cand(s, c0 + li, c0, a.lp, pos, r);
+                                ok = r >= 0;
+                            }
+                            s_key[li] = ok ? float_key(sc) : 0u;
+                        }
                     }
                 }
             }
