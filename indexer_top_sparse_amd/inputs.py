@@ -50,11 +50,13 @@ class Workload:
     heads_kv: int
     dim_qk: int
     dim_v: int
-    kv_dtype: str             # "bf16" | "fp8"
+    kv_dtype: str             # "bf16" | "fp8" (one scale per row) | "fp8t128" (per 128 entries)
     q: torch.Tensor           # bf16 [nq, heads_q, dim_qk]
     k_cache: torch.Tensor     # [num_pages, page_size, heads_kv, k_row] (bf16 or uint8 codes)
     v_cache: Optional[torch.Tensor]  # None when V is the first dim_v entries of each K row
-    kv_scale: Optional[torch.Tensor]  # fp32 [num_pages, page_size] (fp8) else None
+    # fp32 [num_pages, page_size] (fp8), [num_pages, page_size, heads_kv, ceil(dim_qk / 128)]
+    # (fp8t128), else None
+    kv_scale: Optional[torch.Tensor]
     softmax_scale: float
     seeds: dict = field(default_factory=dict)
     # uint8 E8M0 bytes [num_pages, page_size, idx_dim / 32] (mxfp8 indexer keys) else None
@@ -114,6 +116,22 @@ def quantize_rows_e4m3(x: torch.Tensor):
     sigma = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
     codes = (x / sigma.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
     return codes.view(torch.uint8), sigma.to(torch.float32)
+
+
+def quantize_tiles_e4m3(x: torch.Tensor, tile: int = 128):
+    """Quantize fp32 ``x`` [..., n] to OCP E4M3 with one scale per ``tile`` consecutive elements
+    of the last dim (a shorter last tile keeps its own scale): sigma = tile absmax / 448 (1 for an
+    all-zero tile), code = RNE(clamp(x / sigma, -448, 448)). Returns (uint8 codes [..., n], fp32
+    sigma [..., ceil(n / tile)])."""
+    n = x.shape[-1]
+    nt = -(-n // tile)
+    pad = torch.zeros(*x.shape[:-1], nt * tile - n, dtype=x.dtype)
+    t = torch.cat([x, pad], dim=-1).reshape(*x.shape[:-1], nt, tile)
+    amax = t.abs().amax(dim=-1)
+    sigma = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    codes = (t / sigma.unsqueeze(-1)).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    codes = codes.view(torch.uint8).reshape(*x.shape[:-1], nt * tile)[..., :n].contiguous()
+    return codes, sigma.to(torch.float32)
 
 
 def quantize_rows_mxfp8(x: torch.Tensor):
@@ -184,11 +202,12 @@ PRESETS = {
                           page_size=64, idx_heads=64, idx_dim=128, weights="scaled", topk=2048,
                           heads_q=128, heads_kv=1, dim_qk=576, dim_v=512, mla=True, dtype="fp8",
                           q_len=1, block_topk=0)),
-    # the ragged E4M3 batch with the indexer in MXFP8 (groups of 32, E8M0 scales)
+    # the ragged batch in the pages' own FP8 granularities: the indexer in MXFP8 (groups of 32,
+    # E8M0 scales) and the KV cache in E4M3 with one scale per 128 entries of each row
     "mxfp8ragged": (6, dict(num_seqs=64, ctx="loguniform", ctx_lo=4096, ctx_hi=131072,
                             page_size=64, idx_heads=64, idx_dim=128, weights="scaled", topk=2048,
                             heads_q=128, heads_kv=1, dim_qk=576, dim_v=512, mla=True,
-                            dtype="fp8", idx_dtype="mxfp8", q_len=1, block_topk=0)),
+                            dtype="fp8t128", idx_dtype="mxfp8", q_len=1, block_topk=0)),
 }
 
 
@@ -263,6 +282,13 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
         k_cache, sc = quantize_rows_e4m3(kvf.reshape(num_pages, P, Hkv * dqk))
         k_cache = k_cache.reshape(num_pages, P, Hkv, dqk)
         kv_scale = sc
+    elif dtype == "fp8t128":
+        assert p["mla"], "tile scales are defined for latent rows (V inside K)"
+        # scales [pages, P, Hkv, tiles]; in slices of pages to bound the temporaries
+        parts = [quantize_tiles_e4m3(kvf[i:i + 2048], 128) for i in range(0, num_pages, 2048)]
+        k_cache = torch.cat([c for c, _ in parts])
+        kv_scale = torch.cat([t for _, t in parts])
+        del parts
     else:
         k_cache = kvf.to(torch.bfloat16)
     del kvf

@@ -51,7 +51,7 @@ def load(real: str = "f64"):
     lib.ora_topk_in_blocks.argtypes = [i32, P, P, i32, i32, P, P, i32, P, P, P, i32, i32, P,
                                        i32, i32, P]
     lib.ora_sparse_attn.argtypes = [i32, P, P, i32, i32, i32, i32, P, i32, P, P, P, P, i64,
-                                    i64, i64, i64, P, i32, i32, i32, P, f32, P]
+                                    i64, i64, i64, i32, i32, P, i32, i32, i32, P, f32, P]
     lib.ora_bf16.restype = C.c_double if real == "f64" else C.c_float
     lib.ora_bf16.argtypes = [C.c_uint16]
     lib.ora_e4m3.restype = C.c_double if real == "f64" else C.c_float
@@ -102,7 +102,9 @@ def _rows(wl, rows):
 
 
 def _fmt(dtype: str) -> int:
-    return 0 if dtype == "bf16" else 1
+    """Stored-vector formats: bf16; E4M3 with one fp32 scale per row; E4M3 with one fp32 scale
+    per 128-entry tile of each token and head (KV only)."""
+    return {"bf16": 0, "fp8": 1, "fp8t128": 2}[dtype]
 
 
 def bf16_decode(bits: np.ndarray, real: str = "f64") -> np.ndarray:
@@ -237,11 +239,16 @@ def sparse_attn(wl, idx: np.ndarray, rows=None, real: str = "f64") -> np.ndarray
         vc = _np(wl.v_cache)
         v_stride, v_head_stride = wl.heads_kv * wl.v_cache.shape[-1], wl.v_cache.shape[-1]
     sc = None if wl.kv_scale is None else _np(wl.kv_scale, np.float32)
+    k_tiles = v_tiles = 0
+    if wl.kv_dtype == "fp8t128":
+        assert wl.v_cache is None, "tile scales are defined for latent rows (V inside K)"
+        k_tiles = v_tiles = -(-wl.dim_qk // 128)
     pt = _np(wl.page_table, np.int32)
     out = np.empty((len(rows), wl.heads_q, wl.dim_v), dtype=lib.real_dtype)
     rc = lib.ora_sparse_attn(len(rows), _p(q_seq), _p(q_pos), wl.heads_q, wl.heads_kv,
                              wl.dim_qk, wl.dim_v, _p(q), _fmt(wl.kv_dtype), _p(kc), _p(vc),
-                             _p(sc), _p(sc), k_stride, v_stride, k_row, v_head_stride, _p(pt),
+                             _p(sc), _p(sc), k_stride, v_stride, k_row, v_head_stride, k_tiles,
+                             v_tiles, _p(pt),
                              wl.pages_per_seq, wl.page_size, k, _p(idx),
                              float(wl.softmax_scale), _p(out))
     assert rc == 0, "oracle sparse_attn rejected its inputs"

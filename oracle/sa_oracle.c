@@ -131,8 +131,8 @@ static int64_t slot_of(const int32_t *page_table, int pages_per_seq, int page_si
     return phys * page_size + offset;
 }
 
-/* element i of a stored vector: format 0 = bf16 bit patterns, 1 = E4M3 codes times a per-row
- * fp32 scale (scale_row is that row's scale; ignored for bf16). */
+/* element i of a stored vector: format 0 = bf16 bit patterns, 1 or 2 = E4M3 codes times an
+ * fp32 scale (scale_row: the scale that applies to this element; ignored for bf16). */
 static REAL elem(int fmt, const void *base, int64_t index, float scale_row) {
     if (fmt == 0) return ora_bf16(((const uint16_t *)base)[index]);
     return ora_e4m3(((const uint8_t *)base)[index]) * (REAL)scale_row;
@@ -384,15 +384,22 @@ int ora_topk_in_blocks(int nq, const int32_t *q_seq, const int64_t *q_pos, int h
  * An empty selection gives o = 0. Element (slot, g, i) of K is k_cache[slot * k_stride +
  * g * k_head_stride + i]; likewise V. V may be the same buffer as K (a latent row whose first
  * dim_v entries are the value). fp8 rows (kv_fmt 1) are code * k_scale[slot] (v_scale[slot]).
+ * kv_fmt 2 is FP8 with one scale per 128 consecutive entries within each token and head
+ * ([CANN] §3: per-token-head-tile quantization with a block of 128): entry i of head g of the
+ * row at slot is code * k_scale[(slot * heads_kv + g) * k_tiles + i / 128], k_tiles =
+ * ceil(dim_qk / 128) (a last, shorter tile keeps its own scale); V likewise with v_tiles. A
+ * latent V (the same buffer as K) passes the K scales and k_tiles, so entry i of the value is
+ * scaled exactly as entry i of the key row.
  * out: [nq, heads_q, dim_v].
  */
 int ora_sparse_attn(int nq, const int32_t *q_seq, const int64_t *q_pos, int heads_q,
                     int heads_kv, int dim_qk, int dim_v, const uint16_t *q, int kv_fmt,
                     const void *k_cache, const void *v_cache, const float *k_scale,
                     const float *v_scale, int64_t k_stride, int64_t v_stride,
-                    int64_t k_head_stride, int64_t v_head_stride, const int32_t *page_table,
-                    int pages_per_seq, int page_size, int k, const int32_t *idx,
-                    float softmax_scale, REAL *out) {
+                    int64_t k_head_stride, int64_t v_head_stride, int k_tiles, int v_tiles,
+                    const int32_t *page_table, int pages_per_seq, int page_size, int k,
+                    const int32_t *idx, float softmax_scale, REAL *out) {
+    if (kv_fmt == 2 && (k_tiles != (dim_qk + 127) / 128 || v_tiles < (dim_v + 127) / 128)) return 1;
     if (heads_kv <= 0 || heads_q % heads_kv) return 1;
     for (int r = 0; r < nq; r++)
         for (int j = 0; j < k; j++) {
@@ -415,11 +422,13 @@ int ora_sparse_attn(int nq, const int32_t *q_seq, const int64_t *q_pos, int head
         for (int j = 0; j < k; j++) {
             if (sel[j] < 0) continue;
             int64_t slot = slot_of(page_table, pages_per_seq, page_size, q_seq[r], sel[j]);
-            float ks = k_scale ? k_scale[slot] : 1.0f;
+            float ks = (k_scale && kv_fmt == 1) ? k_scale[slot] : 1.0f;
             REAL d = 0;
-            for (int i = 0; i < dim_qk; i++)
+            for (int i = 0; i < dim_qk; i++) {
+                if (kv_fmt == 2) ks = k_scale[(slot * heads_kv + g) * k_tiles + i / 128];
                 d += ora_bf16(qv[i]) *
                      elem(kv_fmt, k_cache, slot * k_stride + g * k_head_stride + i, ks);
+            }
             logit[j] = (REAL)softmax_scale * d;
             slots[j] = slot;
             if (isnan((double)logit[j])) bad = 1;
@@ -432,11 +441,13 @@ int ora_sparse_attn(int nq, const int32_t *q_seq, const int64_t *q_pos, int head
             for (int j = 0; j < k; j++) {
                 if (sel[j] < 0) continue;
                 REAL p = exp(logit[j] - m);
-                float vs = v_scale ? v_scale[slots[j]] : 1.0f;
+                float vs = (v_scale && kv_fmt == 1) ? v_scale[slots[j]] : 1.0f;
                 den += p;
-                for (int i = 0; i < dim_v; i++)
+                for (int i = 0; i < dim_v; i++) {
+                    if (kv_fmt == 2) vs = v_scale[(slots[j] * heads_kv + g) * v_tiles + i / 128];
                     o[i] += p * elem(kv_fmt, v_cache, slots[j] * v_stride + g * v_head_stride + i,
                                      vs);
+                }
             }
             for (int i = 0; i < dim_v; i++) o[i] /= den;
         }
