@@ -49,7 +49,8 @@ def algorithmic_bytes(wl):
     P, K = wl.page_size, wl.topk
     key_row = {"bf16": 2 * wl.idx_dim, "fp8": wl.idx_dim + 4,            # codes + fp32 row scale
                "mxfp8": wl.idx_dim + wl.idx_dim // 32}[wl.idx_dtype]    # codes + E8M0 per 32
-    kv_row = wl.k_row * (1 if wl.kv_dtype == "fp8" else 2) + (4 if wl.kv_dtype == "fp8" else 0)
+    kv_row = {"bf16": 2 * wl.k_row, "fp8": wl.k_row + 4,                     # codes + row scale
+              "fp8t128": wl.k_row + 4 * -(-wl.k_row // 128)}[wl.kv_dtype]   # + tile scales
     sel = attn = 0
     for n in wl.ctx_lens:
         npg = math.ceil(n / P)

@@ -60,8 +60,10 @@ typedef enum sa_status {
 typedef enum sa_dtype {
     SA_BF16 = 0,     /* bfloat16 */
     SA_FP8_E4M3 = 1, /* OCP E4M3 codes (max 448) times one fp32 scale per stored row */
-    SA_MXFP8 = 2     /* OCP microscaling: E4M3 codes, and for every 32 consecutive entries of a
+    SA_MXFP8 = 2,    /* OCP microscaling: E4M3 codes, and for every 32 consecutive entries of a
                         row one E8M0 byte e giving the scale 2^(e - 127) (indexer keys only) */
+    SA_FP8_E4M3_T128 = 3 /* OCP E4M3 codes times one fp32 scale per 128 consecutive entries of a
+                            row, a shorter last tile keeping its own (KV only) */
 } sa_dtype;
 
 /* Sequences, their lengths and the page table of the blocked KV layout ([Domestic] §3.2;
@@ -109,16 +111,21 @@ typedef struct sa_indexer {
 /* The attention KV cache. One KV head (MQA/MLA style: every query head reads the same row).
  * Row of slot s: K = k[s][0..dim_qk), V = v[s][0..dim_v), or, when v == NULL, V is the first
  * dim_v entries of the K row (a latent row as in MLA). For E4M3 rows, value = code *
- * scale[s] (one scale per row, used for K and V). */
+ * scale[s] (one scale per row, used for K and V). For E4M3 rows with 128-entry tiles ([CANN] §3:
+ * FP8 KV quantized per token-head-tile with a block of 128), entry i of the row at slot s is
+ * code * scale[s * 5 + i / 128]: five scales per 576-entry latent row, the fifth for the 64
+ * entries 512..575; entry i < 512 of V uses the scale of entry i of the row. */
 typedef struct sa_kv {
     int32_t heads_q;          /* query heads: 1..128 */
     int32_t heads_kv;         /* must be 1 */
     int32_t dim_qk;           /* 576 (latent, v == NULL, dim_v 512) or 128 (dim_v 128) */
     int32_t dim_v;            /* 512 or 128 */
-    sa_dtype dtype;           /* SA_BF16 or SA_FP8_E4M3 (E4M3 only with v == NULL) */
+    sa_dtype dtype;           /* SA_BF16, SA_FP8_E4M3 or SA_FP8_E4M3_T128 (E4M3 only with
+                                 v == NULL) */
     const void *k;            /* device [num_pages][page_size][dim_qk] */
     const void *v;            /* device [num_pages][page_size][dim_v], or NULL (latent) */
-    const float *scale;       /* device [num_pages][page_size] for E4M3, else NULL */
+    const float *scale;       /* device [num_pages][page_size] for E4M3, [num_pages][page_size][5]
+                                 for E4M3 with 128-entry tiles, else NULL */
     float softmax_scale;      /* logits are softmax_scale * (q . K) */
 } sa_kv;
 

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
-SA_BF16, SA_FP8_E4M3, SA_MXFP8 = 0, 1, 2
+SA_BF16, SA_FP8_E4M3, SA_MXFP8, SA_FP8_E4M3_T128 = 0, 1, 2, 3
 
 
 class SaError(RuntimeError):
@@ -133,7 +133,11 @@ def indexer_desc(heads, dim, keys, key_scale=None, pooled=None, key_mx_scale=Non
 
 
 def kv_desc(heads_q, dim_qk, dim_v, k, v=None, scale=None, softmax_scale=1.0, heads_kv=1):
-    dt = SA_FP8_E4M3 if scale is not None else SA_BF16
+    """E4M3 rows when ``scale`` is given: one scale per row ([pages, P]) or one per 128-entry
+    tile ([pages, P, heads_kv, tiles])."""
+    dt = SA_BF16
+    if scale is not None:
+        dt = SA_FP8_E4M3_T128 if scale.dim() == 4 else SA_FP8_E4M3
     return sa_kv(heads_q, heads_kv, dim_qk, dim_v, dt, k.data_ptr(),
                  v.data_ptr() if v is not None else None,
                  scale.data_ptr() if scale is not None else None, float(softmax_scale))

@@ -99,8 +99,9 @@ sa_status check_kv(const sa_kv *kv) {
     const bool latent = kv->dim_qk == 576 && kv->dim_v == 512 && kv->v == nullptr;
     const bool small = kv->dim_qk == 128 && kv->dim_v == 128;
     if (!latent && !small) return fail(SA_ERR_UNSUPPORTED, "(dim_qk, dim_v) must be (576, 512) latent or (128, 128)");
-    if (kv->dtype != SA_BF16 && kv->dtype != SA_FP8_E4M3) return fail(SA_ERR_INVALID, "unknown kv dtype");
-    if (kv->dtype == SA_FP8_E4M3 && (!latent || !kv->scale))
+    if (kv->dtype != SA_BF16 && kv->dtype != SA_FP8_E4M3 && kv->dtype != SA_FP8_E4M3_T128)
+        return fail(SA_ERR_INVALID, "unknown kv dtype");
+    if (kv->dtype != SA_BF16 && (!latent || !kv->scale))
         return fail(SA_ERR_UNSUPPORTED, "E4M3 KV needs latent rows (v == NULL) and a scale array");
     if (kv->dtype == SA_BF16 && kv->scale) return fail(SA_ERR_INVALID, "scale given for bf16 KV");
     if (!kv->k || !aligned16(kv->k) || (kv->v && !aligned16(kv->v)))
@@ -323,7 +324,7 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
     if (rows == 0) return SA_OK;
     hipError_t e = launch_sparse_attn(a, kv->dim_qk, kv->dim_v, kv->v != nullptr,
-                                      kv->dtype == SA_FP8_E4M3, st);
+                                      (int)kv->dtype, st);
     if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
     return SA_OK;
 }

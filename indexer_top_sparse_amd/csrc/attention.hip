@@ -9,6 +9,7 @@
 // once in LDS and used by every wave of the workgroup (see k_sparse_attn_pairs). Index sets
 // split over several workgroups publish normalised partials that k_attn_merge combines.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -50,9 +51,16 @@ struct AttnShape {
 // of the next tile overlaps nothing but is covered by a whole tile of loads.
 constexpr int kPairHeads = 64;
 
-template <int DQK, int DV, bool SEPV, bool FP8>
+// FP8 rows carry one scale per row, or with T128 one scale per 128-entry tile ([CANN] §3:
+// per-token-head-tile FP8 KV). Codes are widened to bf16 exactly either way; a row scale
+// multiplies the logits and P, tile scales multiply the per-tile partial dot products (QK) and
+// one copy of P per tile of d_v (PV).
+template <int DQK, int DV, bool SEPV, bool FP8, bool T128 = false>
 __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
     using S = AttnShape<DQK, DV, SEPV, FP8>;
+    constexpr bool ROWSC = FP8 && !T128;                 // one scale per row
+    constexpr int NSC = T128 ? (DQK + 127) / 128 : 1;    // scales per row
+    static_assert(!T128 || (FP8 && !SEPV && DV == 512), "tile scales: latent E4M3 rows");
     constexpr int NT = 512;
     constexpr int KH = DQK / 32 / 2;    // k-steps per wave (half of d)
     constexpr int DT = DV / 16 / 2;     // 16-wide d_v tiles per wave (half of d_v)
@@ -66,7 +74,8 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t stage[2][S::BUF];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // dynamic lds: [4 pairs][2 halves][2][64 lanes] f32x4 partial scores | [split_len] int32
-    // slots | [split_len] fp32 logit bias (0 or -inf) | [split_len] fp32 E4M3 scale (E4M3 only)
+    // slots | [split_len] fp32 logit bias (0 or -inf) | E4M3 scales (E4M3 only): [split_len]
+    // per row, or [NSC][split_len] per tile
     f32x4 *s_x = reinterpret_cast<f32x4 *>(lds);
     int32_t *s_slot = reinterpret_cast<int32_t *>(lds + 4 * 2 * 2 * 64 * 16);
     float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
@@ -99,7 +108,11 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
         }
         s_slot[j] = slot;
         s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
-        if (FP8) s_sig[j] = slot < 0 ? 0.f : a.kv_scale[slot];
+        if (ROWSC) s_sig[j] = slot < 0 ? 0.f : a.kv_scale[slot];
+        if (T128)
+#pragma unroll
+            for (int c = 0; c < NSC; ++c)
+                s_sig[c * a.split_len + j] = slot < 0 ? 0.f : a.kv_scale[(int64_t)slot * NSC + c];
     }
     // query fragments (B operand of S^T = K Q^T): head L of the pair, d = 32 s + 8 g + e for
     // this wave's half of the k-steps
@@ -177,15 +190,50 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
         load(t + 2);
         // ---- partial S^T over this wave's half of d: two 16-row M tiles
         f32x4 sa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (!T128) {
 #pragma unroll
-        for (int s = 0; s < KH; ++s)
+            for (int s = 0; s < KH; ++s)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int r = 16 * mt + L;
-                const u32x4 kf = *reinterpret_cast<const u32x4 *>(
-                    kb + r * S::ROWB_K + 16 * ((4 * (half * KH + s) + g) ^ swz(r)));
-                sa[mt] = mfma16x16x32(kf, qf[s], sa[mt]);
-            }
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int r = 16 * mt + L;
+                    const u32x4 kf = *reinterpret_cast<const u32x4 *>(
+                        kb + r * S::ROWB_K + 16 * ((4 * (half * KH + s) + g) ^ swz(r)));
+                    sa[mt] = mfma16x16x32(kf, qf[s], sa[mt]);
+                }
+        } else {
+            // one accumulator per 128-entry tile that this half of d touches (k-step s of the
+            // row covers d = 32 s .. 32 s + 31, so tile s / 4); the tile's scales of the lane's
+            // rows (16 mt + 4 g + i) multiply it before the halves are exchanged
+            auto qk_half = [&](auto hc) {
+                constexpr int H = decltype(hc)::value;
+                constexpr int T0 = (H * KH) / 4, NTL = (H * KH + KH - 1) / 4 - T0 + 1;
+                f32x4 acc[NTL][2];
+#pragma unroll
+                for (int tl = 0; tl < NTL; ++tl)
+                    acc[tl][0] = acc[tl][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KH; ++s)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const int r = 16 * mt + L;
+                        const u32x4 kf = *reinterpret_cast<const u32x4 *>(
+                            kb + r * S::ROWB_K + 16 * ((4 * (H * KH + s) + g) ^ swz(r)));
+                        const int tl = (H * KH + s) / 4 - T0;
+                        acc[tl][mt] = mfma16x16x32(kf, qf[s], acc[tl][mt]);
+                    }
+#pragma unroll
+                for (int tl = 0; tl < NTL; ++tl)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        const f32x4 sg = *reinterpret_cast<const f32x4 *>(
+                            s_sig + (T0 + tl) * a.split_len + t * kTile + 16 * mt + 4 * g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sa[mt][i] = fmaf(acc[tl][mt][i], sg[i], sa[mt][i]);
+                    }
+            };
+            if (half == 0) qk_half(std::integral_constant<int, 0>{});
+            else qk_half(std::integral_constant<int, 1>{});
+        }
         // ---- exchange halves with the partner wave (float addition commutes, so both waves
         //      obtain the same sums)
         f32x4 *xo = s_x + ((pair * 2 + half) * 2) * 64 + l;
@@ -199,15 +247,15 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
         const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bia);
         const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bia + 16);
         f32x4 sg0 = {1.f, 1.f, 1.f, 1.f}, sg1 = {1.f, 1.f, 1.f, 1.f};
-        if (FP8) {
+        if (ROWSC) {
             sg0 = *reinterpret_cast<const f32x4 *>(s_sig + t * kTile + 4 * g);
             sg1 = *reinterpret_cast<const f32x4 *>(s_sig + t * kTile + 4 * g + 16);
         }
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = fmaf(sum0[i], FP8 ? a.scale_log2 * sg0[i] : a.scale_log2, b0[i]);
-            x[4 + i] = fmaf(sum1[i], FP8 ? a.scale_log2 * sg1[i] : a.scale_log2, b1[i]);
+            x[i] = fmaf(sum0[i], ROWSC ? a.scale_log2 * sg0[i] : a.scale_log2, b0[i]);
+            x[4 + i] = fmaf(sum1[i], ROWSC ? a.scale_log2 * sg1[i] : a.scale_log2, b1[i]);
         }
         float m_tile = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                              fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -229,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
             p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
             l_run += p[e];
         }
-        if (FP8) {
+        if (ROWSC) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[i] *= sg0[i];
@@ -237,9 +285,22 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
             }
         }
         // P^T B operand: k = 8 g + e <-> the lane's own rows, in the order of the V reads below:
-        // e = 0..3 rows 4g, 4g+1, 16+4g, 16+4g+1; e = 4..7 the same plus 2
-        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[4], p[5]),
-                          pack_bf16x2(p[2], p[3]), pack_bf16x2(p[6], p[7])};
+        // e = 0..3 rows 4g, 4g+1, 16+4g, 16+4g+1; e = 4..7 the same plus 2. With tile scales,
+        // one operand per 128-entry tile of this wave's half of d_v, P scaled by that tile's
+        // scales of the lane's rows.
+        constexpr int NPB = T128 ? (DV / 2) / 128 : 1;
+        u32x4 pbs[NPB];
+#pragma unroll
+        for (int tt = 0; tt < NPB; ++tt) {
+            f32x4 s0 = {1.f, 1.f, 1.f, 1.f}, s1 = {1.f, 1.f, 1.f, 1.f};
+            if (T128) {
+                const float *sp = s_sig + (half * NPB + tt) * a.split_len + t * kTile + 4 * g;
+                s0 = *reinterpret_cast<const f32x4 *>(sp);
+                s1 = *reinterpret_cast<const f32x4 *>(sp + 16);
+            }
+            pbs[tt] = u32x4{pack_bf16x2(p[0] * s0[0], p[1] * s0[1]), pack_bf16x2(p[4] * s1[0], p[5] * s1[1]),
+                            pack_bf16x2(p[2] * s0[2], p[3] * s0[3]), pack_bf16x2(p[6] * s1[2], p[7] * s1[3])};
+        }
         // ---- O^T += V^T P^T over this wave's half of d_v. Transposing reads: input lane j of
         //      group g loads columns [4 (j % 4), +4) of row R(j / 4), with R(q) = 4 g + (q & 1)
         //      + 16 (q >> 1) (+ 2 for the second read); output lane L then holds column L of
@@ -258,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
                 (SA_LDS i16x4 *)(vbp + 16 * (c ^ sw2) + byte_in));
             const u32x2 w0 = __builtin_bit_cast(u32x2, t0);
             const u32x2 w1 = __builtin_bit_cast(u32x2, t1);
-            o[n] = mfma16x16x32(u32x4{w0[0], w0[1], w1[0], w1[1]}, pb, o[n]);
+            o[n] = mfma16x16x32(u32x4{w0[0], w0[1], w1[0], w1[1]}, pbs[(16 * n * NPB) / (DV / 2)], o[n]);
         }
         lds_barrier();  // tile t fully read; tile t + 1 stored
     }
@@ -348,10 +409,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         *reinterpret_cast<uint32_t *>(orow + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
 }
 
-template <int DQK, int DV, bool SEPV, bool FP8>
+template <int DQK, int DV, bool SEPV, bool FP8, bool T128 = false>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
-    const size_t lds = (size_t)4 * 2 * 2 * 64 * 16 + (size_t)a.split_len * (FP8 ? 12 : 8);
-    auto kern = k_sparse_attn_pairs<DQK, DV, SEPV, FP8>;
+    constexpr int NSC = T128 ? (DQK + 127) / 128 : (FP8 ? 1 : 0);  // scales per staged row
+    const size_t lds = (size_t)4 * 2 * 2 * 64 * 16 + (size_t)a.split_len * (8 + 4 * NSC);
+    auto kern = k_sparse_attn_pairs<DQK, DV, SEPV, FP8, T128>;
     // raise the kernel's dynamic-LDS limit only when a launch needs more than already granted
     static std::atomic<int> granted{-1};
     hipError_t e = hipSuccess;
@@ -370,11 +432,14 @@ static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, bool fp8,
+hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, int kv_fmt,
                               hipStream_t st) {
-    if (dqk == 576 && dv == 512 && !sep_v)
+    const bool fp8 = kv_fmt != 0;
+    if (dqk == 576 && dv == 512 && !sep_v) {
+        if (kv_fmt == 3) return launch_attn_t<576, 512, false, true, true>(a, st);
         return fp8 ? launch_attn_t<576, 512, false, true>(a, st)
                    : launch_attn_t<576, 512, false, false>(a, st);
+    }
     if (dqk == 128 && dv == 128 && !fp8)
         return sep_v ? launch_attn_t<128, 128, true, false>(a, st)
                      : launch_attn_t<128, 128, false, false>(a, st);

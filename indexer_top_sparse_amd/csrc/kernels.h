@@ -118,7 +118,8 @@ void *decode_select_kernel(int dim, int heads, int key_fmt, int mode);  // null:
 size_t decode_select_static_lds();
 size_t decode_select_dynamic_lds(int mode, int chunk, int lp);
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);
-hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, bool fp8,
+// kv_fmt: 0 bf16, 1 E4M3 with a row scale, 3 E4M3 with a scale per 128-entry tile (sa_dtype)
+hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, int kv_fmt,
                               hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 

@@ -157,6 +157,31 @@ def test_mx_full_size_sampled_rows():
     assert err <= 5e-2
 
 
+@pytest.mark.parametrize("spread", [0, 6])
+def test_fp8_tile_kv_attention_on_oracle_indices(spread):
+    """sa_sparse_attn over E4M3 latent rows with one scale per 128 entries, on the oracle's own
+    index sets. spread > 0 multiplies every (row, tile) scale by 2^U[-spread, spread], so that
+    neighbouring tiles of a row differ by up to 2^(2 spread): a wrong tile index or a scale
+    applied to the wrong partial sum moves the output by far more than the bound, which is
+    relative to the largest output (bf16 rounding of P and of the output)."""
+    wl = inputs.make("mxfp8ragged", num_seqs=3, ctx=[3000, 40, 2100])
+    if spread:
+        g = torch.Generator().manual_seed(17)
+        e = torch.randint(-spread, spread + 1, wl.kv_scale.shape, generator=g)
+        wl = dataclasses.replace(wl, kv_scale=(wl.kv_scale * torch.pow(2.0, e.float())).contiguous())
+    _say(f"E4M3 tile-128 KV attention, scale spread 2^+-{spread}")
+    dw = device.to_device(wl)
+    ref = oracle.decode_step(wl)
+    idx = torch.from_numpy(ref["idx"]).cuda()
+    ws = device.new_workspace(dw)
+    out = device.sparse_attn(dw, idx, ws).float().cpu().numpy()
+    want = oracle.sparse_attn(wl, ref["idx"])
+    err = np.abs(out - want).max()
+    bound = 1e-2 * np.abs(want).max()
+    _say(f"  max abs error {err:.3e} (bound {bound:.3e})")
+    assert err <= bound
+
+
 def test_mx_two_level_is_rejected():
     wl = inputs.make("mxfp8ragged", num_seqs=2, ctx=[3000, 4000])
     dw = device.to_device(wl)
