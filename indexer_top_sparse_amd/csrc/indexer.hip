@@ -725,19 +725,24 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             cr.cand(s, i, c0, a.lp, pos, r);
             return r < 0 ? 0 : r;
         };
-        // Every step issues the same loads: a step past the wave's last tile reloads that tile
-        // (an L2 hit), and loads whose value is not needed read a valid row and are discarded
-        // by the consumer. The number of loads issued after a tile's own is then the same on every
+        // Every step issues the same loads: a step past the wave's last tile reads row 0 of the
+        // key table (the same bytes for every such step of the launch, so L2 serves them),
+        // and loads whose value is not needed read a valid row and are discarded by the
+        // consumer. The number of loads issued after a tile's own is then the same on every
         // path, so the wait before each tile is exact and kPre tiles stay in flight; a load
         // behind a branch would make the compiler wait for every outstanding load instead.
         auto issue = [&](int slot, int k) {
+            // all-ones for a real tile, zero past the last one; opaque to the compiler, which
+            // would otherwise turn the masking into branches around the loads
+            int64_t keep = -(int64_t)(k < my_tiles);
+            asm volatile("" : "+v"(keep));
             k = min(k, my_tiles - 1);
             const int i0 = c0 + 16 * (w + k * kSelWaves);
             const int64_t base = contiguous ? tile_base_row(cr, i0, a.lp) : 0;
 #pragma unroll
             for (int x = 0; x < KT::NL; ++x) {
                 const int tr = KT::TPL * x + l / KT::CPR;
-                const int64_t row = contiguous ? base + tr : lrow(i0 + tr);
+                const int64_t row = (contiguous ? base + tr : lrow(i0 + tr)) & keep;
                 f[slot].v[x] = ldg16_stream(a.keys + row * KT::RB + 16 * (l % KT::CPR));
             }
             if (FP8) {
@@ -746,7 +751,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 int64_t r;
                 cr.cand(s, i < c1 ? i : c0, c0, a.lp, pos, r);
                 // a candidate without a row (a dropped block) reads row 0; its key is discarded
-                const int64_t rr = r >= 0 ? r : 0;
+                const int64_t rr = (r >= 0 ? r : 0) & keep;
                 if (MX) f[slot].mx = key_mx_scale<DIM>(a.key_mx, rr);
                 else f[slot].scale = a.key_scale[rr];
             }
