@@ -64,8 +64,10 @@ def load(real: str = "f64"):
     lib.ora_mx_quantize_bf16.argtypes = [P, i32, P, P]
     lib.ora_index_scores_mx.argtypes = [i32, P, P, i32, i32, P, P, P, P, P, i32, i32, i64, P]
     lib.ora_index_scores_mx.restype = C.c_int
+    lib.ora_cache_append.argtypes = [i32, P, P, P, i32, i32, P, i32, i32, P, P, P, P, P, i32,
+                                     i32, i32, i32, P, P, P, P, P]
     for fn in ("ora_index_scores", "ora_block_scores", "ora_topk", "ora_topk_in_blocks",
-               "ora_sparse_attn"):
+               "ora_sparse_attn", "ora_cache_append"):
         getattr(lib, fn).restype = C.c_int
     lib.real_dtype = rt
     _loaded[real] = lib
@@ -281,3 +283,36 @@ def decode_step(wl, rows=None, real: str = "f64"):
     res["idx"] = idx
     res["out"] = sparse_attn(wl, idx, rows_arr, real)
     return res
+
+
+def cache_append(wl, k_idx_new, kv_new, v_new=None, indexer=True, kv=True) -> dict:
+    """The cache writes of the step before the path: the new token rows (one per query row of
+    ``wl``, at the positions ``wl.q_pos()``) written into copies of the workload's caches.
+
+    k_idx_new: bf16 [rows, d_I]; kv_new: bf16 [rows, heads_kv, dim_qk]; v_new: bf16
+    [rows, heads_kv, dim_v] for separate V caches. Returns numpy copies of the caches after the
+    append: idx_keys, idx_scale, idx_mx_scale, pooled, k_cache, v_cache, kv_scale (None where
+    the workload has none)."""
+    lib = load()
+    rows, q_seq, q_pos = _rows(wl, None)
+    ctx = np.asarray(wl.ctx_lens, dtype=np.int32)
+    pt = _np(wl.page_table, np.int32)
+    cp = lambda t, dt=None: None if t is None else _np(t, dt).copy()
+    out = {
+        "idx_keys": cp(wl.idx_keys), "idx_scale": cp(wl.idx_scale, np.float32),
+        "idx_mx_scale": cp(wl.idx_mx_scale, np.uint8), "pooled": cp(wl.pooled),
+        "k_cache": cp(wl.k_cache), "v_cache": cp(wl.v_cache), "kv_scale": cp(wl.kv_scale, np.float32),
+    }
+    kin = _np(k_idx_new).copy() if indexer else None
+    kvin = _np(kv_new).copy() if kv else None
+    vin = _np(v_new).copy() if (kv and v_new is not None) else None
+    idx_fmt = {"bf16": 0, "fp8": 1, "mxfp8": 2}[wl.idx_dtype]
+    kv_fmt = _fmt(wl.kv_dtype)
+    rc = lib.ora_cache_append(
+        len(rows), _p(q_seq), _p(q_pos), _p(pt), wl.pages_per_seq, wl.page_size, _p(ctx),
+        wl.idx_dim if indexer else 0, idx_fmt, _p(kin), _p(out["idx_keys"]), _p(out["idx_scale"]),
+        _p(out["idx_mx_scale"]), _p(out["pooled"]), wl.heads_kv if kv else 0, wl.dim_qk,
+        wl.dim_v, kv_fmt, _p(kvin), _p(vin), _p(out["k_cache"]), _p(out["v_cache"]),
+        _p(out["kv_scale"]))
+    assert rc == 0, "oracle cache_append rejected its inputs"
+    return out

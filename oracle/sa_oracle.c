@@ -456,3 +456,113 @@ int ora_sparse_attn(int nq, const int32_t *q_seq, const int64_t *q_pos, int head
     }
     return bad;
 }
+
+/* ---------------------------------------------------------------- cache append */
+
+/* Quantize one row of n bf16 values to E4M3 with one fp32 scale (the per-row format):
+ * sigma = amax / 448 in fp32 (1 for an all-zero row), code = E4M3(x / sigma) with the quotient
+ * rounded to fp32 first (IEEE division), then to E4M3 (nearest, ties to even, saturating). */
+static float quantize_row_e4m3(const uint16_t *in, int n, uint8_t *codes) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; i++) {
+        float v = fabsf((float)ora_bf16(in[i]));
+        if (v > amax) amax = v;
+    }
+    float sigma = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int i = 0; i < n; i++) {
+        float y = (float)ora_bf16(in[i]) / sigma;
+        codes[i] = ora_e4m3_encode((double)y);
+    }
+    return sigma;
+}
+
+/* bf16 of a value computed in fp64: rounded to fp32 first, then to bf16 (both to nearest even),
+ * as the cache's block summaries are stored. */
+static uint16_t bf16_from_f64(double x) {
+    float f = (float)x;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)(u >> 16); /* inf / nan unchanged */
+    uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+/*
+ * Cache append: the step just before the path. Each new token row r of sequence row_seq[r] at
+ * position row_pos[r] is written into the paged caches at its slot (page table + offset):
+ *   - indexer key: bf16 copied (idx_fmt 0), E4M3 with a row scale (1, quantize_row_e4m3), or
+ *     MXFP8 (2, ora_mx_quantize_bf16) ([CANN] §3 for the FP8 formats);
+ *   - KV row(s): bf16 copied (kv_fmt 0), E4M3 with a row scale over the token's whole row
+ *     (1), or E4M3 with one scale per 128 entries of each head (2, [CANN] §3);
+ *   - the block summary of every block that received a token, when `pooled` is given (bf16
+ *     keys only): the mean of the block's valid keys (positions up to ctx_len - 1), summed in
+ *     fp64 in ascending position order, divided by the count, stored as bf16_from_f64 ([SameDay]
+ *     §3.1: coarse filtering reads summaries kept in the cache).
+ * Either part may be absent (idx_dim 0, or heads_kv 0). Caches are updated in place.
+ */
+int ora_cache_append(int nrows, const int32_t *row_seq, const int64_t *row_pos,
+                     const int32_t *page_table, int pages_per_seq, int page_size,
+                     const int32_t *ctx_lens, int idx_dim, int idx_fmt, const uint16_t *k_idx_new,
+                     void *idx_keys, float *idx_scale, uint8_t *idx_mx, uint16_t *pooled,
+                     int heads_kv, int dim_qk, int dim_v, int kv_fmt, const uint16_t *k_new,
+                     const uint16_t *v_new, void *k_cache, void *v_cache, float *kv_scale) {
+    for (int r = 0; r < nrows; r++) {
+        int b = row_seq[r];
+        int64_t pos = row_pos[r];
+        if (pos < 0 || pos >= ctx_lens[b]) return 1;
+        int64_t slot = slot_of(page_table, pages_per_seq, page_size, b, pos);
+        if (idx_dim > 0) {
+            const uint16_t *src = k_idx_new + (int64_t)r * idx_dim;
+            if (idx_fmt == 0) {
+                memcpy((uint16_t *)idx_keys + slot * idx_dim, src, 2 * (size_t)idx_dim);
+            } else if (idx_fmt == 1) {
+                idx_scale[slot] = quantize_row_e4m3(src, idx_dim, (uint8_t *)idx_keys + slot * idx_dim);
+            } else {
+                ora_mx_quantize_bf16(src, idx_dim, (uint8_t *)idx_keys + slot * idx_dim,
+                                     idx_mx + slot * (idx_dim / 32));
+            }
+        }
+        if (heads_kv > 0) {
+            int64_t kw = (int64_t)heads_kv * dim_qk;
+            const uint16_t *src = k_new + (int64_t)r * kw;
+            if (kv_fmt == 0) {
+                memcpy((uint16_t *)k_cache + slot * kw, src, 2 * (size_t)kw);
+                if (v_new) {
+                    int64_t vw = (int64_t)heads_kv * dim_v;
+                    memcpy((uint16_t *)v_cache + slot * vw, v_new + (int64_t)r * vw, 2 * (size_t)vw);
+                }
+            } else if (kv_fmt == 1) {
+                kv_scale[slot] = quantize_row_e4m3(src, (int)kw, (uint8_t *)k_cache + slot * kw);
+            } else {
+                int nt = (dim_qk + 127) / 128;
+                for (int g = 0; g < heads_kv; g++)
+                    for (int t = 0; t < nt; t++) {
+                        int n = dim_qk - 128 * t < 128 ? dim_qk - 128 * t : 128;
+                        kv_scale[(slot * heads_kv + g) * nt + t] = quantize_row_e4m3(
+                            src + (int64_t)g * dim_qk + 128 * t, n,
+                            (uint8_t *)k_cache + slot * kw + (int64_t)g * dim_qk + 128 * t);
+                    }
+            }
+        }
+    }
+    if (pooled && idx_dim > 0 && idx_fmt == 0) {
+        for (int r = 0; r < nrows; r++) {
+            int b = row_seq[r];
+            int64_t pos = row_pos[r];
+            int64_t blk = pos / page_size;
+            int64_t first = blk * page_size;
+            int64_t last = first + page_size - 1;
+            if (last > ctx_lens[b] - 1) last = ctx_lens[b] - 1;
+            int64_t phys = page_table[(int64_t)b * pages_per_seq + blk];
+            for (int d = 0; d < idx_dim; d++) {
+                double s = 0.0;
+                for (int64_t t = first; t <= last; t++) {
+                    int64_t sl = slot_of(page_table, pages_per_seq, page_size, b, t);
+                    s += (double)ora_bf16(((const uint16_t *)idx_keys)[sl * idx_dim + d]);
+                }
+                pooled[phys * idx_dim + d] = bf16_from_f64(s / (double)(last - first + 1));
+            }
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,145 @@
+"""Pins of the oracle's cache append (the writes of the step just before the path: the new
+token's indexer key and KV row, quantized into the cache's format, and the summary of the block
+that received it). Test infrastructure, CPU only.
+
+Expected caches are built independently of the oracle: slots from the page table in plain
+Python, quantized rows from the input generator's torch quantizers (torch's E4M3 type), and
+block summaries from the generator's own summary function over the whole updated key cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from indexer_top_sparse_amd import inputs
+
+
+def _new_rows(wl, seed):
+    g = torch.Generator().manual_seed(seed)
+    n = wl.num_queries
+    k_idx = (torch.randn((n, wl.idx_dim), generator=g) * 3).to(torch.bfloat16)
+    kv = torch.randn((n, wl.heads_kv, wl.dim_qk), generator=g).to(torch.bfloat16)
+    v = None
+    if wl.v_cache is not None:
+        v = torch.randn((n, wl.heads_kv, wl.dim_v), generator=g).to(torch.bfloat16)
+    return k_idx, kv, v
+
+
+def _slots(wl):
+    """(page, offset) of every query row's position, in plain Python."""
+    out = []
+    pos = wl.q_pos().tolist()
+    seq = wl.q_seq().tolist()
+    for b, p in zip(seq, pos):
+        out.append((int(wl.page_table[b, p // wl.page_size]), p % wl.page_size))
+    return out
+
+
+def _expected(wl, k_idx, kv, v):
+    exp = {}
+    slots = _slots(wl)
+    keys = wl.idx_keys.clone()
+    if wl.idx_dtype == "bf16":
+        for r, (pg, off) in enumerate(slots):
+            keys[pg, off] = k_idx[r]
+        exp["idx_keys"] = keys
+        if wl.pooled is not None:
+            exp["pooled"] = inputs._pooled_keys(keys, wl.page_table, wl.ctx_lens, wl.page_size)
+    elif wl.idx_dtype == "fp8":
+        codes, sc = inputs.quantize_rows_e4m3(k_idx.float())
+        scale = wl.idx_scale.clone()
+        for r, (pg, off) in enumerate(slots):
+            keys[pg, off] = codes[r]
+            scale[pg, off] = sc[r]
+        exp["idx_keys"], exp["idx_scale"] = keys, scale
+    else:
+        codes, e8 = inputs.quantize_rows_mxfp8(k_idx.float())
+        mx = wl.idx_mx_scale.clone()
+        for r, (pg, off) in enumerate(slots):
+            keys[pg, off] = codes[r]
+            mx[pg, off] = e8[r]
+        exp["idx_keys"], exp["idx_mx_scale"] = keys, mx
+    kc = wl.k_cache.clone()
+    if wl.kv_dtype == "bf16":
+        for r, (pg, off) in enumerate(slots):
+            kc[pg, off] = kv[r]
+        exp["k_cache"] = kc
+        if v is not None:
+            vc = wl.v_cache.clone()
+            for r, (pg, off) in enumerate(slots):
+                vc[pg, off] = v[r]
+            exp["v_cache"] = vc
+    elif wl.kv_dtype == "fp8":
+        codes, sc = inputs.quantize_rows_e4m3(kv.float().reshape(kv.shape[0], -1))
+        scale = wl.kv_scale.clone()
+        for r, (pg, off) in enumerate(slots):
+            kc[pg, off] = codes[r].reshape(kc.shape[2:])
+            scale[pg, off] = sc[r]
+        exp["k_cache"], exp["kv_scale"] = kc, scale
+    else:
+        codes, sc = inputs.quantize_tiles_e4m3(kv.float(), 128)
+        scale = wl.kv_scale.clone()
+        for r, (pg, off) in enumerate(slots):
+            kc[pg, off] = codes[r]
+            scale[pg, off] = sc[r]
+        exp["k_cache"], exp["kv_scale"] = kc, scale
+    return exp
+
+
+def _np_bits(t):
+    t = t.contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@pytest.mark.parametrize("preset,over", [
+    ("tiny", dict(num_seqs=3, ctx=[100, 64, 129])),                       # bf16, separate K/V
+    ("decode32k", dict(num_seqs=3, ctx=[65, 300, 1])),                     # bf16 latent rows
+    ("long1m", dict(num_seqs=2, ctx=[129, 4096], block_topk=4)),           # bf16 + summaries
+    ("fp8ragged", dict(num_seqs=3, ctx=[4096, 5000, 4200])),               # E4M3 row scales
+    ("mxfp8ragged", dict(num_seqs=2, ctx=[4100, 4500])),                   # MXFP8 + 128 tiles
+    ("long1m", dict(num_seqs=1, ctx=200, q_len=70, block_topk=4)),         # 70 rows, 3 blocks
+])
+def test_append_matches_the_generators_quantizers_and_summaries(preset, over):
+    wl = inputs.make(preset, **over)
+    k_idx, kv, v = _new_rows(wl, 5)
+    got = oracle.cache_append(wl, k_idx, kv, v)
+    exp = _expected(wl, k_idx, kv, v)
+    for name, t in exp.items():
+        np.testing.assert_array_equal(got[name], _np_bits(t), err_msg=name)
+    # nothing else moved
+    for name in ("idx_keys", "k_cache"):
+        if name not in exp:
+            np.testing.assert_array_equal(got[name], _np_bits(getattr(wl, name)))
+
+
+def test_first_token_of_a_block_is_its_own_summary():
+    """A token at a block's first position leaves that block with one valid key: the summary is
+    the key itself (the mean of one bf16 value is exact)."""
+    wl = inputs.make("long1m", num_seqs=2, ctx=[129, 65], block_topk=4)  # positions 128 and 64
+    k_idx, kv, v = _new_rows(wl, 9)
+    got = oracle.cache_append(wl, k_idx, kv, v)
+    for r, b in enumerate((0, 1)):
+        p = wl.ctx_lens[b] - 1
+        pg = int(wl.page_table[b, p // wl.page_size])
+        np.testing.assert_array_equal(got["pooled"][pg], _np_bits(k_idx[r]))
+
+
+def test_append_then_scores_see_the_new_key():
+    """After appending a key equal to a multiple of the query's first head, the score of the
+    new position is w0 * |q0|^2 * c when the other heads' queries are zero (R1's formula with
+    one active head)."""
+    wl = inputs.make("decode32k", num_seqs=1, ctx=[300])
+    q = torch.zeros_like(wl.q_idx, dtype=torch.float32)
+    q[0, 0, :4] = torch.tensor([1.0, -2.0, 0.5, 3.0])
+    wl.q_idx = q.to(torch.bfloat16)
+    wl.w = torch.zeros_like(wl.w)
+    wl.w[0, 0] = 0.25
+    k_idx = torch.zeros((1, wl.idx_dim))
+    k_idx[0, :4] = 2.0 * q[0, 0, :4]
+    _, kv, v = _new_rows(wl, 1)
+    got = oracle.cache_append(wl, k_idx.to(torch.bfloat16), kv, v)
+    wl.idx_keys = torch.from_numpy(got["idx_keys"]).view(torch.bfloat16)
+    s = oracle.index_scores(wl)[0]
+    assert s[299] == 0.25 * 2.0 * (1 + 4 + 0.25 + 9)
