@@ -498,7 +498,9 @@ static uint16_t bf16_from_f64(double x) {
  *     keys only): the mean of the block's valid keys (positions up to ctx_len - 1), summed in
  *     fp64 in ascending position order, divided by the count, stored as bf16_from_f64 ([SameDay]
  *     §3.1: coarse filtering reads summaries kept in the cache).
- * Either part may be absent (idx_dim 0, or heads_kv 0). Caches are updated in place.
+ * Either part may be absent (idx_dim 0, or heads_kv 0). A sequence of length 0 receives
+ * nothing (a decode batch has one row per sequence, empty ones included). Caches are updated in
+ * place.
  */
 int ora_cache_append(int nrows, const int32_t *row_seq, const int64_t *row_pos,
                      const int32_t *page_table, int pages_per_seq, int page_size,
@@ -509,6 +511,7 @@ int ora_cache_append(int nrows, const int32_t *row_seq, const int64_t *row_pos,
     for (int r = 0; r < nrows; r++) {
         int b = row_seq[r];
         int64_t pos = row_pos[r];
+        if (ctx_lens[b] == 0) continue; /* an empty sequence receives nothing */
         if (pos < 0 || pos >= ctx_lens[b]) return 1;
         int64_t slot = slot_of(page_table, pages_per_seq, page_size, b, pos);
         if (idx_dim > 0) {
@@ -549,6 +552,7 @@ int ora_cache_append(int nrows, const int32_t *row_seq, const int64_t *row_pos,
         for (int r = 0; r < nrows; r++) {
             int b = row_seq[r];
             int64_t pos = row_pos[r];
+            if (ctx_lens[b] == 0) continue;
             int64_t blk = pos / page_size;
             int64_t first = blk * page_size;
             int64_t last = first + page_size - 1;

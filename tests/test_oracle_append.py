@@ -26,12 +26,13 @@ def _new_rows(wl, seed):
 
 
 def _slots(wl):
-    """(page, offset) of every query row's position, in plain Python."""
+    """(row, page, offset) of every query row of a non-empty sequence, in plain Python."""
     out = []
     pos = wl.q_pos().tolist()
     seq = wl.q_seq().tolist()
-    for b, p in zip(seq, pos):
-        out.append((int(wl.page_table[b, p // wl.page_size]), p % wl.page_size))
+    for r, (b, p) in enumerate(zip(seq, pos)):
+        if wl.ctx_lens[b] > 0:  # an empty sequence receives nothing
+            out.append((r, int(wl.page_table[b, p // wl.page_size]), p % wl.page_size))
     return out
 
 
@@ -40,7 +41,7 @@ def _expected(wl, k_idx, kv, v):
     slots = _slots(wl)
     keys = wl.idx_keys.clone()
     if wl.idx_dtype == "bf16":
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             keys[pg, off] = k_idx[r]
         exp["idx_keys"] = keys
         if wl.pooled is not None:
@@ -48,38 +49,38 @@ def _expected(wl, k_idx, kv, v):
     elif wl.idx_dtype == "fp8":
         codes, sc = inputs.quantize_rows_e4m3(k_idx.float())
         scale = wl.idx_scale.clone()
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             keys[pg, off] = codes[r]
             scale[pg, off] = sc[r]
         exp["idx_keys"], exp["idx_scale"] = keys, scale
     else:
         codes, e8 = inputs.quantize_rows_mxfp8(k_idx.float())
         mx = wl.idx_mx_scale.clone()
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             keys[pg, off] = codes[r]
             mx[pg, off] = e8[r]
         exp["idx_keys"], exp["idx_mx_scale"] = keys, mx
     kc = wl.k_cache.clone()
     if wl.kv_dtype == "bf16":
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             kc[pg, off] = kv[r]
         exp["k_cache"] = kc
         if v is not None:
             vc = wl.v_cache.clone()
-            for r, (pg, off) in enumerate(slots):
+            for r, pg, off in slots:
                 vc[pg, off] = v[r]
             exp["v_cache"] = vc
     elif wl.kv_dtype == "fp8":
         codes, sc = inputs.quantize_rows_e4m3(kv.float().reshape(kv.shape[0], -1))
         scale = wl.kv_scale.clone()
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             kc[pg, off] = codes[r].reshape(kc.shape[2:])
             scale[pg, off] = sc[r]
         exp["k_cache"], exp["kv_scale"] = kc, scale
     else:
         codes, sc = inputs.quantize_tiles_e4m3(kv.float(), 128)
         scale = wl.kv_scale.clone()
-        for r, (pg, off) in enumerate(slots):
+        for r, pg, off in slots:
             kc[pg, off] = codes[r]
             scale[pg, off] = sc[r]
         exp["k_cache"], exp["kv_scale"] = kc, scale
@@ -95,7 +96,7 @@ def _np_bits(t):
 
 @pytest.mark.parametrize("preset,over", [
     ("tiny", dict(num_seqs=3, ctx=[100, 64, 129])),                       # bf16, separate K/V
-    ("decode32k", dict(num_seqs=3, ctx=[65, 300, 1])),                     # bf16 latent rows
+    ("decode32k", dict(num_seqs=4, ctx=[65, 300, 1, 0])),                  # bf16 latent rows
     ("long1m", dict(num_seqs=2, ctx=[129, 4096], block_topk=4)),           # bf16 + summaries
     ("fp8ragged", dict(num_seqs=3, ctx=[4096, 5000, 4200])),               # E4M3 row scales
     ("mxfp8ragged", dict(num_seqs=2, ctx=[4100, 4500])),                   # MXFP8 + 128 tiles
