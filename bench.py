@@ -305,6 +305,38 @@ def main():
     assert B.workspace_error(ws) == 0
     log(f"[bench] per launch: select {sel_avg * 1e3:.1f} us, attention {att_avg * 1e3:.1f} us")
 
+    # ---- the step before the path (reported beside it, not part of it): appending one new
+    #      token per sequence to the caches (after the timings above, since it changes them)
+    g = torch.Generator().manual_seed(7)
+    k_new = torch.randn((wl.num_seqs, wl.idx_dim), generator=g).to(torch.bfloat16).cuda()
+    kv_new = torch.randn((wl.num_seqs, wl.heads_kv, wl.dim_qk), generator=g).to(torch.bfloat16).cuda()
+    v_new = None
+    if wl.v_cache is not None:
+        v_new = torch.randn((wl.num_seqs, wl.heads_kv, wl.dim_v), generator=g).to(torch.bfloat16).cuda()
+    def app(i):
+        d = reps[i % len(reps)]
+        B.cache_append(d.batch, d.ix, d.kv, k_new, kv_new, v_new)
+
+    # a few microseconds of GPU work per call: K calls are captured in one HIP graph and replayed,
+    # so that the host's per-call cost does not hide the kernels' own time
+    app(0)
+    gph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gph, stream=side):
+            for i in range(args.steps):
+                app(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    gph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    app_avg = g0.elapsed_time(g1) / args.steps
+    log(f"[bench] cache append of {wl.num_seqs} tokens: {app_avg * 1e3:.1f} us (graph replay)")
+
     ab = algorithmic_bytes(wl)
     tokens_per_s = wl.num_seqs / (ms_step * 1e-3)
     step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
@@ -363,7 +395,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": ab[dominant],
                      "avg_launch_us": dom_ms * 1e3},
-        "kernels_us": {"select": sel_avg * 1e3, "attention": att_avg * 1e3},
+        "kernels_us": {"select": sel_avg * 1e3, "attention": att_avg * 1e3,
+                       "cache_append": app_avg * 1e3},
         "cpu_baseline": cpu,
         "source_hash": kernel_source_hash(),
     }

@@ -213,6 +213,34 @@ sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_k
                          int32_t block_k, int32_t *idx_out, void *out, void *workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * sa_cache_append -- the cache writes of the step just before the path: every new token's
+ * indexer key and KV row go into the paged caches at their slots, quantized into the caches'
+ * formats, and the summary of every block that received a token is recomputed ([SameDay] §3.1:
+ * coarse filtering reads block summaries the cache keeps; [CANN] §3: the FP8 formats).
+ * New tokens: with batch->q_indptr == NULL one per sequence, at position ctx_lens[b] - 1;
+ * otherwise rows q_indptr[b] .. q_indptr[b+1]-1 of sequence b, at positions ctx_lens[b] - n_b ..
+ * ctx_lens[b] - 1 (n_b its row count). The lengths already count the new tokens, and their pages
+ * must be mapped in the page table. Sequences of length 0 receive nothing.
+ *   k_idx_new device bf16 [rows][ix->dim], or NULL to leave the indexer cache unchanged (ix may
+ *             then be NULL)
+ *   kv_new    device bf16 [rows][kv->heads_kv][kv->dim_qk], or NULL to leave the KV cache
+ *             unchanged (kv may then be NULL)
+ *   v_new     device bf16 [rows][kv->heads_kv][kv->dim_v] exactly when kv->v is a separate cache
+ * Written through the descriptors' pointers: ix->keys, ix->key_scale / ix->key_mx_scale,
+ * ix->pooled (bf16 keys only), kv->k, kv->scale, kv->v.
+ *   E4M3 (row or 128-entry tile): sigma = group max |x| / 448 in fp32 (1 for all zeros), code =
+ *     E4M3(x / sigma), the quotient an IEEE fp32 division, rounded to nearest even, saturating.
+ *   MXFP8: as described for sa_indexer.
+ *   Block summary: mean of the block's keys at positions <= ctx_lens[b] - 1, summed in fp64 in
+ *     position order, divided by their count, rounded to fp32 and then to bf16.
+ * Errors: SA_ERR_INVALID for NULL or misaligned buffers, or lengths shorter than the new rows;
+ * SA_ERR_UNSUPPORTED for summaries over non-bf16 keys.
+ */
+sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                          const void *k_idx_new, const void *kv_new, const void *v_new,
+                          void *stream);
+
 /* Workspace bytes that every entry point above needs for this batch, cache shape, k and
  * block_k (kv may be NULL when only indexer/Top-K calls use the workspace). */
 size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int32_t block_k);

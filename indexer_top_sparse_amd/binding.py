@@ -46,7 +46,7 @@ class sa_kv(C.Structure):
 
 _lib = None
 EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-           "sa_decode_step", "sa_workspace_size",
+           "sa_decode_step", "sa_cache_append", "sa_workspace_size",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -67,6 +67,7 @@ def load(path: str = LIB_PATH):
     lib.sa_index_select.argtypes = [pb, pi, P, P, i32, i32, P, P, sz, P]
     lib.sa_block_select.argtypes = [pb, pi, P, P, i32, P, P, sz, P]
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
+    lib.sa_cache_append.argtypes = [pb, pi, pk, P, P, P, P]
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
     lib.sa_workspace_init.argtypes = [P, sz, P]
@@ -76,7 +77,7 @@ def load(path: str = LIB_PATH):
     lib.sa_last_error.restype = C.c_char_p
     lib.sa_version.restype = i32
     for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-               "sa_decode_step", "sa_workspace_init", "sa_workspace_error"):
+               "sa_decode_step", "sa_cache_append", "sa_workspace_init", "sa_workspace_error"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -206,3 +207,11 @@ def decode_step(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, ou
     _check(load().sa_decode_step(C.byref(batch.s), C.byref(ix), C.byref(kv), _ptr(q_idx),
                                  _ptr(w), _ptr(q), k, block_k, _ptr(idx_out), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def cache_append(batch: Batch, ix: sa_indexer | None, kv: sa_kv | None, k_idx_new=None,
+                 kv_new=None, v_new=None, stream=None) -> None:
+    """New token rows into the caches that ``ix`` and ``kv`` describe (see sa_cache_append)."""
+    _check(load().sa_cache_append(C.byref(batch.s), C.byref(ix) if ix is not None else None,
+                                  C.byref(kv) if kv is not None else None, _ptr(k_idx_new),
+                                  _ptr(kv_new), _ptr(v_new), _stream(stream)))

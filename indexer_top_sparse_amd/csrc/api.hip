@@ -529,4 +529,56 @@ sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_k
     return run_attn(batch, rp.rows, kv, q, idx, slots, k, out, wsb, L, hs);
 }
 
+sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                          const void *k_idx_new, const void *kv_new, const void *v_new,
+                          void *stream) {
+    RowPlan rp;
+    sa_status st = check_batch(batch, &rp);
+    if (st != SA_OK) return st;
+    AppendArgs a{};
+    a.num_seqs = batch->num_seqs;
+    a.lp = log2i(batch->page_size);
+    a.pages_per_seq = batch->pages_per_seq;
+    a.page_table = batch->page_table;
+    a.ctx_lens = batch->ctx_lens;
+    a.q_indptr = batch->q_indptr;
+    bool pool = false;
+    if (k_idx_new) {
+        if ((st = check_indexer(ix)) != SA_OK) return st;
+        if (!aligned16(k_idx_new)) return fail(SA_ERR_INVALID, "k_idx_new not 16-byte aligned");
+        if (ix->pooled && ix->key_dtype != SA_BF16)
+            return fail(SA_ERR_UNSUPPORTED, "block summaries are kept for bf16 indexer keys only");
+        a.idx_dim = ix->dim;
+        a.idx_fmt = (int)ix->key_dtype;  // 0 bf16, 1 E4M3 + row scale, 2 MXFP8
+        a.k_idx_new = static_cast<const uint16_t *>(k_idx_new);
+        a.idx_keys = static_cast<uint8_t *>(const_cast<void *>(ix->keys));
+        a.idx_scale = const_cast<float *>(ix->key_scale);
+        a.idx_mx = const_cast<uint8_t *>(ix->key_mx_scale);
+        a.pooled = static_cast<uint16_t *>(const_cast<void *>(ix->pooled));
+        pool = ix->pooled != nullptr;
+    }
+    if (kv_new) {
+        if ((st = check_kv(kv)) != SA_OK) return st;
+        if (!aligned16(kv_new) || (v_new && !aligned16(v_new)))
+            return fail(SA_ERR_INVALID, "kv_new / v_new not 16-byte aligned");
+        if ((v_new != nullptr) != (kv->v != nullptr))
+            return fail(SA_ERR_INVALID, "v_new must be given exactly for a separate V cache");
+        a.heads_kv = kv->heads_kv;
+        a.dim_qk = kv->dim_qk;
+        a.dim_v = kv->dim_v;
+        a.kv_fmt = kv->dtype == SA_BF16 ? 0 : (kv->dtype == SA_FP8_E4M3 ? 1 : 2);
+        a.kv_new = static_cast<const uint16_t *>(kv_new);
+        a.v_new = static_cast<const uint16_t *>(v_new);
+        a.kc = static_cast<uint8_t *>(const_cast<void *>(kv->k));
+        a.vc = static_cast<uint8_t *>(const_cast<void *>(kv->v));
+        a.kv_scale = const_cast<float *>(kv->scale);
+    } else if (v_new) {
+        return fail(SA_ERR_INVALID, "v_new without kv_new");
+    }
+    if (rp.rows == 0 || (!k_idx_new && !kv_new)) return SA_OK;
+    hipError_t e = launch_cache_append(a, rp.rows, pool, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "cache append launch");
+    return SA_OK;
+}
+
 }  // extern "C"

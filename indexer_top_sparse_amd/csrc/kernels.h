@@ -123,4 +123,21 @@ hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, in
                               hipStream_t st);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t st);
 
+// Cache append: new token rows (the last qlen positions of each sequence) into the caches.
+struct AppendArgs {
+    int num_seqs, lp, pages_per_seq;
+    const int32_t *page_table, *ctx_lens, *q_indptr;
+    int idx_dim, idx_fmt;           // idx_fmt: 0 bf16, 1 E4M3 + row scale, 2 MXFP8
+    const uint16_t *k_idx_new;      // bf16 [rows][idx_dim], or null
+    uint8_t *idx_keys;
+    float *idx_scale;
+    uint8_t *idx_mx;
+    uint16_t *pooled;               // bf16 [pages][idx_dim], or null
+    int heads_kv, dim_qk, dim_v, kv_fmt;  // kv_fmt: 0 bf16, 1 E4M3 + row scale, 2 + tile scales
+    const uint16_t *kv_new, *v_new;  // bf16 [rows][heads_kv][dim_qk] / [dim_v], or null
+    uint8_t *kc, *vc;
+    float *kv_scale;
+};
+hipError_t launch_cache_append(const AppendArgs &a, int rows, bool pool, hipStream_t st);
+
 }  // namespace sa

@@ -235,8 +235,9 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
     else:
         ctx_lens = [int(p["ctx"])] * B
 
-    q_len = p["q_len"]
-    q_lens = [min(q_len, n) if n > 0 else 0 for n in ctx_lens]
+    q_len = p["q_len"]  # query rows per sequence: one count for all, or one per sequence
+    ql = list(q_len) if isinstance(q_len, (list, tuple)) else [q_len] * B
+    q_lens = [min(q, n) if n > 0 else 0 for q, n in zip(ql, ctx_lens)]
     if q_len == 1:
         q_lens = [1] * B  # decode: one query row per sequence even when empty
     nq = sum(q_lens)

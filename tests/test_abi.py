@@ -133,3 +133,29 @@ def test_sparse_attn_needs_a_large_enough_workspace(lib):
                             P(idx.data_ptr()), 2048, P(a.kvc.data_ptr()), P(base + 16), need,
                             None)
     assert st == B.SA_ERR_WORKSPACE  # not 256-byte aligned
+
+
+def test_cache_append_validation(lib):
+    a = _FakeDev()
+    P = C.c_void_p
+    new = torch.zeros((2, 576), dtype=torch.bfloat16)
+
+    def app(ix=None, kv=None, k_idx=None, kv_new=None, v_new=None, batch=None):
+        return lib.sa_cache_append(batch or C.byref(a.batch.s), ix, kv, k_idx, kv_new, v_new, None)
+
+    # V rows for a latent cache (no separate V)
+    assert app(kv=C.byref(a.kv), kv_new=P(new.data_ptr()), v_new=P(new.data_ptr())) == B.SA_ERR_INVALID
+    # V rows without KV rows
+    assert app(v_new=P(new.data_ptr())) == B.SA_ERR_INVALID
+    # misaligned new rows
+    assert app(kv=C.byref(a.kv), kv_new=P(new.data_ptr() + 2)) == B.SA_ERR_INVALID
+    # indexer rows without a descriptor
+    assert app(k_idx=P(new.data_ptr())) == B.SA_ERR_INVALID
+    # block summaries are defined over bf16 keys only
+    codes = torch.zeros((8, 64, 128), dtype=torch.uint8)
+    scale = torch.ones((8, 64), dtype=torch.float32)
+    pooled = torch.zeros((8, 128), dtype=torch.bfloat16)
+    ix = B.indexer_desc(64, 128, codes, scale, pooled)
+    assert app(ix=C.byref(ix), k_idx=P(new.data_ptr())) == B.SA_ERR_UNSUPPORTED
+    # nothing to write is not an error
+    assert app() == B.SA_OK
