@@ -306,3 +306,32 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
         v_cache=v_cache, kv_scale=kv_scale, softmax_scale=float(scale),
         seeds={"config_id": config_id, "seed_offset": off}, idx_mx_scale=idx_mx_scale,
     )
+
+
+# ---------------------------------------------------------------------------- indexer prolog
+
+@dataclass
+class PrologInputs:
+    """Synthetic inputs of the indexer prolog (no trained weights): per new token a query
+    latent x_q and a hidden state x; projection weights [out_features, in_features]."""
+    x_q: torch.Tensor    # bf16 [rows, d_q]
+    x: torch.Tensor      # bf16 [rows, d_model]
+    w_q: torch.Tensor    # bf16 [H_I * d_I, d_q]
+    w_k: torch.Tensor    # bf16 [d_I, d_model]
+    w_w: torch.Tensor    # bf16 [H_I, d_model]
+    gamma: torch.Tensor  # fp32 [d_I]
+    beta: torch.Tensor   # fp32 [d_I]
+
+
+def make_prolog(rows: int, heads: int, dim: int, d_q: int = 1536, d_model: int = 7168,
+                seed: int = 0) -> PrologInputs:
+    """Seeded prolog inputs: activations N(0,1); weights N(0,1)/sqrt(fan_in); LayerNorm weight
+    1 + N(0, 0.1^2) and bias N(0, 0.1^2). All bf16 except the LayerNorm parameters."""
+    g = lambda i: _gen(9, i, seed)
+    bf = lambda shape, i, s=1.0: (torch.randn(shape, generator=g(i)) * s).to(torch.bfloat16)
+    return PrologInputs(
+        x_q=bf((rows, d_q), 1), x=bf((rows, d_model), 2),
+        w_q=bf((heads * dim, d_q), 3, d_q ** -0.5), w_k=bf((dim, d_model), 4, d_model ** -0.5),
+        w_w=bf((heads, d_model), 5, d_model ** -0.5),
+        gamma=1.0 + 0.1 * torch.randn(dim, generator=g(6)),
+        beta=0.1 * torch.randn(dim, generator=g(7)))

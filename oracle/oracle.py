@@ -316,3 +316,28 @@ def cache_append(wl, k_idx_new, kv_new, v_new=None, indexer=True, kv=True) -> di
         _p(out["kv_scale"]))
     assert rc == 0, "oracle cache_append rejected its inputs"
     return out
+
+
+# ---------------------------------------------------------------------------- indexer prolog
+
+LN_EPS = 1e-6
+
+
+def indexer_prolog(x_q, x, w_q, w_k, w_w, gamma, beta, eps: float = LN_EPS):
+    """The indexer prolog ([CANN] §2.2: Q projection, K normalization, head-weight projection),
+    in fp64 from the given (bf16) inputs, with the plain definitions:
+        q_I = x_q W_q^T      (row r, head h: entries h*d_I .. h*d_I + d_I - 1)
+        k_I = LayerNorm(x W_k^T) * gamma + beta   (mean and biased variance over d_I, eps)
+        w   = x W_w^T
+    Weights are [out_features, in_features]. Returns (q_I [rows, H_I*d_I], k_I [rows, d_I],
+    w [rows, H_I]) as float64 numpy arrays. (Q quantization, the pages' fourth prolog operation,
+    happens inside the MXFP8 indexer.)"""
+    f = lambda t: np.asarray(t.float().numpy() if hasattr(t, "float") else t, dtype=np.float64)
+    xq, xx = f(x_q), f(x)
+    q = xq @ f(w_q).T
+    y = xx @ f(w_k).T
+    mu = y.mean(axis=1, keepdims=True)
+    var = ((y - mu) ** 2).mean(axis=1, keepdims=True)
+    k = (y - mu) / np.sqrt(var + eps) * f(gamma)[None, :] + f(beta)[None, :]
+    w = xx @ f(w_w).T
+    return q, k, w
