@@ -337,6 +337,34 @@ def main():
     app_avg = g0.elapsed_time(g1) / args.steps
     log(f"[bench] cache append of {wl.num_seqs} tokens: {app_avg * 1e3:.1f} us (graph replay)")
 
+    # ---- the indexer prolog of the same tokens (synthetic weights; query input 1536 wide,
+    #      hidden 7168 wide), timed the same way
+    pi = inputs.make_prolog(wl.num_seqs, wl.idx_heads, wl.idx_dim)
+    pt = {k: getattr(pi, k).cuda().contiguous() for k in ("x_q", "x", "w_q", "w_k", "w_w", "gamma", "beta")}
+    pdesc = B.prolog_desc(wl.idx_heads, wl.idx_dim, pt["w_q"], pt["w_k"], pt["w_w"], pt["gamma"],
+                          pt["beta"])
+    q_o = torch.empty((wl.num_seqs, wl.idx_heads, wl.idx_dim), dtype=torch.bfloat16, device="cuda")
+    k_o = torch.empty((wl.num_seqs, wl.idx_dim), dtype=torch.bfloat16, device="cuda")
+    w_o = torch.empty((wl.num_seqs, wl.idx_heads), dtype=torch.float32, device="cuda")
+    pws = torch.empty(wl.num_seqs * wl.idx_dim * 4, dtype=torch.uint8, device="cuda")
+    B.indexer_prolog(pdesc, pt["x_q"], pt["x"], q_o, k_o, w_o, pws)
+    gp = torch.cuda.CUDAGraph()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gp, stream=side):
+            for i in range(args.steps):
+                B.indexer_prolog(pdesc, pt["x_q"], pt["x"], q_o, k_o, w_o, pws)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    gp.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    pro_avg = g0.elapsed_time(g1) / args.steps
+    pro_bytes = 2 * (pi.w_q.numel() + pi.w_k.numel() + pi.w_w.numel() + pi.x_q.numel() + pi.x.numel())
+    log(f"[bench] indexer prolog of {wl.num_seqs} tokens: {pro_avg * 1e3:.1f} us "
+        f"({pro_bytes / (pro_avg * 1e-3) / 1e9:.0f} GB/s of weights and inputs)")
+
     ab = algorithmic_bytes(wl)
     tokens_per_s = wl.num_seqs / (ms_step * 1e-3)
     step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
@@ -396,7 +424,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": ab[dominant],
                      "avg_launch_us": dom_ms * 1e3},
         "kernels_us": {"select": sel_avg * 1e3, "attention": att_avg * 1e3,
-                       "cache_append": app_avg * 1e3},
+                       "cache_append": app_avg * 1e3, "indexer_prolog": pro_avg * 1e3},
         "cpu_baseline": cpu,
         "source_hash": kernel_source_hash(),
     }

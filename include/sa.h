@@ -241,6 +241,42 @@ sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_
                           const void *k_idx_new, const void *kv_new, const void *v_new,
                           void *stream);
 
+/* Weights of the indexer prolog (synthetic in this library's workloads; no trained weights are
+ * involved). Weights are [out_features][in_features], row-major bf16. */
+typedef struct sa_prolog {
+    int32_t heads;           /* H_I: 1..64 */
+    int32_t dim;             /* d_I: 64 or 128 */
+    int32_t d_q;             /* width of the query input: a positive multiple of 128 */
+    int32_t d_model;         /* width of the hidden input: a positive multiple of 128 */
+    const void *w_q;         /* device bf16 [heads * dim][d_q] */
+    const void *w_k;         /* device bf16 [dim][d_model] */
+    const void *w_w;         /* device bf16 [heads][d_model] */
+    const float *ln_gamma;   /* device fp32 [dim] */
+    const float *ln_beta;    /* device fp32 [dim] */
+    float ln_eps;            /* > 0 */
+} sa_prolog;
+
+/*
+ * sa_indexer_prolog -- the input preparation of the indexer for `rows` new tokens ([CANN]
+ * §2.2: Q projection and K normalization, Q quantization and the head-weight projection, as
+ * independent work ahead of the indexer):
+ *     q_I[r][h][:] = x_q[r] . W_q[h*dim .. h*dim + dim - 1]^T        (bf16 out, fp32 sums)
+ *     k_I[r]       = LayerNorm(x[r] . W_k^T) * gamma + beta           (bf16 out)
+ *     w[r][h]      = x[r] . W_w[h]^T                                   (fp32 out)
+ * LayerNorm: mean and biased variance over the dim entries, (y - mean) / sqrt(var + eps).
+ * q_I and w feed the indexer (an MXFP8 indexer quantizes q_I itself), k_I is the new token's
+ * indexer key for sa_cache_append. The three projections run in one launch, the LayerNorm in a
+ * second one, on `stream`.
+ *   x_q device bf16 [rows][d_q];  x device bf16 [rows][d_model]
+ *   q_out device bf16 [rows][heads][dim];  k_out device bf16 [rows][dim];  w_out fp32 [rows][heads]
+ *   workspace: device, >= rows * dim * 4 bytes, 16-byte aligned (the pre-norm key)
+ * Errors: SA_ERR_INVALID for NULL or misaligned pointers, rows < 1 or a small workspace;
+ * SA_ERR_UNSUPPORTED for other shapes.
+ */
+sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, const void *x,
+                            void *q_out, void *k_out, float *w_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Workspace bytes that every entry point above needs for this batch, cache shape, k and
  * block_k (kv may be NULL when only indexer/Top-K calls use the workspace). */
 size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int32_t block_k);

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "append.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "attention.hip", "append.hip", "prolog.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-function", "-Wno-unused-variable",

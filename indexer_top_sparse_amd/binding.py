@@ -38,6 +38,13 @@ class sa_indexer(C.Structure):
                 ("key_mx_scale", C.c_void_p)]
 
 
+class sa_prolog(C.Structure):
+    _fields_ = [("heads", C.c_int32), ("dim", C.c_int32), ("d_q", C.c_int32),
+                ("d_model", C.c_int32), ("w_q", C.c_void_p), ("w_k", C.c_void_p),
+                ("w_w", C.c_void_p), ("ln_gamma", C.c_void_p), ("ln_beta", C.c_void_p),
+                ("ln_eps", C.c_float)]
+
+
 class sa_kv(C.Structure):
     _fields_ = [("heads_q", C.c_int32), ("heads_kv", C.c_int32), ("dim_qk", C.c_int32),
                 ("dim_v", C.c_int32), ("dtype", C.c_int), ("k", C.c_void_p), ("v", C.c_void_p),
@@ -46,7 +53,7 @@ class sa_kv(C.Structure):
 
 _lib = None
 EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-           "sa_decode_step", "sa_cache_append", "sa_workspace_size",
+           "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_workspace_size",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -68,6 +75,7 @@ def load(path: str = LIB_PATH):
     lib.sa_block_select.argtypes = [pb, pi, P, P, i32, P, P, sz, P]
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
     lib.sa_cache_append.argtypes = [pb, pi, pk, P, P, P, P]
+    lib.sa_indexer_prolog.argtypes = [C.POINTER(sa_prolog), i32, P, P, P, P, P, P, sz, P]
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
     lib.sa_workspace_init.argtypes = [P, sz, P]
@@ -77,7 +85,8 @@ def load(path: str = LIB_PATH):
     lib.sa_last_error.restype = C.c_char_p
     lib.sa_version.restype = i32
     for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-               "sa_decode_step", "sa_cache_append", "sa_workspace_init", "sa_workspace_error"):
+               "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_workspace_init",
+               "sa_workspace_error"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
     return lib
@@ -215,3 +224,15 @@ def cache_append(batch: Batch, ix: sa_indexer | None, kv: sa_kv | None, k_idx_ne
     _check(load().sa_cache_append(C.byref(batch.s), C.byref(ix) if ix is not None else None,
                                   C.byref(kv) if kv is not None else None, _ptr(k_idx_new),
                                   _ptr(kv_new), _ptr(v_new), _stream(stream)))
+
+
+def prolog_desc(heads, dim, w_q, w_k, w_w, gamma, beta, eps=1e-6) -> sa_prolog:
+    return sa_prolog(heads, dim, w_q.shape[1], w_k.shape[1], w_q.data_ptr(), w_k.data_ptr(),
+                     w_w.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps))
+
+
+def indexer_prolog(p: sa_prolog, x_q, x, q_out, k_out, w_out, ws, stream=None) -> None:
+    """q_I, k_I and w of x_q.shape[0] new tokens (see sa_indexer_prolog)."""
+    _check(load().sa_indexer_prolog(C.byref(p), x_q.shape[0], _ptr(x_q), _ptr(x), _ptr(q_out),
+                                    _ptr(k_out), _ptr(w_out), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)))

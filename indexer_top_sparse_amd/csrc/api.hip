@@ -581,4 +581,42 @@ sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_
     return SA_OK;
 }
 
+sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, const void *x,
+                            void *q_out, void *k_out, float *w_out, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    if (!p) return fail(SA_ERR_INVALID, "prolog descriptor is NULL");
+    if (rows < 1) return fail(SA_ERR_INVALID, "rows must be >= 1");
+    if (p->heads < 1 || p->heads > 64) return fail(SA_ERR_UNSUPPORTED, "prolog heads must be 1..64");
+    if (p->dim != 64 && p->dim != 128) return fail(SA_ERR_UNSUPPORTED, "prolog dim must be 64 or 128");
+    if (p->d_q < 128 || p->d_q % 128 || p->d_model < 128 || p->d_model % 128)
+        return fail(SA_ERR_UNSUPPORTED, "d_q and d_model must be positive multiples of 128");
+    if (!(p->ln_eps > 0.f)) return fail(SA_ERR_INVALID, "ln_eps must be > 0");
+    const void *ptrs[] = {p->w_q, p->w_k, p->w_w, x_q, x, q_out, k_out, workspace};
+    for (const void *q : ptrs)
+        if (!q || !aligned16(q)) return fail(SA_ERR_INVALID, "prolog buffers must be non-NULL and 16-byte aligned");
+    if (!p->ln_gamma || !p->ln_beta || !w_out) return fail(SA_ERR_INVALID, "ln_gamma, ln_beta and w_out are required");
+    if (workspace_bytes < (size_t)rows * p->dim * 4) return fail(SA_ERR_WORKSPACE, "prolog workspace smaller than rows * dim * 4 bytes");
+    PrologArgs a;
+    a.rows = rows;
+    a.heads = p->heads;
+    a.dim = p->dim;
+    a.d_q = p->d_q;
+    a.d_model = p->d_model;
+    a.x_q = static_cast<const uint16_t *>(x_q);
+    a.x = static_cast<const uint16_t *>(x);
+    a.w_q = static_cast<const uint16_t *>(p->w_q);
+    a.w_k = static_cast<const uint16_t *>(p->w_k);
+    a.w_w = static_cast<const uint16_t *>(p->w_w);
+    a.gamma = p->ln_gamma;
+    a.beta = p->ln_beta;
+    a.eps = p->ln_eps;
+    a.q_out = static_cast<uint16_t *>(q_out);
+    a.w_out = w_out;
+    a.k_out = static_cast<uint16_t *>(k_out);
+    a.k_pre = static_cast<float *>(workspace);
+    hipError_t e = launch_prolog(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "prolog launch");
+    return SA_OK;
+}
+
 }  // extern "C"

@@ -140,4 +140,19 @@ struct AppendArgs {
 };
 hipError_t launch_cache_append(const AppendArgs &a, int rows, bool pool, hipStream_t st);
 
+// Indexer prolog: query / key / head-weight projections of new token rows, then the key's
+// LayerNorm.
+struct PrologArgs {
+    int rows, heads, dim, d_q, d_model;
+    const uint16_t *x_q, *x;         // bf16 [rows][d_q], [rows][d_model]
+    const uint16_t *w_q, *w_k, *w_w;  // bf16 [heads*dim][d_q], [dim][d_model], [heads][d_model]
+    const float *gamma, *beta;       // fp32 [dim]
+    float eps;
+    uint16_t *q_out;                 // bf16 [rows][heads][dim]
+    float *w_out;                    // fp32 [rows][heads]
+    uint16_t *k_out;                 // bf16 [rows][dim]
+    float *k_pre;                    // fp32 [rows][dim] scratch (pre-norm key)
+};
+hipError_t launch_prolog(const PrologArgs &a, hipStream_t st);
+
 }  // namespace sa

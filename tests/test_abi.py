@@ -159,3 +159,21 @@ def test_cache_append_validation(lib):
     assert app(ix=C.byref(ix), k_idx=P(new.data_ptr())) == B.SA_ERR_UNSUPPORTED
     # nothing to write is not an error
     assert app() == B.SA_OK
+
+
+def test_prolog_validation(lib):
+    z = torch.zeros(4096, dtype=torch.float32)
+    P = C.c_void_p(z.data_ptr())
+
+    def prolog(heads=4, dim=64, d_q=128, d_model=128, eps=1e-6, rows=2, ws=4096 * 4, x=P):
+        p = B.sa_prolog(heads, dim, d_q, d_model, z.data_ptr(), z.data_ptr(), z.data_ptr(),
+                        z.data_ptr(), z.data_ptr(), eps)
+        return lib.sa_indexer_prolog(C.byref(p), rows, x, P, P, P, P, P, ws, None)
+
+    assert prolog(dim=96) == B.SA_ERR_UNSUPPORTED
+    assert prolog(d_q=100) == B.SA_ERR_UNSUPPORTED
+    assert prolog(heads=65) == B.SA_ERR_UNSUPPORTED
+    assert prolog(rows=0) == B.SA_ERR_INVALID
+    assert prolog(eps=0.0) == B.SA_ERR_INVALID
+    assert prolog(x=None) == B.SA_ERR_INVALID
+    assert prolog(ws=100) == B.SA_ERR_WORKSPACE
