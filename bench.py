@@ -346,7 +346,7 @@ def main():
     q_o = torch.empty((wl.num_seqs, wl.idx_heads, wl.idx_dim), dtype=torch.bfloat16, device="cuda")
     k_o = torch.empty((wl.num_seqs, wl.idx_dim), dtype=torch.bfloat16, device="cuda")
     w_o = torch.empty((wl.num_seqs, wl.idx_heads), dtype=torch.float32, device="cuda")
-    pws = torch.empty(wl.num_seqs * wl.idx_dim * 4, dtype=torch.uint8, device="cuda")
+    pws = B.prolog_workspace(pdesc, wl.num_seqs)
     B.indexer_prolog(pdesc, pt["x_q"], pt["x"], q_o, k_o, w_o, pws)
     gp = torch.cuda.CUDAGraph()
     side.wait_stream(stream)

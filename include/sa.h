@@ -269,13 +269,18 @@ typedef struct sa_prolog {
  * second one, on `stream`.
  *   x_q device bf16 [rows][d_q];  x device bf16 [rows][d_model]
  *   q_out device bf16 [rows][heads][dim];  k_out device bf16 [rows][dim];  w_out fp32 [rows][heads]
- *   workspace: device, >= rows * dim * 4 bytes, 16-byte aligned (the pre-norm key)
+ *   workspace: device, >= sa_prolog_workspace_size(p, rows) bytes, 16-byte aligned (partial
+ *              sums of the key and head-weight projections)
  * Errors: SA_ERR_INVALID for NULL or misaligned pointers, rows < 1 or a small workspace;
  * SA_ERR_UNSUPPORTED for other shapes.
  */
 sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, const void *x,
                             void *q_out, void *k_out, float *w_out, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of sa_indexer_prolog for `rows` tokens (0 for an invalid descriptor):
+ * 4 * rows * (dim + heads) * (d_model / s), s = 512, 256 or 128, the largest dividing d_model. */
+size_t sa_prolog_workspace_size(const sa_prolog *p, int32_t rows);
 
 /* Workspace bytes that every entry point above needs for this batch, cache shape, k and
  * block_k (kv may be NULL when only indexer/Top-K calls use the workspace). */

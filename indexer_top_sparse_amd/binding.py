@@ -53,7 +53,8 @@ class sa_kv(C.Structure):
 
 _lib = None
 EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-           "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_workspace_size",
+           "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_prolog_workspace_size",
+           "sa_workspace_size",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
     lib.sa_cache_append.argtypes = [pb, pi, pk, P, P, P, P]
     lib.sa_indexer_prolog.argtypes = [C.POINTER(sa_prolog), i32, P, P, P, P, P, P, sz, P]
+    lib.sa_prolog_workspace_size.argtypes = [C.POINTER(sa_prolog), i32]
+    lib.sa_prolog_workspace_size.restype = sz
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
     lib.sa_workspace_init.argtypes = [P, sz, P]
@@ -229,6 +232,13 @@ def cache_append(batch: Batch, ix: sa_indexer | None, kv: sa_kv | None, k_idx_ne
 def prolog_desc(heads, dim, w_q, w_k, w_w, gamma, beta, eps=1e-6) -> sa_prolog:
     return sa_prolog(heads, dim, w_q.shape[1], w_k.shape[1], w_q.data_ptr(), w_k.data_ptr(),
                      w_w.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps))
+
+
+def prolog_workspace(p: sa_prolog, rows: int, device="cuda") -> torch.Tensor:
+    n = load().sa_prolog_workspace_size(C.byref(p), rows)
+    if n == 0:
+        _check(SA_ERR_INVALID)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def indexer_prolog(p: sa_prolog, x_q, x, q_out, k_out, w_out, ws, stream=None) -> None:

@@ -581,6 +581,11 @@ sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_
     return SA_OK;
 }
 
+size_t sa_prolog_workspace_size(const sa_prolog *p, int32_t rows) {
+    if (!p || rows < 1 || p->d_model < 128 || p->d_model % 128 || p->heads < 1 || p->dim < 1) return 0;
+    return prolog_workspace_bytes(rows, p->dim, p->heads, p->d_model);
+}
+
 sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, const void *x,
                             void *q_out, void *k_out, float *w_out, void *workspace,
                             size_t workspace_bytes, void *stream) {
@@ -595,7 +600,8 @@ sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, c
     for (const void *q : ptrs)
         if (!q || !aligned16(q)) return fail(SA_ERR_INVALID, "prolog buffers must be non-NULL and 16-byte aligned");
     if (!p->ln_gamma || !p->ln_beta || !w_out) return fail(SA_ERR_INVALID, "ln_gamma, ln_beta and w_out are required");
-    if (workspace_bytes < (size_t)rows * p->dim * 4) return fail(SA_ERR_WORKSPACE, "prolog workspace smaller than rows * dim * 4 bytes");
+    if (workspace_bytes < prolog_workspace_bytes(rows, p->dim, p->heads, p->d_model))
+        return fail(SA_ERR_WORKSPACE, "prolog workspace smaller than sa_prolog_workspace_size");
     PrologArgs a;
     a.rows = rows;
     a.heads = p->heads;
@@ -613,7 +619,7 @@ sa_status sa_indexer_prolog(const sa_prolog *p, int32_t rows, const void *x_q, c
     a.q_out = static_cast<uint16_t *>(q_out);
     a.w_out = w_out;
     a.k_out = static_cast<uint16_t *>(k_out);
-    a.k_pre = static_cast<float *>(workspace);
+    a.part = static_cast<float *>(workspace);
     hipError_t e = launch_prolog(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "prolog launch");
     return SA_OK;

@@ -151,8 +151,9 @@ struct PrologArgs {
     uint16_t *q_out;                 // bf16 [rows][heads][dim]
     float *w_out;                    // fp32 [rows][heads]
     uint16_t *k_out;                 // bf16 [rows][dim]
-    float *k_pre;                    // fp32 [rows][dim] scratch (pre-norm key)
+    float *part;                     // fp32 [slices][rows][dim + heads] partial sums (workspace)
 };
 hipError_t launch_prolog(const PrologArgs &a, hipStream_t st);
+size_t prolog_workspace_bytes(int rows, int dim, int heads, int d_model);
 
 }  // namespace sa

@@ -177,3 +177,5 @@ def test_prolog_validation(lib):
     assert prolog(eps=0.0) == B.SA_ERR_INVALID
     assert prolog(x=None) == B.SA_ERR_INVALID
     assert prolog(ws=100) == B.SA_ERR_WORKSPACE
+    p = B.sa_prolog(4, 64, 128, 7168, 0, 0, 0, 0, 0, 1e-6)
+    assert lib.sa_prolog_workspace_size(C.byref(p), 3) == 4 * 3 * (64 + 4) * 14

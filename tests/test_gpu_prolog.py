@@ -32,7 +32,7 @@ def _run(pi, rows, heads, dim):
     q = torch.empty((rows, heads, dim), dtype=torch.bfloat16, device="cuda")
     k = torch.empty((rows, dim), dtype=torch.bfloat16, device="cuda")
     w = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
-    ws = torch.empty(rows * dim * 4, dtype=torch.uint8, device="cuda")
+    ws = binding.prolog_workspace(p, rows)
     binding.indexer_prolog(p, t["x_q"], t["x"], q, k, w, ws)
     torch.cuda.synchronize()
     return q.float().cpu().numpy().reshape(rows, -1), k.float().cpu().numpy(), w.cpu().numpy()
