@@ -241,6 +241,52 @@ sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_
                           const void *k_idx_new, const void *kv_new, const void *v_new,
                           void *stream);
 
+/*
+ * Paged cache allocator (host side; [SameDay] §3.1: fixed-size blocks that the sparse selection
+ * indexes directly, reference counts and copy-on-write for requests sharing a prefix; §3.2:
+ * blocks acquired incrementally during decoding and reclaimed once no request references them;
+ * §4.3: coalescing and splitting of free blocks, an emergency reserve). The pool only hands out
+ * page numbers; it owns no device memory. Its page tables feed sa_batch. Calls on one pool are
+ * serialised by a lock.
+ *   Free pages form runs of consecutive pages; a freed page merges with the runs it touches, and
+ *   an allocation splits a run. A sequence growing by n pages takes the page right after its
+ *   last one when free, else the smallest run holding all n, else pages from the largest runs.
+ *   The last emergency_pages free pages go only to urgent requests.
+ */
+typedef struct sa_pool sa_pool;
+/* NULL for num_pages < 1, page_size < 1 or emergency_pages outside [0, num_pages] */
+sa_pool *sa_pool_create(int32_t num_pages, int32_t page_size, int32_t emergency_pages);
+void sa_pool_destroy(sa_pool *pool);
+/* free pages, number of free runs, longest free run (any pointer may be NULL) */
+sa_status sa_pool_stats(sa_pool *pool, int32_t *free_pages, int32_t *free_runs, int32_t *largest_run);
+/* sequences hold pages that a page count references; -1 on error */
+int32_t sa_seq_new(sa_pool *pool);
+/* a new sequence sharing every page (and the length) of `parent`: a shared prefix */
+int32_t sa_seq_fork(sa_pool *pool, int32_t parent);
+/* Grows `seq` to new_len tokens, taking pages on demand. When the page that receives the first
+ * new token is shared with another sequence it is replaced by a fresh page (copy-on-write): the
+ * (old, new) page pair is written to copies[0..1] and *n_copies = 1, and the caller copies the
+ * page's contents (sa_copy_pages) before writing the new token. urgent != 0 may use the
+ * emergency reserve. SA_ERR_WORKSPACE when the pool cannot supply the pages (nothing changes);
+ * max_copies must be >= 1 when a copy can arise. new_len <= the current length does nothing. */
+sa_status sa_seq_reserve(sa_pool *pool, int32_t seq, int32_t new_len, int32_t urgent,
+                         int32_t *copies, int32_t max_copies, int32_t *n_copies);
+/* Releases `seq`: each of its pages loses one reference; unreferenced pages are free again. */
+sa_status sa_seq_free(sa_pool *pool, int32_t seq);
+int32_t sa_seq_len(sa_pool *pool, int32_t seq);
+/* Physical page of each logical page of `seq` (*n_pages of them); SA_ERR_WORKSPACE when more
+ * than max_pages. */
+sa_status sa_seq_page_table(sa_pool *pool, int32_t seq, int32_t *page_table, int32_t max_pages,
+                            int32_t *n_pages);
+int32_t sa_pool_refcount(sa_pool *pool, int32_t page);
+
+/* Device copies of whole pages in every cache table the descriptors name (indexer keys and
+ * their scales, block summaries, K, V and their scales): for each pair i, page pairs[2i] to
+ * page pairs[2i+1] (device int32 [n][2]), e.g. the copy-on-write pairs of sa_seq_reserve.
+ * ix or kv may be NULL. Pairs must name distinct destinations. */
+sa_status sa_copy_pages(const sa_indexer *ix, const sa_kv *kv, int32_t page_size,
+                        const int32_t *pairs, int32_t n, void *stream);
+
 /* Weights of the indexer prolog (synthetic in this library's workloads; no trained weights are
  * involved). Weights are [out_features][in_features], row-major bf16. */
 typedef struct sa_prolog {

@@ -54,7 +54,9 @@ class sa_kv(C.Structure):
 _lib = None
 EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
            "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_prolog_workspace_size",
-           "sa_workspace_size",
+           "sa_workspace_size", "sa_pool_create", "sa_pool_destroy", "sa_pool_stats", "sa_seq_new",
+           "sa_seq_fork", "sa_seq_reserve", "sa_seq_free", "sa_seq_len", "sa_seq_page_table",
+           "sa_pool_refcount", "sa_copy_pages",
            "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
            "sa_version")
 
@@ -78,6 +80,23 @@ def load(path: str = LIB_PATH):
     lib.sa_cache_append.argtypes = [pb, pi, pk, P, P, P, P]
     lib.sa_indexer_prolog.argtypes = [C.POINTER(sa_prolog), i32, P, P, P, P, P, P, sz, P]
     lib.sa_prolog_workspace_size.argtypes = [C.POINTER(sa_prolog), i32]
+    lib.sa_pool_create.argtypes = [i32, i32, i32]
+    lib.sa_pool_create.restype = P
+    lib.sa_pool_destroy.argtypes = [P]
+    lib.sa_pool_destroy.restype = None
+    ip = C.POINTER(C.c_int32)
+    lib.sa_pool_stats.argtypes = [P, ip, ip, ip]
+    lib.sa_seq_new.argtypes = [P]
+    lib.sa_seq_fork.argtypes = [P, i32]
+    lib.sa_seq_reserve.argtypes = [P, i32, i32, i32, ip, i32, ip]
+    lib.sa_seq_free.argtypes = [P, i32]
+    lib.sa_seq_len.argtypes = [P, i32]
+    lib.sa_seq_page_table.argtypes = [P, i32, ip, i32, ip]
+    lib.sa_pool_refcount.argtypes = [P, i32]
+    lib.sa_copy_pages.argtypes = [pi, pk, i32, P, i32, P]
+    for fn in ("sa_pool_stats", "sa_seq_new", "sa_seq_fork", "sa_seq_reserve", "sa_seq_free",
+               "sa_seq_len", "sa_seq_page_table", "sa_pool_refcount", "sa_copy_pages"):
+        getattr(lib, fn).restype = C.c_int
     lib.sa_prolog_workspace_size.restype = sz
     lib.sa_workspace_size.argtypes = [pb, pk, i32, i32]
     lib.sa_workspace_size.restype = sz
@@ -246,3 +265,66 @@ def indexer_prolog(p: sa_prolog, x_q, x, q_out, k_out, w_out, ws, stream=None) -
     _check(load().sa_indexer_prolog(C.byref(p), x_q.shape[0], _ptr(x_q), _ptr(x), _ptr(q_out),
                                     _ptr(k_out), _ptr(w_out), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class Pool:
+    """Host-side paged cache allocator (see sa_pool_create): page numbers for sequences, shared
+    prefixes with copy-on-write, coalesced free runs and an emergency reserve."""
+
+    def __init__(self, num_pages: int, page_size: int, emergency_pages: int = 0):
+        self.lib = load()
+        self.h = self.lib.sa_pool_create(num_pages, page_size, emergency_pages)
+        if not self.h:
+            raise SaError(SA_ERR_INVALID, "sa_pool_create rejected its arguments")
+        self.num_pages, self.page_size = num_pages, page_size
+
+    def __del__(self):
+        if getattr(self, "h", None):
+            self.lib.sa_pool_destroy(self.h)
+            self.h = None
+
+    def stats(self):
+        f, r, m = C.c_int32(), C.c_int32(), C.c_int32()
+        _check(self.lib.sa_pool_stats(self.h, C.byref(f), C.byref(r), C.byref(m)))
+        return f.value, r.value, m.value
+
+    def new(self) -> int:
+        s = self.lib.sa_seq_new(self.h)
+        if s < 0:
+            raise SaError(SA_ERR_INVALID, "sa_seq_new failed")
+        return s
+
+    def fork(self, parent: int) -> int:
+        s = self.lib.sa_seq_fork(self.h, parent)
+        if s < 0:
+            raise SaError(SA_ERR_INVALID, "sa_seq_fork failed")
+        return s
+
+    def reserve(self, seq: int, new_len: int, urgent: bool = False):
+        """Grow to new_len tokens; returns the copy-on-write (src, dst) page pairs."""
+        cp = (C.c_int32 * 2)()
+        n = C.c_int32()
+        _check(self.lib.sa_seq_reserve(self.h, seq, new_len, int(urgent), cp, 1, C.byref(n)))
+        return [(cp[0], cp[1])] if n.value else []
+
+    def free(self, seq: int) -> None:
+        _check(self.lib.sa_seq_free(self.h, seq))
+
+    def length(self, seq: int) -> int:
+        return self.lib.sa_seq_len(self.h, seq)
+
+    def page_table(self, seq: int):
+        buf = (C.c_int32 * self.num_pages)()
+        n = C.c_int32()
+        _check(self.lib.sa_seq_page_table(self.h, seq, buf, self.num_pages, C.byref(n)))
+        return list(buf[:n.value])
+
+    def refcount(self, page: int) -> int:
+        return self.lib.sa_pool_refcount(self.h, page)
+
+
+def copy_pages(ix: sa_indexer | None, kv: sa_kv | None, page_size: int, pairs, stream=None) -> None:
+    """Device copies of whole pages (pairs: device int32 [n, 2])."""
+    _check(load().sa_copy_pages(C.byref(ix) if ix is not None else None,
+                                C.byref(kv) if kv is not None else None, page_size,
+                                _ptr(pairs), pairs.shape[0], _stream(stream)))

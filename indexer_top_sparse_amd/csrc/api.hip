@@ -581,6 +581,41 @@ sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_
     return SA_OK;
 }
 
+sa_status sa_copy_pages(const sa_indexer *ix, const sa_kv *kv, int32_t page_size,
+                        const int32_t *pairs, int32_t n, void *stream) {
+    if (n < 0 || (n > 0 && !pairs) || page_size < 1) return fail(SA_ERR_INVALID, "pairs, n or page_size invalid");
+    sa_status st;
+    PageCopyArgs a{};
+    a.pairs = pairs;
+    const int64_t P = page_size;
+    if (ix) {
+        if ((st = check_indexer(ix)) != SA_OK) return st;
+        const int64_t kb = ix->key_dtype == SA_BF16 ? 2 * ix->dim : ix->dim;
+        a.base[0] = static_cast<uint8_t *>(const_cast<void *>(ix->keys));
+        a.page_bytes[0] = P * kb;
+        a.base[1] = reinterpret_cast<uint8_t *>(const_cast<float *>(ix->key_scale));
+        a.page_bytes[1] = P * 4;
+        a.base[2] = const_cast<uint8_t *>(ix->key_mx_scale);
+        a.page_bytes[2] = P * (ix->dim / 32);
+        a.base[3] = static_cast<uint8_t *>(const_cast<void *>(ix->pooled));
+        a.page_bytes[3] = 2 * (int64_t)ix->dim;  // one summary row per page
+    }
+    if (kv) {
+        if ((st = check_kv(kv)) != SA_OK) return st;
+        const int64_t w = (int64_t)kv->heads_kv * kv->dim_qk;
+        a.base[4] = static_cast<uint8_t *>(const_cast<void *>(kv->k));
+        a.page_bytes[4] = P * (kv->dtype == SA_BF16 ? 2 * w : w);
+        a.base[5] = static_cast<uint8_t *>(const_cast<void *>(kv->v));
+        a.page_bytes[5] = P * 2 * (int64_t)kv->heads_kv * kv->dim_v;
+        a.base[6] = reinterpret_cast<uint8_t *>(const_cast<float *>(kv->scale));
+        a.page_bytes[6] = P * 4 * (kv->dtype == SA_FP8_E4M3_T128 ? (int64_t)kv->heads_kv * ((kv->dim_qk + 127) / 128) : 1);
+    }
+    if (n == 0) return SA_OK;
+    hipError_t e = launch_copy_pages(a, n, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "page copy launch");
+    return SA_OK;
+}
+
 size_t sa_prolog_workspace_size(const sa_prolog *p, int32_t rows) {
     if (!p || rows < 1 || p->d_model < 128 || p->d_model % 128 || p->heads < 1 || p->dim < 1) return 0;
     return prolog_workspace_bytes(rows, p->dim, p->heads, p->d_model);

@@ -151,6 +151,28 @@ __global__ __launch_bounds__(128) void k_pool_update(AppendArgs a) {
     a.pooled[page * a.idx_dim + d] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Whole-page copies (copy-on-write of shared pages): workgroup (pair, table) copies page src
+// of one table to page dst, 4-byte words when the page's bytes allow, else bytes.
+__global__ __launch_bounds__(256) void k_copy_pages(PageCopyArgs a) {
+    const int pr = blockIdx.x, t = blockIdx.y;
+    const int64_t bytes = a.page_bytes[t];
+    if (!a.base[t] || bytes == 0) return;
+    const int64_t src = a.pairs[2 * pr], dst = a.pairs[2 * pr + 1];
+    uint8_t *b = a.base[t];
+    if (bytes % 4 == 0) {
+        const uint32_t *s = reinterpret_cast<const uint32_t *>(b + src * bytes);
+        uint32_t *d = reinterpret_cast<uint32_t *>(b + dst * bytes);
+        for (int64_t i = threadIdx.x; i < bytes / 4; i += 256) d[i] = s[i];
+    } else {
+        for (int64_t i = threadIdx.x; i < bytes; i += 256) b[dst * bytes + i] = b[src * bytes + i];
+    }
+}
+
+hipError_t launch_copy_pages(const PageCopyArgs &a, int n, hipStream_t st) {
+    hipLaunchKernelGGL(k_copy_pages, dim3((unsigned)n, (unsigned)kPageTables), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_cache_append(const AppendArgs &a, int rows, bool pool, hipStream_t st) {
     hipLaunchKernelGGL(k_cache_append, dim3((unsigned)rows), dim3(kAppThreads), 0, st, a);
     hipError_t e = hipGetLastError();

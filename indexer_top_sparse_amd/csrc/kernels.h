@@ -140,6 +140,15 @@ struct AppendArgs {
 };
 hipError_t launch_cache_append(const AppendArgs &a, int rows, bool pool, hipStream_t st);
 
+// Whole-page copies across the cache tables: page src of every table to page dst.
+constexpr int kPageTables = 7;  // keys, key scales, MXFP8 exponents, summaries, K, V, KV scales
+struct PageCopyArgs {
+    const int32_t *pairs;               // device [n][2] (src, dst)
+    uint8_t *base[kPageTables];         // table base, or null
+    int64_t page_bytes[kPageTables];    // bytes of one page in the table
+};
+hipError_t launch_copy_pages(const PageCopyArgs &a, int n, hipStream_t st);
+
 // Indexer prolog: query / key / head-weight projections of new token rows, then the key's
 // LayerNorm.
 struct PrologArgs {
