@@ -196,15 +196,22 @@ __device__ __forceinline__ void full_barrier() {
 // are then undefined, and the host can read the flag).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+// `g` is the generation the caller last saw: thread 0 reads it once when the workgroup starts
+// (barrier_gen), before any barrier of the launch can complete (each needs every workgroup of
+// the sequence, including this one), and every barrier advances it by one; so no barrier
+// re-reads the generation before arriving. Only thread 0's copy is used.
+__device__ __forceinline__ uint32_t barrier_gen(const uint32_t *gen) {
+    return __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, uint32_t n,
-                                              uint32_t *err) {
+                                              uint32_t *err, uint32_t &g) {
     __shared__ int s_ok;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics and stores have been performed
     __syncthreads();
     if (threadIdx.x == 0) {
         int ok = 1;
-        const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
+        const uint32_t g0 = g;
         const uint32_t arrived =
             __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (arrived == n - 1) {
@@ -225,6 +232,7 @@ __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, ui
         __builtin_amdgcn_s_waitcnt(0);
         s_ok = ok;
     }
+    ++g;
     __syncthreads();
     return s_ok != 0;
 }

@@ -669,6 +669,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     if (sh.res[0] == 0xFFFFFFFFu) return;  // grid padding (never co-waited on)
     const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], clen = sh.res[3];
     __syncthreads();  // sh.res is reused below
+    SelSync *ss = a.sync + seq;
+    uint32_t bgen = tid == 0 ? barrier_gen(&ss->gen) : 0u;  // see group_barrier
     SeqCtx s;
     s.seq = seq;
     s.ctx = a.ctx_lens[seq];
@@ -799,7 +801,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     __syncthreads();
 
     // ---- radix select over the sequence
-    SelSync *ss = a.sync + seq;
+    uint32_t *s_base = reinterpret_cast<uint32_t *>(s_stage);  // the transpose area is free now
     uint32_t prefix = 0;
     int pbits = 0;
     uint32_t need = 0, total = 0;
@@ -820,9 +822,15 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         }
         __syncthreads();
         uint32_t *gh = ss->hist[pass];
-        for (int i = tid; i < nb; i += kSelThreads)
-            if (sh.hist[i]) add_agent(&gh[i], sh.hist[i]);
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        // pass 0 keeps what each bin held before this workgroup's addition: if the bin turns
+        // out to be the threshold bin, that is where this workgroup's candidates in it go in
+        // the sequence's list (no further allocation round trip)
+        for (int i = tid; i < nb; i += kSelThreads) {
+            const uint32_t c = sh.hist[i];
+            if (pass == 0) s_base[i] = c ? fetch_add_agent(&gh[i], c) : 0u;
+            else if (c) add_agent(&gh[i], c);
+        }
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
         // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t)
         uint32_t hv[4];
         uint32_t csum = 0;
@@ -879,19 +887,17 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         //      distinct, and a larger composite means a larger score or, for equal scores, a
         //      lower candidate index (= lower position). After one exchange every workgroup
         //      reads the list and finds the exact threshold composite in LDS.
-        uint32_t above = 0, eq = 0;
-        for (int i = tid; i < cnt; i += kSelThreads) {
-            const uint32_t k = s_key[i];
-            if (k == 0u) continue;
-            const uint32_t p = k >> 21;
-            above += p > prefix;
-            eq += p == prefix;
+        // this workgroup's candidates above the bin, from its pass-0 histogram (still in LDS):
+        // thread t sums bins [nb - 4(t+1), nb - 4t) above the threshold bin
+        uint32_t above = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = 2048 - 4 * tid - 1 - j;
+            if (b > (int)prefix) above += sh.hist[b];
         }
-        uint32_t above_tot, eq_tot;
+        uint32_t above_tot;
         block_excl_scan<kSelThreads>(above, sh.scan, &above_tot);
-        const uint32_t eq_base = block_excl_scan<kSelThreads>(eq, sh.scan, &eq_tot);
         if (tid == 0) {
-            sh.res[6] = eq_tot ? fetch_add_agent(&ss->list_n, eq_tot) : 0u;
             st_agent(&ss->cnt[chunk][0], above_tot);
             sh.grp[0] = 0u;
         }
@@ -900,8 +906,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             // the list's order is irrelevant (every reader takes all of it), so each wave
             // appends the bin's candidates of one round at consecutive slots: a wave-level
             // ballot and one LDS atomic per wave and round keep the stores coalesced
-            (void)eq_base;
-            const uint32_t lbase = sh.res[6];
+            const uint32_t lbase = s_base[prefix];
             for (int i0 = 0; i0 < cnt; i0 += kSelThreads) {
                 const int i = i0 + tid;
                 const uint32_t k = i < cnt ? s_key[i] : 0u;
@@ -919,7 +924,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 }
             }
         }
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
         // the list (at most kListCap entries) stays in registers: thread tid holds entries
         // tid + kSelThreads r; 0 marks an empty slot (list keys are never 0). All loads are
         // issued before the first is used.
@@ -930,7 +935,6 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             const int j = tid + kSelThreads * r;
             lc[r] = j < (int)listn ? ld_agent64(&ss->list[j]) : 0ull;
         }
-        if (chunk == 0 && tid == 0) st_agent(&ss->list_n, 0u);  // only the appends used it
         const uint32_t Ah = tid < chunk ? ld_agent(&ss->cnt[tid][0]) : 0u;
         uint32_t a_before;
         block_excl_scan<kSelThreads>(Ah, sh.scan, &a_before);
@@ -1080,7 +1084,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             st_agent(&ss->cnt[chunk][0], A);
             st_agent(&ss->cnt[chunk][1], Eq);
         }
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
         // prefix over the earlier workgroups of this sequence (chunk order = position order);
         // G <= kSelThreads, so thread h reads the record of workgroup h
         uint32_t Ah = 0, Eh = 0;
@@ -1150,7 +1154,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- leave the histograms zeroed for the next launch. Every histogram read happens
     //      before the count-exchange (or list) barrier; without that barrier (nothing to
     //      select) one more barrier separates the last reads from the clearing.
-    if (k_eff == 0) ok = group_barrier(&ss->count, &ss->gen, G, a.err) && ok;
+    if (k_eff == 0) ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
     for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
         st_agent(&ss->hist[0][0] + i, 0u);
     (void)ok;
