@@ -53,27 +53,42 @@ __device__ __forceinline__ PlJob pl_job(const PrologArgs &a, int t) {
 // y[m][n] = sum_k x[m][k] * W[n][k] over the job's contraction for MT 16-row tiles from row m0
 // and its kPlCols columns. MFMA 16x16x32: A = x (lane l: row l%16, k = 8(l/16)..), B = W^T (lane
 // l: column l%16 of a 16-column tile, the same k); one activation fragment feeds kPlCT MFMAs.
-// Rows and columns past the ends read the last valid row (loads stay unconditional) and are not
-// stored. Every tile of the grid reads the same activation rows, so each tile walks its
-// contraction from a different starting k-step: the requests of concurrent tiles then spread
-// over the L2 channels instead of meeting on the same lines.
+// Every 16-row x 32-k piece is loaded coalesced (lane l: row l/4, 16 bytes l%4: four requests
+// of 64 contiguous bytes per 16 lanes, instead of sixteen of 16 bytes in the MFMA lane order)
+// and transposed into the MFMA order through the wave's own 1 KiB of LDS (XOR-swizzled, so both
+// sides are free of bank conflicts). Rows and columns past the ends read the last valid row
+// (loads stay unconditional) and are not stored. Every tile of the grid reads the same
+// activation rows, so each tile walks its contraction from a different starting k-step: the
+// requests of concurrent tiles then spread over the L2 channels.
 template <int MT>
 __global__ __launch_bounds__(kPlThreads) void k_prolog_gemm(PrologArgs a, int m0) {
     __shared__ f32x4 red[4][kPlCT][MT][64];
+    __shared__ u32x4 tr[4][64];  // per-wave transpose area
     const PlJob j = pl_job(a, blockIdx.x);
     const int l = lane_id(), w = wave_id(), g = l >> 4;
     const int kq = j.K / 4;  // this wave's quarter of the contraction, a multiple of 32
     const int steps = kq / 32;
+    // coalesced load order: lane l takes row l/4, bytes 16 (l%4) .. of the 64 of a k-step
+    const int lr = l >> 2, lc = l & 3;
     const uint16_t *wp[kPlCT];
 #pragma unroll
     for (int ct = 0; ct < kPlCT; ++ct) {
-        const int nrow = min(j.n0 + 16 * ct + (l & 15), j.nmax - 1) - j.n0;
-        wp[ct] = j.w + (size_t)nrow * j.ldx + (size_t)w * kq + 8 * g;
+        const int nrow = min(j.n0 + 16 * ct + lr, j.nmax - 1) - j.n0;
+        wp[ct] = j.w + (size_t)nrow * j.ldx + (size_t)w * kq + 8 * lc;
     }
     const uint16_t *xp[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        xp[mt] = j.x + (size_t)min(m0 + 16 * mt + (l & 15), a.rows - 1) * j.ldx + (size_t)w * kq + 8 * g;
+        xp[mt] = j.x + (size_t)min(m0 + 16 * mt + lr, a.rows - 1) * j.ldx + (size_t)w * kq + 8 * lc;
+    // 16-byte unit of (row r, chunk c) in the transpose area: 4 rows per 256-byte line, the
+    // chunk index XOR-ed with the line index
+    auto unit = [](int r, int c) { return (r >> 2) * 16 + (r & 3) * 4 + (c ^ ((r >> 2) & 3)); };
+    u32x4 *tw = tr[w];
+    const int wu = unit(lr, lc), ru = unit(l & 15, g);
+    auto frag = [&](u32x4 v) {  // coalesced piece -> MFMA fragment (this wave's LDS only)
+        tw[wu] = v;
+        return tw[ru];
+    };
     f32x4 acc[kPlCT][MT];
 #pragma unroll
     for (int ct = 0; ct < kPlCT; ++ct)
@@ -99,12 +114,18 @@ __global__ __launch_bounds__(kPlThreads) void k_prolog_gemm(PrologArgs a, int m0
     auto mul = [&](int buf, int grp) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (grp * U + u < steps)
+            if (grp * U + u < steps) {
+                u32x4 bf[kPlCT], xv[MT];
+#pragma unroll
+                for (int ct = 0; ct < kPlCT; ++ct) bf[ct] = frag(b[buf][u][ct]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) xv[mt] = frag(xf[buf][u][mt]);
 #pragma unroll
                 for (int ct = 0; ct < kPlCT; ++ct)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc[ct][mt] = mfma16x16x32(xf[buf][u][mt], b[buf][u][ct], acc[ct][mt]);
+                        acc[ct][mt] = mfma16x16x32(xv[mt], bf[ct], acc[ct][mt]);
+            }
     };
     load(0, 0);
     for (int grp = 0; grp < ng; grp += 2) {
@@ -144,9 +165,19 @@ __global__ __launch_bounds__(256) void k_prolog_norm(PrologArgs a) {
     __shared__ float s_red[2][4];
     const int row = blockIdx.x, c = threadIdx.x, l = lane_id(), w = wave_id();
     const int ncols = a.dim + a.heads, ns = a.d_model / pl_slice(a.d_model);
+    // the slices' partial sums, eight loads in flight, added in slice order
     float y = 0.f;
-    if (c < ncols)
-        for (int sl = 0; sl < ns; ++sl) y += a.part[((size_t)sl * a.rows + row) * ncols + c];
+    const float *pp = a.part + (size_t)row * ncols + min(c, ncols - 1);
+    const size_t stride = (size_t)a.rows * ncols;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = pp[(size_t)min(s0 + u, ns - 1) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < ns) y += v[u];
+    }
+    if (c >= ncols) y = 0.f;
     if (c >= a.dim && c < ncols) a.w_out[(size_t)row * a.heads + (c - a.dim)] = y;
     const bool key = c < a.dim;
     // block sums over the key columns (dim <= 128: waves 0 and 1)
