@@ -117,20 +117,22 @@ __device__ __forceinline__ float sum_xor32(float x) {
 __device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips): shifts by 1, 2, 4
+// and 8 lanes inside each row of 16 (a lane without a source adds 0), then row r adds the last
+// lane of row r - 1 (rows 1 and 3), then lane 31 (rows 2 and 3).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(v, o, 64);
-        if (l >= o) v += t;
-    }
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return v;
 }
 
+// Sum over the 64 lanes, the same in every lane.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
 }
 
 // Exclusive prefix sum across the block (NT threads); `scratch` needs NT/64 + 1 words.
@@ -190,37 +192,29 @@ __device__ __forceinline__ void full_barrier() {
 // read only with device-scope atomic operations, which are performed at the device coherence
 // point rather than in a per-XCD L2; so no cache-wide fence is needed. Ordering comes from
 // waiting until every atomic this workgroup issued has completed (s_waitcnt) before arriving,
-// and from reading shared data only after the release has been observed.
-// `count` returns to 0 after every barrier; `gen` only grows. A bounded spin keeps every wave
-// finite: on expiry bit 0 of *err is set and the call returns false (results of that launch
-// are then undefined, and the host can read the flag).
+// and from reading shared data only after every arrival has been observed.
+// `count` only grows during a launch: the j-th barrier (j = 1, 2, ...) of a group of n
+// workgroups is passed once count reaches j n, so the last arrival itself releases the others
+// (no reset and no second atomic on the way). `j` is the caller's barrier number, advanced
+// here; only thread 0's copy is used. group_leave returns count to 0 for the next launch.
+// A bounded spin keeps every wave finite: on expiry bit 0 of *err is set and the call returns
+// false (results of that launch are then undefined, and the host can read the flag).
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// `g` is the generation the caller last saw: thread 0 reads it once when the workgroup starts
-// (barrier_gen), before any barrier of the launch can complete (each needs every workgroup of
-// the sequence, including this one), and every barrier advances it by one; so no barrier
-// re-reads the generation before arriving. Only thread 0's copy is used.
-__device__ __forceinline__ uint32_t barrier_gen(const uint32_t *gen) {
-    return __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, uint32_t n,
-                                              uint32_t *err, uint32_t &g) {
+__device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t n, uint32_t *err,
+                                              uint32_t &j) {
     __shared__ int s_ok;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics and stores have been performed
     __syncthreads();
+    ++j;
     if (threadIdx.x == 0) {
         int ok = 1;
-        const uint32_t g0 = g;
+        const uint32_t target = j * n;
         const uint32_t arrived =
-            __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (arrived == n - 1) {
-            __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_s_waitcnt(0);  // the reset lands before the release below
-            __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
+            __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        if (arrived < target) {
             uint32_t spins = 0;
-            while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+            while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
                 __builtin_amdgcn_s_sleep(1);
                 if (++spins > kSpinLimit) {
                     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -232,9 +226,18 @@ __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t *gen, ui
         __builtin_amdgcn_s_waitcnt(0);
         s_ok = ok;
     }
-    ++g;
     __syncthreads();
     return s_ok != 0;
+}
+
+// After a workgroup's last barrier of the launch: the last of the n to leave (every other one
+// has passed all its barriers, so nobody reads `count` any more) returns both counters to 0.
+__device__ __forceinline__ void group_leave(uint32_t *count, uint32_t *left, uint32_t n) {
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(left, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1) {
+        __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(left, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {

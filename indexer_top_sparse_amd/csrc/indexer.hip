@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], clen = sh.res[3];
     __syncthreads();  // sh.res is reused below
     SelSync *ss = a.sync + seq;
-    uint32_t bgen = tid == 0 ? barrier_gen(&ss->gen) : 0u;  // see group_barrier
+    uint32_t nbar = 0;  // barriers passed (see group_barrier)
     SeqCtx s;
     s.seq = seq;
     s.ctx = a.ctx_lens[seq];
@@ -704,6 +704,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             }
         }
     }
+    // the first radix pass's histogram (top 11 key bits) is built while the keys stream in
+    for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
     __syncthreads();
 
     // ---- scores of this chunk -> LDS keys (0 = not a candidate)
@@ -791,7 +793,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                                 cr.cand(s, c0 + li, c0, a.lp, pos, r);
                                 ok = r >= 0;
                             }
-                            s_key[li] = ok ? float_key(sc) : 0u;
+                            const uint32_t key = ok ? float_key(sc) : 0u;
+                            s_key[li] = key;
+                            if (key) atomicAdd(&sh.hist[key >> 21], 1u);
                         }
                     }
                 }
@@ -812,15 +816,17 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int bits = pass < 2 ? 11 : 10;
         const int shift = 32 - pbits - bits;
         const int nb = 1 << bits;
-        for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < cnt; i += kSelThreads) {
-            const uint32_t k = s_key[i];
-            if (k == 0u) continue;
-            if (pbits && (k >> (32 - pbits)) != prefix) continue;
-            atomicAdd(&sh.hist[(k >> shift) & (nb - 1)], 1u);
+        if (pass > 0) {  // pass 0's histogram was built with the keys
+            for (int i = tid; i < kHistBins; i += kSelThreads) sh.hist[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < cnt; i += kSelThreads) {
+                const uint32_t k = s_key[i];
+                if (k == 0u) continue;
+                if ((k >> (32 - pbits)) != prefix) continue;
+                atomicAdd(&sh.hist[(k >> shift) & (nb - 1)], 1u);
+            }
+            __syncthreads();
         }
-        __syncthreads();
         uint32_t *gh = ss->hist[pass];
         // pass 0 keeps what each bin held before this workgroup's addition: if the bin turns
         // out to be the threshold bin, that is where this workgroup's candidates in it go in
@@ -830,7 +836,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             if (pass == 0) s_base[i] = c ? fetch_add_agent(&gh[i], c) : 0u;
             else if (c) add_agent(&gh[i], c);
         }
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
         // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t)
         uint32_t hv[4];
         uint32_t csum = 0;
@@ -904,27 +910,42 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         __syncthreads();
         {
             // the list's order is irrelevant (every reader takes all of it), so each wave
-            // appends the bin's candidates of one round at consecutive slots: a wave-level
-            // ballot and one LDS atomic per wave and round keep the stores coalesced
+            // appends the bin's candidates of AB rounds at consecutive slots: one ballot per
+            // round, one LDS atomic per wave for all of them, and coalesced stores
             const uint32_t lbase = s_base[prefix];
-            for (int i0 = 0; i0 < cnt; i0 += kSelThreads) {
-                const int i = i0 + tid;
-                const uint32_t k = i < cnt ? s_key[i] : 0u;
-                const bool in_bin = k != 0u && (k >> 21) == prefix;
-                const uint64_t m = __ballot(in_bin);
-                if (m == 0) continue;
+            constexpr int AB = 8;  // rounds whose keys are read before any is used
+            for (int r0 = 0; r0 < cnt; r0 += AB * kSelThreads) {
+                uint32_t kk[AB];
+#pragma unroll
+                for (int u = 0; u < AB; ++u) kk[u] = s_key[min(r0 + u * kSelThreads + tid, cnt - 1)];
+                uint64_t m[AB];
+                uint32_t wtot = 0;
+#pragma unroll
+                for (int u = 0; u < AB; ++u) {
+                    asm volatile("" : "+v"(kk[u]));  // keeps the reads above out of branches
+                    const bool in_bin = r0 + u * kSelThreads + tid < cnt && kk[u] != 0u &&
+                                        (kk[u] >> 21) == prefix;
+                    m[u] = __ballot(in_bin);
+                    wtot += (uint32_t)__popcll(m[u]);
+                }
+                if (wtot == 0) continue;
                 uint32_t woff = 0;
-                if (l == 0) woff = atomicAdd(&sh.grp[0], (uint32_t)__popcll(m));
-                woff = __shfl(woff, 0, 64);
-                if (in_bin) {
-                    const uint32_t below = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    st_agent64(&ss->list[lbase + woff + below],
-                               ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i));
+                if (l == 0) woff = atomicAdd(&sh.grp[0], wtot);
+                woff = __builtin_amdgcn_readfirstlane(woff);
+#pragma unroll
+                for (int u = 0; u < AB; ++u) {
+                    if ((m[u] >> l) & 1ull) {
+                        const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
+                        const int i = r0 + u * kSelThreads + tid;
+                        st_agent64(&ss->list[lbase + woff + below],
+                                   ((uint64_t)kk[u] << 32) | (uint32_t)~(uint32_t)(c0 + i));
+                    }
+                    woff += (uint32_t)__popcll(m[u]);
                 }
             }
         }
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
         // the list (at most kListCap entries) stays in registers: thread tid holds entries
         // tid + kSelThreads r; 0 marks an empty slot (list keys are never 0). All loads are
         // issued before the first is used.
@@ -1004,56 +1025,44 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             const uint64_t c = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i);
             return (c >> (64 - pb)) >= pre;
         };
-        // ordered emission: wave w owns the consecutive groups [g0, g1) of 64 candidates (one
-        // lane per candidate). A first pass counts the wave's selected candidates with one
-        // ballot per group; the wave totals, in wave order, give each wave its first slot; a
-        // second pass repeats the ballots and every selected lane writes at that slot plus the
-        // selected candidates before it.
-        const int ng = (cnt + 63) >> 6;
-        const int gpw = (ng + kSelWaves - 1) / kSelWaves;
-        const int g0 = wave_id() * gpw, g1 = min(ng, g0 + gpw);
-        // keys of EB groups are read before any is used
-        constexpr int EB = 8;
-        auto keys = [&](int gb, uint32_t *kk) {
+        // ordered emission: thread t owns the local candidates [E t, E t + E). Each thread
+        // counts its selected candidates (keys read eight at a time, unconditionally), one
+        // block scan gives its first slot after the earlier workgroups' selections, and a
+        // second walk writes them in position order.
+        const int E = (cnt + kSelThreads - 1) / kSelThreads;
+        const int e0 = min(cnt, tid * E), e1 = min(cnt, e0 + E);
+        auto keys8 = [&](int b, uint32_t *kk) {
 #pragma unroll
-            for (int u = 0; u < EB; ++u) {
-                const int i = 64 * (gb + u) + l;
-                kk[u] = (gb + u < g1 && i < cnt) ? s_key[i] : 0u;
+            for (int u = 0; u < 8; ++u) kk[u] = s_key[min(b + u, e1 - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                asm volatile("" : "+v"(kk[u]));  // keeps the reads above out of branches
+                kk[u] = b + u < e1 ? kk[u] : 0u;
             }
         };
-        uint32_t wcount = 0;
-        for (int gb = g0; gb < g1; gb += EB) {
-            uint32_t kk[EB];
-            keys(gb, kk);
+        uint32_t my_sel = 0;
+        for (int b = e0; b < e1; b += 8) {
+            uint32_t kk[8];
+            keys8(b, kk);
 #pragma unroll
-            for (int u = 0; u < EB; ++u)
-                wcount += (uint32_t)__popcll(__ballot(take(kk[u], 64 * (gb + u) + l)));
+            for (int u = 0; u < 8; ++u) my_sel += take(kk[u], b + u) ? 1u : 0u;
         }
-        // sh.hist is free here: its last reads ended before the radix loop's last barrier
-        if (l == 0) sh.hist[wave_id()] = wcount;
-        __syncthreads();
-        uint32_t run = a_before + taken_before;
-        for (int v = 0; v < wave_id(); ++v) run += sh.hist[v];
-        for (int gb = g0; gb < g1; gb += EB) {
-            uint32_t kk[EB];
-            keys(gb, kk);
+        uint32_t tmp_tot;
+        uint32_t dst = a_before + taken_before + block_excl_scan<kSelThreads>(my_sel, sh.scan, &tmp_tot);
+        for (int b = e0; b < e1; b += 8) {
+            uint32_t kk[8];
+            keys8(b, kk);
 #pragma unroll
-            for (int u = 0; u < EB; ++u) {
-                const int i = 64 * (gb + u) + l;
-                const bool sel = take(kk[u], i);
-                const uint64_t m = __ballot(sel);
-                if (sel) {
-                    const uint32_t dst = run + __builtin_amdgcn_mbcnt_hi(
-                                                   (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    int pos;
-                    int64_t row;
-                    cr.cand(s, c0 + i, c0, a.lp, pos, row);
-                    if (dst < (uint32_t)K) {
-                        out[dst] = pos;
-                        if (slots) slots[dst] = (int32_t)row;
-                    }
+            for (int u = 0; u < 8; ++u) {
+                if (!take(kk[u], b + u)) continue;
+                int pos;
+                int64_t row;
+                cr.cand(s, c0 + b + u, c0, a.lp, pos, row);
+                if (dst < (uint32_t)K) {
+                    out[dst] = pos;
+                    if (slots) slots[dst] = (int32_t)row;
                 }
-                run += (uint32_t)__popcll(m);
+                ++dst;
             }
         }
     } else if (k_eff > 0) {
@@ -1084,7 +1093,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             st_agent(&ss->cnt[chunk][0], A);
             st_agent(&ss->cnt[chunk][1], Eq);
         }
-        ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
         // prefix over the earlier workgroups of this sequence (chunk order = position order);
         // G <= kSelThreads, so thread h reads the record of workgroup h
         uint32_t Ah = 0, Eh = 0;
@@ -1154,9 +1163,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- leave the histograms zeroed for the next launch. Every histogram read happens
     //      before the count-exchange (or list) barrier; without that barrier (nothing to
     //      select) one more barrier separates the last reads from the clearing.
-    if (k_eff == 0) ok = group_barrier(&ss->count, &ss->gen, G, a.err, bgen) && ok;
+    if (k_eff == 0) ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
     for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
         st_agent(&ss->hist[0][0] + i, 0u);
+    group_leave(&ss->count, &ss->left, G);
     (void)ok;
 }
 

@@ -15,8 +15,8 @@ constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup
 constexpr int kListCap = 4096;  // threshold-bin candidates resolved through the list
 
 struct SelSync {
-    uint32_t count;
-    uint32_t gen;
+    uint32_t count;   // barrier arrivals in the current launch (0 between launches)
+    uint32_t left;    // workgroups past their last barrier (0 between launches)
     uint32_t list_n;  // entries appended to `list` in the current launch (0 between launches)
     uint32_t pad[61];
     uint32_t hist[3][2048];
