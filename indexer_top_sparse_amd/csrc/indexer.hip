@@ -1007,23 +1007,25 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             __syncthreads();
             if (whole) break;
         }
+        // the threshold composite: comparing the top pb bits with pre is the same test as
+        // comparing the whole composite with thr. Every composite of the bin or above it is
+        // at least 2^32 (keys of candidates are never 0), so a candidate is selected exactly
+        // when its composite (key << 32 | ~index, key 0 for non-candidates) is at least thr.
+        const uint64_t thr = pre << (64 - pb);
         // list candidates of earlier workgroups that are selected
         uint32_t tb = 0;
 #pragma unroll
         for (int r = 0; r < LPT; ++r) {
             const uint64_t c = lc[r];
             const uint32_t ci = ~(uint32_t)c;
-            // candidates of earlier workgroups: below this chunk's first candidate c0
-            tb += c != 0ull && ((c >> (64 - pb)) >= pre) && ci < (uint32_t)c0;
+            // candidates of earlier workgroups: below this chunk's first candidate c0 (an empty
+            // slot, 0, is below thr)
+            tb += c >= thr && ci < (uint32_t)c0;
         }
         uint32_t taken_before;
         block_excl_scan<kSelThreads>(tb, sh.scan, &taken_before);
         auto take = [&](uint32_t k, int i) -> bool {  // k = s_key[i]
-            if (k == 0u) return false;
-            const uint32_t p = k >> 21;
-            if (p != prefix) return p > prefix;
-            const uint64_t c = ((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i);
-            return (c >> (64 - pb)) >= pre;
+            return (((uint64_t)k << 32) | (uint32_t)~(uint32_t)(c0 + i)) >= thr;
         };
         // ordered emission: thread t owns the local candidates [E t, E t + E). Each thread
         // counts its selected candidates (keys read eight at a time, unconditionally), one
