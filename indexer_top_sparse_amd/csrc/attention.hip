@@ -114,21 +114,19 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
             for (int c = 0; c < NSC; ++c)
                 s_sig[c * a.split_len + j] = slot < 0 ? 0.f : a.kv_scale[(int64_t)slot * NSC + c];
     }
+    __syncthreads();  // the slot table is complete
     // query fragments (B operand of S^T = K Q^T): head L of the pair, d = 32 s + 8 g + e for
-    // this wave's half of the k-steps
+    // this wave's half of the k-steps. A lane past the last head reads head 0 (its column of
+    // scores stays its own and is never stored), so no load sits behind a branch. They are
+    // issued together with the first tile's rows and complete before its store.
     const int head = kPairHeads * hg + 16 * pair + L;
     const bool live = head < a.heads_q;
     u32x4 qf[KH];
     {
         const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + (live ? head : 0)) * DQK + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KH; ++s)
-            qf[s] = live ? ldg16(qr + 32 * (half * KH + s)) : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < KH; ++s) qf[s] = ldg16(qr + 32 * (half * KH + s));
     }
-    // query fragments and the slot table complete here, so that inside the loop the only
-    // vector-memory loads in flight are gathered rows
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     // ---- gather: thread (row srow, j = sj) moves global chunks j, j + TPR, ... of its row
     u32x4 stg[PER];
