@@ -718,7 +718,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int w = wave_id();
         const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
         using KT = KeyTile<DIM, FP8>;
-        constexpr int kPre = 16 / KT::NL;  // tiles in flight per wave: 16 KiB of keys
+        // tiles in flight per wave: 8 KiB of keys (16 and 24 KiB streamed more slowly: with
+        // every CU pulling keys at once, more requests in flight only lengthen the queues)
+        constexpr int kPre = 8 / KT::NL;
         KT f[kPre];
         u32x4 *stage = s_stage[w];
         const bool contiguous = MODE != kBlocks && a.lp >= 4;
