@@ -718,9 +718,11 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int w = wave_id();
         const int my_tiles = ntiles > w ? (ntiles - w + kSelWaves - 1) / kSelWaves : 0;
         using KT = KeyTile<DIM, FP8>;
-        // tiles in flight per wave: 8 KiB of keys (16 and 24 KiB streamed more slowly: with
-        // every CU pulling keys at once, more requests in flight only lengthen the queues)
-        constexpr int kPre = 8 / KT::NL;
+        // tiles in flight per wave: 4 KiB of keys, 8 KiB for MXFP8 (whose tiles cost the least
+        // compute). With every CU pulling keys at once, more requests in flight only lengthen
+        // the memory queues: back to back at decode32k, 4 KiB take 55.7 us per launch against
+        // 56.5 with 8 KiB, and 16 or 24 KiB were slower still.
+        constexpr int kPre = (MX ? 8 : 4) / KT::NL;
         KT f[kPre];
         u32x4 *stage = s_stage[w];
         const bool contiguous = MODE != kBlocks && a.lp >= 4;
