@@ -156,6 +156,33 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
     return base + incl - v;
 }
 
+// Two exclusive prefix sums across the block at once (one pair of barriers); `scratch` needs
+// 2 NT/64 words. Returns the prefix of v; *excl_u gets the prefix of u, *total_v the block total
+// of v.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t v, uint32_t u, uint32_t *scratch,
+                                                     uint32_t *total_v, uint32_t *excl_u) {
+    constexpr int NWV = NT / 64;
+    const uint32_t iv = wave_incl_scan(v), iu = wave_incl_scan(u);
+    __syncthreads();
+    if (lane_id() == 63) {
+        scratch[wave_id()] = iv;
+        scratch[NWV + wave_id()] = iu;
+    }
+    __syncthreads();
+    uint32_t bv = 0, bu = 0, tv = 0;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+        const uint32_t sv = scratch[i], su = scratch[NWV + i];
+        bv += (i < wave_id()) ? sv : 0u;
+        bu += (i < wave_id()) ? su : 0u;
+        tv += sv;
+    }
+    *total_v = tv;
+    *excl_u = bu + iu - u;
+    return bv + iv - v;
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, then meets the
 // other waves. Unlike __syncthreads() it does not wait for outstanding global loads, so a
 // global->LDS prefetch into another buffer stays in flight across it. The signal fences keep

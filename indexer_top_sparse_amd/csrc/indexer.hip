@@ -574,7 +574,7 @@ constexpr int kHistBins = 2048;
 
 struct alignas(16) SelShared {
     uint32_t hist[kHistBins];
-    uint32_t scan[kSelWaves + 1];
+    uint32_t scan[2 * kSelWaves + 1];
     uint32_t res[8];
     uint32_t grp[2];
 };
@@ -841,18 +841,22 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             else if (c) add_agent(&gh[i], c);
         }
         ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
-        // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t)
-        uint32_t hv[4];
-        uint32_t csum = 0;
+        // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t). In
+        // pass 0 the same scan runs over this workgroup's own histogram, which gives its count
+        // above the threshold bin.
+        uint32_t hv[4], lv[4];
+        uint32_t csum = 0, lsum = 0;
         const int top = nb - 4 * tid - 1;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int b = top - j;
             hv[j] = b >= 0 ? ld_agent(&gh[b]) : 0u;
+            lv[j] = (pass == 0 && b >= 0) ? sh.hist[b] : 0u;
             csum += hv[j];
+            lsum += lv[j];
         }
-        uint32_t tot;
-        const uint32_t above0 = block_excl_scan<kSelThreads>(csum, sh.scan, &tot);
+        uint32_t tot, labove0;
+        const uint32_t above0 = block_excl_scan2<kSelThreads>(csum, lsum, sh.scan, &tot, &labove0);
         if (pass == 0) {
             total = tot;
             need = min((uint32_t)a.k, tot);
@@ -860,15 +864,17 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         if (need == 0u) break;
         if (tid == 0) sh.res[3] = 0xFFFFFFFFu;
         __syncthreads();
-        uint32_t run = above0;
+        uint32_t run = above0, lrun = labove0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (run < need && run + hv[j] >= need) {
                 sh.res[3] = (uint32_t)(top - j);
                 sh.res[4] = run;
                 sh.res[5] = hv[j];
+                sh.res[6] = lrun;  // pass 0: this workgroup's candidates above the bin
             }
             run += hv[j];
+            lrun += lv[j];
         }
         __syncthreads();
         const uint32_t T = sh.res[3];
@@ -897,16 +903,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         //      distinct, and a larger composite means a larger score or, for equal scores, a
         //      lower candidate index (= lower position). After one exchange every workgroup
         //      reads the list and finds the exact threshold composite in LDS.
-        // this workgroup's candidates above the bin, from its pass-0 histogram (still in LDS):
-        // thread t sums bins [nb - 4(t+1), nb - 4t) above the threshold bin
-        uint32_t above = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int b = 2048 - 4 * tid - 1 - j;
-            if (b > (int)prefix) above += sh.hist[b];
-        }
-        uint32_t above_tot;
-        block_excl_scan<kSelThreads>(above, sh.scan, &above_tot);
+        // this workgroup's candidates above the bin (found with the pass-0 scan)
+        const uint32_t above_tot = sh.res[6];
         if (tid == 0) {
             st_agent(&ss->cnt[chunk][0], above_tot);
             sh.grp[0] = 0u;
@@ -961,6 +959,10 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             lc[r] = j < (int)listn ? ld_agent64(&ss->list[j]) : 0ull;
         }
         const uint32_t Ah = tid < chunk ? ld_agent(&ss->cnt[tid][0]) : 0u;
+        // the pass-0 histogram (the only one this path uses) was last read before the barrier
+        // above: clear it for the next launch while the list loads are in flight
+        for (int i = chunk * kSelThreads + tid; i < kHistBins; i += G * kSelThreads)
+            st_agent(&ss->hist[0][i], 0u);
         uint32_t a_before;
         block_excl_scan<kSelThreads>(Ah, sh.scan, &a_before);
         // exact threshold among the list: radix passes over the composites' remaining bits
@@ -1166,12 +1168,15 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             if (slots) slots[j] = -1;
         }
 
-    // ---- leave the histograms zeroed for the next launch. Every histogram read happens
-    //      before the count-exchange (or list) barrier; without that barrier (nothing to
-    //      select) one more barrier separates the last reads from the clearing.
-    if (k_eff == 0) ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
-    for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
-        st_agent(&ss->hist[0][0] + i, 0u);
+    // ---- leave the histograms zeroed for the next launch (the list path cleared its one
+    //      above). Every histogram read happens before the count-exchange barrier; without
+    //      that barrier (nothing to select) one more barrier separates the last reads from
+    //      the clearing.
+    if (!(k_eff > 0 && listn > 0)) {
+        if (k_eff == 0) ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
+        for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
+            st_agent(&ss->hist[0][0] + i, 0u);
+    }
     group_leave(&ss->count, &ss->left, G);
     (void)ok;
 }
