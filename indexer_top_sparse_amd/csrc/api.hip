@@ -224,7 +224,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         // capacity -> chunk -> LDS -> capacity, until the plan fits what it assumed. The chunk
         // is the smallest multiple of 64 whose workgroups (sel_groups per sequence, at most
         // kMaxGroupsPerSeq) all fit in the capacity. A chunk that does not fit (LDS, or more
-        // candidates than the emission's ballot groups cover) halves the sequences of this
+        // candidates than kSelMaxChunk) halves the sequences of this
         // launch.
         int occ = occ0, chunk = 64;
         int64_t groups = 0;

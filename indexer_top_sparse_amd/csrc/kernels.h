@@ -8,7 +8,7 @@
 namespace sa {
 
 constexpr int kMaxGroupsPerSeq = 512;  // workgroups sharing one sequence in a selection
-constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup (512 ballot groups)
+constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup (128 KiB of keys)
 
 // Per-sequence record in the workspace used by the cross-workgroup selection. `count` and the
 // histograms return to zero at the end of every launch; `gen` only grows.
