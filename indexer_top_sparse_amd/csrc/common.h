@@ -157,11 +157,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *scratc
 }
 
 // Two exclusive prefix sums across the block at once (one pair of barriers); `scratch` needs
-// 2 NT/64 words. Returns the prefix of v; *excl_u gets the prefix of u, *total_v the block total
-// of v.
+// 2 NT/64 words. Returns the prefix of v; *excl_u gets the prefix of u, *total_v (and *total_u if
+// given) the block totals.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t v, uint32_t u, uint32_t *scratch,
-                                                     uint32_t *total_v, uint32_t *excl_u) {
+                                                     uint32_t *total_v, uint32_t *excl_u,
+                                                     uint32_t *total_u = nullptr) {
     constexpr int NWV = NT / 64;
     const uint32_t iv = wave_incl_scan(v), iu = wave_incl_scan(u);
     __syncthreads();
@@ -170,15 +171,17 @@ __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t v, uint32_t u, uin
         scratch[NWV + wave_id()] = iu;
     }
     __syncthreads();
-    uint32_t bv = 0, bu = 0, tv = 0;
+    uint32_t bv = 0, bu = 0, tv = 0, tu = 0;
 #pragma unroll
     for (int i = 0; i < NWV; ++i) {
         const uint32_t sv = scratch[i], su = scratch[NWV + i];
         bv += (i < wave_id()) ? sv : 0u;
         bu += (i < wave_id()) ? su : 0u;
         tv += sv;
+        tu += su;
     }
     *total_v = tv;
+    if (total_u) *total_u = tu;
     *excl_u = bu + iu - u;
     return bv + iv - v;
 }

@@ -11,10 +11,12 @@ namespace sa {
 
 constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkUnroll = 8;   // histogram passes: keys per thread whose loads are in flight together
+constexpr int kTkPer = 16;     // emission: consecutive keys per thread per round
 
 __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t scan[kTkWaves + 1];
+    __shared__ uint32_t scan[2 * kTkWaves + 1];
     __shared__ uint32_t res[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     int seq, qoff, qlen;
@@ -34,10 +36,20 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
         const int nb = 1 << bits;
         for (int i = tid; i < 2048; i += kTkThreads) hist[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < n; i += kTkThreads) {
-            const uint32_t k = float_key(sc[i]);
-            if (pbits && (k >> (32 - pbits)) != prefix) continue;
-            atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+        // coalesced keys, kTkUnroll loads in flight per thread: issued unconditionally (clamped
+        // to the last key; the opaque copies keep them out of branches), then masked
+        for (int i0 = tid; i0 < n; i0 += kTkUnroll * kTkThreads) {
+            uint32_t kk[kTkUnroll];
+#pragma unroll
+            for (int u = 0; u < kTkUnroll; ++u) kk[u] = float_key(sc[min(i0 + u * kTkThreads, n - 1)]);
+#pragma unroll
+            for (int u = 0; u < kTkUnroll; ++u) {
+                asm volatile("" : "+v"(kk[u]));
+                const uint32_t k = kk[u];
+                if (i0 + u * kTkThreads >= n) continue;
+                if (pbits && (k >> (32 - pbits)) != prefix) continue;
+                atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+            }
         }
         __syncthreads();
         uint32_t hv[4], csum = 0;
@@ -69,44 +81,49 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
         __syncthreads();
     }
 
+    // ordered emission, rounds of kTkPer consecutive keys per thread: keys above the threshold
+    // prefix are taken, and keys equal to it are taken in position order while fewer than
+    // `need` of them have been (all of them when the threshold bin is taken whole). One scan
+    // of (above, equal) counts per round gives every thread its first slot: the keys above
+    // before it plus the equal keys taken before it.
     if (k_eff > 0) {
         const int shb = 32 - pbits;
-        uint32_t dst_base = 0, eq_base = 0;
-        for (int base = 0; base < n; base += 4 * kTkThreads) {
-            uint32_t keys[4];
-            int my_eq = 0;
+        const uint32_t need_eq = exact ? 0xFFFFFFFFu : need;
+        uint32_t above_base = 0, eq_base = 0;
+        for (int base = 0; base < n; base += kTkPer * kTkThreads) {
+            const int i0 = base + kTkPer * tid;
+            uint32_t keys[kTkPer];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = base + 4 * tid + j;
-                keys[j] = i < n ? float_key(sc[i]) : 0u;
-                my_eq += (i < n) && ((keys[j] >> shb) == prefix);
-            }
-            uint32_t tot_eq, tot_sel;
-            uint32_t er = eq_base + block_excl_scan<kTkThreads>(my_eq, scan, &tot_eq);
-            bool take[4];
-            int my_sel = 0;
+            for (int j = 0; j < kTkPer; ++j) keys[j] = float_key(sc[min(i0 + j, n - 1)]);
+            uint32_t my_above = 0, my_eq = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = base + 4 * tid + j;
+            for (int j = 0; j < kTkPer; ++j) {
+                asm volatile("" : "+v"(keys[j]));
+                const bool in = i0 + j < n;
                 const uint32_t p = keys[j] >> shb;
-                take[j] = false;
-                if (i < n) {
-                    if (p > prefix) take[j] = true;
-                    else if (p == prefix) {
-                        take[j] = exact || er < need;
-                        ++er;
-                    }
-                }
-                my_sel += take[j];
+                my_above += (in && p > prefix) ? 1u : 0u;
+                my_eq += (in && p == prefix) ? 1u : 0u;
             }
-            uint32_t dst = dst_base + block_excl_scan<kTkThreads>(my_sel, scan, &tot_sel);
+            uint32_t tot_above, tot_eq, eq_excl;
+            const uint32_t above_excl =
+                block_excl_scan2<kTkThreads>(my_above, my_eq, scan, &tot_above, &eq_excl, &tot_eq);
+            uint32_t er = eq_base + eq_excl;
+            uint32_t dst = above_base + above_excl + min(er, need_eq);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (take[j]) {
-                    if (dst < k_eff) out[dst] = base + 4 * tid + j;
+            for (int j = 0; j < kTkPer; ++j) {
+                if (i0 + j >= n) break;
+                const uint32_t p = keys[j] >> shb;
+                bool take = p > prefix;
+                if (p == prefix) {
+                    take = er < need_eq;
+                    ++er;
+                }
+                if (take) {
+                    if (dst < k_eff) out[dst] = i0 + j;
                     ++dst;
                 }
-            dst_base += tot_sel;
+            }
+            above_base += tot_above;
             eq_base += tot_eq;
         }
     }
