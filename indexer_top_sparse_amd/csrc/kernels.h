@@ -10,15 +10,14 @@ namespace sa {
 constexpr int kMaxGroupsPerSeq = 512;  // workgroups sharing one sequence in a selection
 constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup (128 KiB of keys)
 
-// Per-sequence record in the workspace used by the cross-workgroup selection. `count` and the
-// histograms return to zero at the end of every launch; `gen` only grows.
+// Per-sequence record in the workspace used by the cross-workgroup selection. The counters and
+// the histograms return to zero by the end of every launch.
 constexpr int kListCap = 4096;  // threshold-bin candidates resolved through the list
 
 struct SelSync {
     uint32_t count;   // barrier arrivals in the current launch (0 between launches)
     uint32_t left;    // workgroups past their last barrier (0 between launches)
-    uint32_t list_n;  // entries appended to `list` in the current launch (0 between launches)
-    uint32_t pad[61];
+    uint32_t pad[62];
     uint32_t hist[3][2048];
     uint32_t cnt[kMaxGroupsPerSeq][2];
     uint64_t list[kListCap];  // (key << 32 | ~candidate) of the threshold bin's candidates
