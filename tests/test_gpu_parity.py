@@ -146,6 +146,23 @@ def test_topk_exact_on_shared_scores():
     np.testing.assert_array_equal(idx, ref)
 
 
+def test_topk_crowded_threshold_bin():
+    """Row Top-K when the first threshold bin and above hold more keys than the LDS list takes
+    (row 0: 20000 distinct scores in [1, 1.02), one bin of the first digit, so the further passes
+    re-read the row) and when they fit (row 1: N(0,1) scores, ties broken by position in LDS)."""
+    rng = np.random.default_rng(5)
+    wl = inputs.make("decode32k", num_seqs=2, ctx=[20000, 12000])
+    dw = device.to_device(wl)
+    s = np.full((2, 20000), -np.inf, dtype=np.float32)
+    s[0] = (1.0 + 0.02 * rng.permutation(20000) / 20000).astype(np.float32)
+    s[1, :12000] = rng.standard_normal(12000).astype(np.float32)
+    s[1, 100:600] = s[1, 50]                     # ties around a typical value
+    st = torch.from_numpy(s).cuda()
+    idx = device.topk(dw, st, k=2048).cpu().numpy()
+    ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
+    np.testing.assert_array_equal(idx, ref)
+
+
 def test_sparse_attn_on_oracle_indices():
     wl = inputs.make("decode32k", num_seqs=3, ctx=[3000, 40, 2100])
     dw = device.to_device(wl)
