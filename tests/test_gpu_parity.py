@@ -149,14 +149,20 @@ def test_topk_exact_on_shared_scores():
 def test_topk_crowded_threshold_bin():
     """Row Top-K when the first threshold bin and above hold more keys than the LDS list takes
     (row 0: 20000 distinct scores in [1, 1.02), one bin of the first digit, so the further passes
-    re-read the row) and when they fit (row 1: N(0,1) scores, ties broken by position in LDS)."""
+    re-read the row), when they fit (row 1: N(0,1) scores, ties broken by position in LDS), and
+    at the list's capacity of 7168 keys (row 2: exactly 7168 in the bin, the LDS path; row 3: one
+    more, the re-reading path)."""
     rng = np.random.default_rng(5)
-    wl = inputs.make("decode32k", num_seqs=2, ctx=[20000, 12000])
+    wl = inputs.make("decode32k", num_seqs=4, ctx=[20000, 12000, 9000, 9000])
     dw = device.to_device(wl)
-    s = np.full((2, 20000), -np.inf, dtype=np.float32)
+    s = np.full((4, 20000), -np.inf, dtype=np.float32)
     s[0] = (1.0 + 0.02 * rng.permutation(20000) / 20000).astype(np.float32)
     s[1, :12000] = rng.standard_normal(12000).astype(np.float32)
     s[1, 100:600] = s[1, 50]                     # ties around a typical value
+    for r, m in ((2, 7168), (3, 7169)):
+        s[r, :9000] = (0.5 * rng.random(9000)).astype(np.float32)          # bins below [2, 2.5)
+        sel = rng.permutation(9000)[:m]
+        s[r, sel] = (2.0 + 0.4 * rng.permutation(m) / m).astype(np.float32)  # one first-digit bin
     st = torch.from_numpy(s).cuda()
     idx = device.topk(dw, st, k=2048).cpu().numpy()
     ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
