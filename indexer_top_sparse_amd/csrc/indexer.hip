@@ -631,15 +631,14 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     // ---- locate this workgroup's (sequence, chunk): chunk counts prefix over sequences
     if (tid < 64) {
         uint32_t base = 0;
-        int found_seq = -1, found_chunk = 0, found_G = 0, found_len = 64;
+        int found_seq = -1, found_chunk = 0, found_G = 0, found_ctx = 0;
         for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
             const int b = b0 + l;
             uint32_t nchunks = 0;
-            int len = 64;
+            int ctx_b = 0;
             if (b < a.num_seqs) {
-                const int nc = ncand_of(MODE, a.ctx_lens[b], a.lp, a.block_k);
-                len = a.chunk;
-                nchunks = sel_groups(nc, len);
+                ctx_b = a.ctx_lens[b];
+                nchunks = sel_groups(ncand_of(MODE, ctx_b, a.lp, a.block_k), a.chunk);
             }
             const uint32_t incl = wave_incl_scan(nchunks);
             const uint32_t excl = base + incl - nchunks;
@@ -647,7 +646,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 found_seq = b;
                 found_chunk = blockIdx.x - excl;
                 found_G = nchunks;
-                found_len = len;
+                found_ctx = ctx_b;
             }
             base += __shfl(incl, 63, 64);
         }
@@ -657,23 +656,24 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         const int fs = __shfl(found_seq, src, 64);
         const int fc = __shfl(found_chunk, src, 64);
         const int fg = __shfl(found_G, src, 64);
-        const int fl = __shfl(found_len, src, 64);
+        const int fx = __shfl(found_ctx, src, 64);
         if (tid == 0) {
             sh.res[0] = m ? fs : 0xFFFFFFFFu;
             sh.res[1] = fc;
             sh.res[2] = fg;
-            sh.res[3] = fl;
+            sh.res[3] = fx;  // the sequence's length, already loaded here
         }
     }
     __syncthreads();
     if (sh.res[0] == 0xFFFFFFFFu) return;  // grid padding (never co-waited on)
-    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], clen = sh.res[3];
+    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], ctx = (int)sh.res[3];
+    const int clen = a.chunk;
     __syncthreads();  // sh.res is reused below
     SelSync *ss = a.sync + seq;
     uint32_t nbar = 0;  // barriers passed (see group_barrier)
     SeqCtx s;
     s.seq = seq;
-    s.ctx = a.ctx_lens[seq];
+    s.ctx = ctx;
     s.ncand = ncand_of(MODE, s.ctx, a.lp, a.block_k);
     s.pt = a.page_table + (int64_t)seq * a.pages_per_seq;
     s.blocks = MODE == kCandidates ? a.blocks + (int64_t)seq * a.block_k : nullptr;
