@@ -401,3 +401,77 @@ def test_f32_oracle_agrees_with_f64():
     for r in range(2):
         assert check_topk_row(b["idx"][r], a["idx"][r], a["scores"][r], 3000, wl.topk) == ""
     np.testing.assert_allclose(b["out"], a["out"], atol=1e-5)
+
+
+def _block_workload(ctx_lens, P=16, block_topk=6, perm_seed=0, seed=21):
+    """Two-level workload whose block summaries are computed here from the logical key rows
+    (fp64 mean over each block's valid tokens, rounded to bf16) and handed to the layout
+    builder per logical block, so nothing on the reference side reads the page table."""
+    g = torch.Generator().manual_seed(seed)
+    B = len(ctx_lens)
+    idx_dim, idx_heads = 32, 4
+    kI = [torch.randn(n, idx_dim, generator=g).to(torch.bfloat16) for n in ctx_lens]
+    pooled = []
+    for n, rows in zip(ctx_lens, kI):
+        nb = -(-n // P)
+        pooled.append(torch.stack([rows[j * P:min(n, (j + 1) * P)].double().mean(0)
+                                   for j in range(nb)]).to(torch.bfloat16))
+    kv = [torch.randn(n, 1, 576, generator=g).to(torch.bfloat16) for n in ctx_lens]
+    wl = custom_workload(
+        ctx_lens=ctx_lens, page_size=P, q_lens=[1] * B,
+        q_idx=torch.randn(B, idx_heads, idx_dim, generator=g).to(torch.bfloat16),
+        w=torch.randn(B, idx_heads, generator=g) / 8, idx_keys_logical=kI,
+        q=torch.randn(B, 2, 576, generator=g).to(torch.bfloat16), kv_logical=kv, topk=40,
+        block_topk=block_topk, pooled_logical=pooled, softmax_scale=1 / 24, perm_seed=perm_seed,
+        dim_v=512)
+    return wl, pooled
+
+
+def _np_block_score(q, w, kbar):
+    """sum_h w_h * max(q_h . kbar, 0) in fp64 (the score formula applied to one summary row)."""
+    d = q.double().numpy() @ kbar.double().numpy()
+    return float(np.sum(w.double().numpy() * np.maximum(d, 0.0)))
+
+
+def test_block_scores_follow_the_page_table():
+    """Coarse stage ([SameDay] §3.1: blocks are ranked by their cached summaries): the score of
+    logical block j is the formula applied to the summary of block j, wherever the page table
+    put it. The pages are shuffled, so reading the summary table by logical index (row j
+    instead of row page_table[b][j]) gives different scores; the test checks that it would."""
+    ctx = [300, 77]
+    wl, pooled = _block_workload(ctx)
+    assert not torch.equal(wl.page_table[0, :5], torch.arange(5, dtype=torch.int32))
+    got = oracle.block_scores(wl)
+    wrong_gap = 0.0
+    for b, n in enumerate(ctx):
+        nb = -(-n // wl.page_size)
+        for j in range(wl.pages_per_seq):
+            if j >= nb:
+                assert np.isneginf(got[b, j])
+                continue
+            ref = _np_block_score(wl.q_idx[b], wl.w[b], pooled[b][j])
+            assert abs(got[b, j] - ref) <= 1e-12 * max(1.0, abs(ref)), (b, j, got[b, j], ref)
+            # what a lookup by logical index would have scored
+            wrong = _np_block_score(wl.q_idx[b], wl.w[b], wl.pooled[j])
+            wrong_gap = max(wrong_gap, abs(wrong - ref))
+    assert wrong_gap > 0.05 * np.abs(got[np.isfinite(got)]).max()
+
+
+def test_two_level_page_permutation_invariance():
+    """The same logical caches under two different page tables give the same block sets, the
+    same token sets and bitwise the same outputs (selection works on logical positions)."""
+    ctx = [300, 77, 150]
+    a, _ = _block_workload(ctx, perm_seed=0)
+    b, _ = _block_workload(ctx, perm_seed=5)
+    assert not torch.equal(a.page_table, b.page_table)
+    ra, rb = oracle.decode_step(a), oracle.decode_step(b)
+    np.testing.assert_array_equal(ra["blocks"], rb["blocks"])
+    np.testing.assert_array_equal(ra["idx"], rb["idx"])
+    np.testing.assert_array_equal(ra["out"], rb["out"])
+    # and the kept blocks are the best-scoring logical blocks computed from the logical rows
+    _, pooled = _block_workload(ctx, perm_seed=0)
+    for s, n in enumerate(ctx):
+        nb = -(-n // a.page_size)
+        sc = [_np_block_score(a.q_idx[s], a.w[s], pooled[s][j]) for j in range(nb)]
+        best = sorted(range(nb), key=lambda j: (-sc[j], j))[:a.block_topk]
+        assert sorted(best) == [j for j in ra["blocks"][s] if j >= 0]
