@@ -124,11 +124,34 @@ int attn_splits(int rows, int k, int heads_q) {
 }
 int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }
 
+// Latent-row attention (bf16 rows of 576 entries, V = the first 512, up to 128 query heads):
+// one workgroup per (query row, split) with every head, the splits merged inside the launch.
+constexpr int kAttnTarget = 256;  // workgroups that fill an MI355X (one per CU)
+bool latent_shape(const sa_kv *kv) {
+    return kv->dim_qk == 576 && kv->dim_v == 512 && kv->v == nullptr && kv->dtype == SA_BF16 &&
+           kv->heads_q <= 128;
+}
+struct AttnPlan {
+    bool latent;
+    int splits, merge;
+};
+// Splits of the latent kernel: enough workgroups to fill the device, at least 4 tiles of 32 rows
+// per split, at most kMaxSplitRows rows per split (the per-row tables live in LDS).
+AttnPlan latent_plan(int rows, int k, int max_splits) {
+    const int r = std::max(rows, 1);
+    int s = std::max(1, (kAttnTarget + r - 1) / r);
+    s = std::min(s, std::max(1, (k + 127) / 128));
+    s = std::min(s, std::max(1, max_splits));
+    s = std::max(s, (k + kMaxSplitRows - 1) / kMaxSplitRows);
+    AttnPlan p{true, s, s == 1 ? 0 : (rows % 8 == 0 ? 2 : 1)};
+    return p;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
     size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, slots = 0, part_o = 0, part_ml = 0,
-           total = 0;
+           rsync = 0, total = 0;
 };
 
 WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int block_k) {
@@ -148,12 +171,18 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
         L.slots = off;  // physical rows of the fused step's index set
         off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(k, 0));
         const int rmax = std::max(rows, b->num_seqs);
-        // the split count only grows as rows shrink; size for the larger of the two
-        const int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
-        L.part_o = off;
-        off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * kv->heads_q * kv->dim_v);
+        // the split count only grows as rows shrink; size for the larger of the two, for
+        // either kernel
+        int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
+        if (latent_shape(kv))
+            s = std::max(s, std::max(latent_plan(rows, k, 1 << 30).splits,
+                                     latent_plan(b->num_seqs, k, 1 << 30).splits));
+        L.part_o = off;  // (the latent kernel's blocks round the heads up to 16)
+        off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * (16 * ((kv->heads_q + 15) / 16)) * kv->dim_v);
         L.part_ml = off;
         off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * kv->heads_q);
+        L.rsync = off;  // per-row merge records (rows of a merge launch fit the device)
+        off = align256(off + sizeof(uint32_t) * kRowSyncWords * (size_t)std::min(rmax, 4096));
     }
     L.total = off;
     return L;
@@ -298,7 +327,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
 sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
                    const int32_t *idx, const int32_t *slots, int k, void *out, uint8_t *ws,
                    const WsLayout &L, hipStream_t st) {
-    AttnArgs a;
+    AttnArgs a{};
     a.num_seqs = b->num_seqs;
     a.lp = log2i(b->page_size);
     a.pages_per_seq = b->pages_per_seq;
@@ -322,7 +351,32 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     a.out = static_cast<uint16_t *>(out);
     a.part_o = reinterpret_cast<uint16_t *>(ws + L.part_o);
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
+    a.row_sync = reinterpret_cast<uint32_t *>(ws + L.rsync);
+    a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+    a.merge_inside = 0;
     if (rows == 0) return SA_OK;
+    if (latent_shape(kv)) {
+        // the splits of a row wait for each other, so a merging grid must fit the device's
+        // resident capacity (one workgroup per CU: the tile ring takes most of the LDS)
+        static int occ = 0;
+        if (occ == 0) occ = attn_latent_occupancy(kMaxSplitRows);
+        const int cap = std::max(occ, 0) * device_cus();
+        AttnPlan p = latent_plan(rows, k, 1 << 30);
+        while (p.merge && lat_grid_host(rows, p.splits, p.merge) > cap) {
+            const AttnPlan q2 = latent_plan(rows, k, p.splits - 1);
+            if (q2.splits >= p.splits) break;
+            p = q2;
+        }
+        if (!p.merge || lat_grid_host(rows, p.splits, p.merge) <= cap) {
+            a.splits = p.splits;
+            a.split_len = split_len(k, p.splits);
+            a.merge_inside = p.merge;
+            a.hgroups = 1;
+            hipError_t e = launch_attn_latent(a, st);
+            if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+            return SA_OK;
+        }
+    }
     hipError_t e = launch_sparse_attn(a, kv->dim_qk, kv->dim_v, kv->v != nullptr,
                                       (int)kv->dtype, st);
     if (e != hipSuccess) return hip_fail(e, "sparse attention launch");

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(512, 1) void k_sparse_attn_pairs(AttnArgs a) {
             for (int c = 0; c < NSC; ++c)
                 s_sig[c * a.split_len + j] = slot < 0 ? 0.f : a.kv_scale[(int64_t)slot * NSC + c];
     }
-    __syncthreads();  // the slot table is complete
+    __syncthreads();  // the slot table is complete: load(0) reads rows written by other threads
     // query fragments (B operand of S^T = K Q^T): head L of the pair, d = 32 s + 8 g + e for
     // this wave's half of the k-steps. A lane past the last head reads head 0 (its column of
     // scores stays its own and is never stored), so no load sits behind a branch. They are
@@ -405,6 +405,401 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; e += 2)
         *reinterpret_cast<uint32_t *>(orow + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
+}
+
+// ================================================== latent rows, all query heads per workgroup
+// bf16 latent rows (576 entries: the first 512 are V) and up to 128 query heads sharing them
+// (MLA-style decode and prefill; [CANN] §1 and §2.1). One workgroup of 8 waves per (query row,
+// split of its index set); wave w owns heads 16 w .. 16 w + 15 with the whole 576-wide
+// contraction, so each gathered row is staged once per split and serves every head, and no
+// partial score crosses waves:
+//   S^T[row][head] = K[row][:] . Q[head][:]       (16x16x32 bf16 MFMA, 2 x 18 per 32-row tile)
+//   online softmax per head                        (a lane holds 8 rows of one head)
+//   O^T[d][head] += V^T[d][row] . P^T[row][head]  (32 MFMAs per tile, V^T by transposing reads)
+// Two waves per SIMD keep the 16x16x32 MFMA at its full rate. A wave's query fragments (72
+// registers) and output accumulators (128) take most of its 256, so addresses are rebuilt per
+// tile and LDS reads run only a few fragments ahead of their MFMAs.
+// Rows move from HBM straight into LDS (global_load_lds_dwordx4) through a ring of three 32-row
+// tiles: while tile t is computed, tiles t + 1 and t + 2 are in flight, and the copies use no
+// registers. Each wave issues kLatCopies copies of 1 KiB per tile (36 KiB per tile; waves 4..7
+// repeat blocks 32..35 in their last copy, writing the same bytes twice), so every wave waits
+// for an exact count.
+//
+// Index sets split over several workgroups (few query rows, as in decode) are merged inside the
+// same launch: each split publishes its output normalised by its own sum (bf16) with its
+// (max, sum) per head through agent-scope stores, the splits of a row meet at a barrier, and
+// then split s merges the heads [s H / S, (s + 1) H / S) for all splits, in split order (the
+// result does not depend on timing). This needs every split of a row resident at once: the
+// host only chooses it when the grid fits the device's resident capacity. Workgroup b runs on
+// XCD b mod 8 (round-robin dispatch), so with a multiple of 8 rows the splits of a row are given
+// indices of one residue mod 8: their merge then reads partials written on the same XCD.
+constexpr int kLatQK = 576, kLatV = 512;
+constexpr int kLatRowB = 2 * kLatQK;          // bytes per staged row
+constexpr int kLatTileB = kTile * kLatRowB;   // 36864 bytes per tile
+constexpr int kLatRing = 3;
+constexpr int kLatWaves = 8;
+constexpr int kLatThreads = 64 * kLatWaves;
+constexpr int kLatCopies = 5;                 // 1 KiB copies per wave per tile
+constexpr int kLatKS = kLatQK / 32;           // 18 k-steps of 32 entries
+constexpr int kLatDT = kLatV / 16;            // 32 d_v tiles of 16 entries
+static_assert(kLatTileB == 36 * 1024, "36 one-KiB copies per tile");
+
+// Workgroup b -> (query row, split). merge_inside 0: one workgroup per row. 1: row b % rows,
+// split b / rows. 2 (rows a multiple of 8): the splits of row r get indices of residue r mod 8.
+__device__ __forceinline__ void lat_row_of(int b, int rows, int splits, int merge, int &r,
+                                           int &split) {
+    if (merge == 0) {
+        r = b;
+        split = 0;
+    } else if (merge == 1) {
+        r = b % rows;
+        split = b / rows;
+    } else {
+        const int local = b >> 3;
+        r = 8 * (local / splits) + (b & 7);
+        split = local % splits;
+    }
+}
+
+__host__ __device__ inline int lat_grid(int rows, int splits, int merge) {
+    return merge == 2 ? 8 * splits * ((rows + 7) / 8) : rows * splits;
+}
+
+// A value the compiler may not take apart (so that it keeps a base register and folds
+// constants into instruction offsets instead of hoisting one register per address).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+__global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // dynamic LDS: ring [3][36864] | slots [split_len] int32 | logit bias [split_len] fp32
+    uint8_t *ring = lds;
+    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + kLatRing * kLatTileB);
+    float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
+    __shared__ int s_leave;
+
+    const int tid = threadIdx.x, l = lane_id(), g = l >> 4, L = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int row, split;
+    lat_row_of(blockIdx.x, a.rows, a.splits, a.merge_inside, row, split);
+    if (row >= a.rows) return;  // padding of the XCD-aligned grid: no barrier counts on it
+    int seq, qoff, qlen;
+    row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
+    const int32_t *pt = a.page_table + (int64_t)seq * a.pages_per_seq;
+    const int j0 = split * a.split_len;
+    const int j1 = min(a.k, j0 + a.split_len);
+    const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+    const int P = 1 << a.lp;
+
+    // ---- query fragments (B operand of S^T = K Q^T): head 16 w + L, entries 32 s + 8 g + e.
+    //      A lane past the last head reads head 0; its column is never stored. Issued first,
+    //      so that their latency overlaps the slot-table loads below.
+    const int head = 16 * w + L;
+    const bool live_wave = 16 * w < a.heads_q;
+    const bool live = head < a.heads_q;
+    u32x4 qf[kLatKS];
+    {
+        const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + (live ? head : 0)) * kLatQK + 8 * g;
+#pragma unroll
+        for (int s = 0; s < kLatKS; ++s) qf[s] = ldg16(qr + 32 * s);
+    }
+    // ---- slot and bias of every selected row of this split
+    for (int j = tid; j < ntiles * kTile; j += kLatThreads) {
+        int32_t slot = -1;
+        if (j0 + j < j1) {
+            if (a.slots) {
+                slot = a.slots[(int64_t)row * a.k + j0 + j];
+            } else {
+                const int e = a.idx[(int64_t)row * a.k + j0 + j];
+                if (e >= 0) slot = pt[e >> a.lp] * P + (e & (P - 1));
+            }
+        }
+        s_slot[j] = slot;
+        s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
+    }
+    // every load above completes here (the query fragments included): inside the tile loop the
+    // only vector-memory operations in flight are this wave's tile copies, which the waits
+    // below count exactly
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // the slot table is complete
+    // ---- staged tile layout: 16-byte chunk c of row r lives at byte
+    //      4096 (c / 8) + 128 r + 16 ((c % 8) ^ swz(r)), i.e. nine column groups of 128 bytes per
+    //      row, each group holding the 32 rows. Copy block b (1 KiB) fills group b / 4, rows
+    //      8 (b % 4) .. + 7: lane j takes row 8 (b % 4) + j / 8 and position j % 8.
+    const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
+    auto issue = [&](int t) {  // copies of tile min(t, ntiles - 1) into ring slot t % 3
+        const int tt = min(t, ntiles - 1);
+        const uint32_t base = ring_lds + (uint32_t)(t % kLatRing) * kLatTileB;
+        // recomputed from an opaque lane id: held across the loop these would take registers
+        const int lc = (int)opaque((uint32_t)l);
+#pragma unroll
+        for (int k = 0; k < kLatCopies; ++k) {
+            const int blk = k < 4 ? w + 8 * k : 32 + (w & 3);
+            const int r = 8 * (blk & 3) + (lc >> 3);
+            const int c = 8 * (blk >> 2) + ((lc & 7) ^ swz(r));
+            const int32_t slot = s_slot[tt * kTile + r];
+            const uint8_t *src = (slot < 0 ? a.zero_row : a.kc + (int64_t)slot * kLatRowB) + 16 * c;
+            copy16_to_lds(src, __builtin_amdgcn_readfirstlane(base + 1024u * (uint32_t)blk));
+        }
+    };
+
+    f32x4 o[kLatDT];
+#pragma unroll
+    for (int n = 0; n < kLatDT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -__builtin_inff(), l_run = 0.f;
+
+    if (ntiles > 0) {
+        issue(0);
+        issue(1);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        // tile t has landed once at most the copies of tile t + 1 are outstanding
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLatCopies));
+        lds_barrier();  // every wave's copies of tile t landed; tile t - 1 fully read
+        issue(t + 2);   // into the slot tile t - 1 occupied
+        if (!live_wave) continue;
+        const uint32_t kb = ring_lds + (uint32_t)(t % kLatRing) * kLatTileB;
+        // ---- S^T over the 576-wide contraction: two 16-row M tiles. Key fragment of k-step s,
+        //      M tile mt: row 16 mt + L, chunk 4 s + g = 8 (s / 2) + (4 (s % 2) + g): column group
+        //      s / 2 is an immediate offset, the swizzle touches the second part only. The bases
+        //      are recomputed per tile from an opaque lane id (held across the loop they would
+        //      take registers). Reads run kKA steps ahead of their MFMA.
+        constexpr int kKA = 4;
+        f32x4 sa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        uint32_t kbase[2][2];
+        {
+            const uint32_t lo = opaque((uint32_t)l), Lo = lo & 15u, go = lo >> 4;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp) {
+                    const int r = 16 * mt + (int)Lo;
+                    kbase[mt][sp] = kb + (uint32_t)(128 * r + 16 * ((4 * sp + (int)go) ^ swz(r)));
+                }
+        }
+        auto kread = [&](int i) {  // step i = 2 s + mt
+            const int s = i >> 1, mt = i & 1;
+            return *reinterpret_cast<const SA_LDS u32x4 *>(kbase[mt][s & 1] + 4096u * (uint32_t)(s >> 1));
+        };
+        u32x4 kf[kKA];
+#pragma unroll
+        for (int i = 0; i < kKA; ++i) kf[i] = kread(i);
+#pragma unroll
+        for (int i = 0; i < 2 * kLatKS; ++i) {
+            const u32x4 cur = kf[i % kKA];
+            if (i + kKA < 2 * kLatKS) kf[i % kKA] = kread(i + kKA);
+            sa[i & 1] = mfma16x16x32(cur, qf[i >> 1], sa[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- logits in the log2 domain: rows 16 mt + 4 g + i of head L
+        const float *bia = s_bias + t * kTile + 4 * g;
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bia);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bia + 16);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = fmaf(sa[0][i], a.scale_log2, b0[i]);
+            x[4 + i] = fmaf(sa[1][i], a.scale_log2, b1[i]);
+        }
+        float m_tile = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        m_tile = fmaxf(m_tile, __shfl_xor(m_tile, 16, 64));
+        m_tile = max_xor32(m_tile);
+        const bool grow = m_tile > m_run + kRescale;
+        if (__any(grow)) {
+            const float m_new = grow ? m_tile : m_run;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int n = 0; n < kLatDT; ++n) o[n] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(x[e] - m_use);
+            l_run += p[e];
+        }
+        // P^T B operand: k = 8 g + e <-> the lane's own rows, in the order of the V reads below:
+        // e = 0..3 rows 4g, 4g+1, 16+4g, 16+4g+1; e = 4..7 the same plus 2
+        const u32x4 pb = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[4], p[5]),
+                               pack_bf16x2(p[2], p[3]), pack_bf16x2(p[6], p[7])};
+        // ---- O^T += V^T P^T. Transposing reads: input lane J of group g loads entries
+        //      [4 (J % 4), +4) of row R(J / 4), R(q) = 4 g + (q & 1) + 16 (q >> 1) (+ 2 for the
+        //      second read); output lane L then holds entry L of rows R(0) .. R(3). Chunk
+        //      2 n + (L % 4) / 2 = 8 (n / 4) + (2 (n % 4) + (L % 4) / 2): column group n / 4 is an
+        //      immediate offset, four bases per read row. Reads run kVA tiles ahead of their MFMA.
+        constexpr int kVA = 3;
+        uint32_t vbase[2][4];
+        {
+            const uint32_t l2 = opaque((uint32_t)l), L2 = l2 & 15u, g2 = l2 >> 4;
+            const int q = (int)(L2 >> 2);
+            const int vr1 = 4 * (int)g2 + (q & 1) + 16 * (q >> 1);
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+                for (int nq = 0; nq < 4; ++nq) {
+                    const int vr = vr1 + 2 * rd;
+                    vbase[rd][nq] = kb + (uint32_t)(128 * vr +
+                                                    16 * ((2 * nq + (int)((L2 & 3u) >> 1)) ^ swz(vr)) +
+                                                    8 * (int)(L2 & 1u));
+                }
+        }
+        auto vread = [&](int n) {
+            const uint32_t off = 4096u * (uint32_t)(n >> 2);
+            const u32x2 w0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                           (SA_LDS i16x4 *)(vbase[0][n & 3] + off)));
+            const u32x2 w1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                           (SA_LDS i16x4 *)(vbase[1][n & 3] + off)));
+            return u32x4{w0[0], w0[1], w1[0], w1[1]};
+        };
+        u32x4 vf[kVA];
+#pragma unroll
+        for (int n = 0; n < kVA; ++n) vf[n] = vread(n);
+#pragma unroll
+        for (int n = 0; n < kLatDT; ++n) {
+            const u32x4 cur = vf[n % kVA];
+            if (n + kVA < kLatDT) vf[n % kVA] = vread(n + kVA);
+            o[n] = mfma16x16x32(cur, pb, o[n]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the copies issued past the last tile land before this workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- epilogue: lane (g, L) holds entries 16 n + 4 g + i of head L
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot = sum_xor32(l_tot);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!a.merge_inside) {
+        if (live) {
+            uint16_t *orow = a.out + ((int64_t)row * a.heads_q + head) * kLatV;
+#pragma unroll
+            for (int n = 0; n < kLatDT; ++n)
+                *reinterpret_cast<u32x2 *>(orow + 16 * n + 4 * g) =
+                    u32x2{pack_bf16x2(o[n][0] * inv, o[n][1] * inv),
+                          pack_bf16x2(o[n][2] * inv, o[n][3] * inv)};
+        }
+        return;
+    }
+    // ---- split partials (agent scope, see st_agent_u64), then the row's barrier. A split's
+    //      partial output is a block of 8-byte units (four bf16), unit
+    //      u = ((w * 32 + n) * 4 + g) * 16 + L holding entries 16 n + 4 g .. + 3 of head
+    //      16 w + L: each store instruction of a wave writes 512 contiguous bytes.
+    const int hq16 = 16 * ((a.heads_q + 15) / 16);
+    const int64_t blk_elems = (int64_t)hq16 * kLatV;
+    if (live_wave) {
+        uint16_t *pblk = a.part_o + ((int64_t)row * a.splits + split) * blk_elems;
+#pragma unroll
+        for (int n = 0; n < kLatDT; ++n) {
+            const uint64_t v = (uint64_t)pack_bf16x2(o[n][0] * inv, o[n][1] * inv) |
+                               ((uint64_t)pack_bf16x2(o[n][2] * inv, o[n][3] * inv) << 32);
+            st_agent_u64(pblk + 4 * (((w * kLatDT + n) * 4 + g) * 16 + L), v);
+        }
+        if (g == 0 && live)
+            st_agent_u64(a.part_ml + 2 * (((int64_t)row * a.splits + split) * a.heads_q + head),
+                         (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_tot) << 32));
+    }
+    uint32_t *rs = a.row_sync + (int64_t)row * kRowSyncWords;
+    uint32_t nbar = 0;
+    const bool ok = group_barrier(&rs[0], (uint32_t)a.splits, a.err, nbar);
+    // ---- merge: split s combines the units [s U / S, (s + 1) U / S) of every split's block
+    //      (U = units per block), one unit per thread at a time, with the loads of up to 8 splits
+    //      in flight; consecutive threads read consecutive units
+    const int units = hq16 * kLatV / 4;
+    const int u0 = (int)((int64_t)units * split / a.splits);
+    const int u1 = (int)((int64_t)units * (split + 1) / a.splits);
+    constexpr int kMS = 8;  // splits whose loads are in flight together
+    if (ok) {
+        for (int u = u0 + tid; u < u1; u += kLatThreads) {
+            const int uw = u >> 11, un = (u >> 6) & 31, ug = (u >> 4) & 3, uL = u & 15;
+            const int hh = 16 * uw + uL;
+            if (hh >= a.heads_q) continue;
+            float M = -__builtin_inff(), Lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < a.splits; s0 += kMS) {
+                uint64_t ml[kMS], v[kMS];
+#pragma unroll
+                for (int x = 0; x < kMS; ++x) {
+                    const int64_t rs_ = (int64_t)row * a.splits + min(s0 + x, a.splits - 1);
+                    ml[x] = ld_agent_u64(a.part_ml + 2 * (rs_ * a.heads_q + hh));
+                    v[x] = ld_agent_u64(a.part_o + rs_ * blk_elems + 4 * (int64_t)u);
+                }
+#pragma unroll
+                for (int x = 0; x < kMS; ++x) {
+                    const float ms = __uint_as_float((uint32_t)ml[x]);
+                    const float ls = __uint_as_float((uint32_t)(ml[x] >> 32));
+                    if (s0 + x >= a.splits || !(ls > 0.f)) continue;
+                    const float mn = fmaxf(M, ms);
+                    const float c = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is summed
+                    const float wgt = __builtin_amdgcn_exp2f(ms - mn) * ls;
+                    Lsum = fmaf(Lsum, c, wgt);
+                    const uint32_t lo32 = (uint32_t)v[x], hi32 = (uint32_t)(v[x] >> 32);
+                    acc[0] = fmaf(acc[0], c, wgt * bf16_lo(lo32));
+                    acc[1] = fmaf(acc[1], c, wgt * bf16_hi(lo32));
+                    acc[2] = fmaf(acc[2], c, wgt * bf16_lo(hi32));
+                    acc[3] = fmaf(acc[3], c, wgt * bf16_hi(hi32));
+                    M = mn;
+                }
+            }
+            const float il = Lsum > 0.f ? 1.f / Lsum : 0.f;
+            *reinterpret_cast<u32x2 *>(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug) =
+                u32x2{pack_bf16x2(acc[0] * il, acc[1] * il), pack_bf16x2(acc[2] * il, acc[3] * il)};
+        }
+    } else if (tid == 0) {
+        __hip_atomic_fetch_or(&rs[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // ---- leave: the last split to leave (all others have written everything) resets the
+    //      record; if any split's wait expired, it also zeroes the row's whole output, so a
+    //      failed call leaves a defined result (zeros, with bit 0 of the error word set)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&rs[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_leave = prev == (uint32_t)a.splits - 1 ? 1 + (int)ld_agent(&rs[2]) : 0;
+    }
+    __syncthreads();
+    if (s_leave == 2) {  // last to leave, after a failure
+        uint16_t *orow = a.out + (int64_t)row * a.heads_q * kLatV;
+        for (int i = tid; i < a.heads_q * kLatV / 8; i += kLatThreads)
+            *reinterpret_cast<u32x4 *>(orow + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (s_leave >= 1 && tid == 0) {
+        st_agent(&rs[0], 0u);
+        st_agent(&rs[1], 0u);
+        st_agent(&rs[2], 0u);
+    }
+}
+
+size_t attn_latent_lds(int split_len) {
+    return (size_t)kLatRing * kLatTileB + (size_t)split_len * 8;
+}
+
+hipError_t launch_attn_latent(const AttnArgs &a, hipStream_t st) {
+    const size_t lds = attn_latent_lds(a.split_len);
+    static std::atomic<int> granted{-1};
+    hipError_t e = hipSuccess;
+    if ((int)lds > granted.load(std::memory_order_relaxed)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_latent),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        granted.store((int)lds, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(k_attn_latent, dim3((unsigned)lat_grid(a.rows, a.splits, a.merge_inside)),
+                       dim3(kLatThreads), lds, st, a);
+    return hipGetLastError();
+}
+
+int lat_grid_host(int rows, int splits, int merge) { return lat_grid(rows, splits, merge); }
+
+int attn_latent_occupancy(int split_len) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(&k_attn_latent),
+                                                     kLatThreads, attn_latent_lds(split_len)) != hipSuccess)
+        return -1;
+    return occ;
 }
 
 template <int DQK, int DV, bool SEPV, bool FP8, bool T128 = false>

@@ -289,6 +289,29 @@ __device__ __forceinline__ void st_agent64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane j's
+// bytes land at LDS byte address lds_base + 16 j; lds_base must be the same in every lane.
+// Written as inline asm on purpose: for the builtin the compiler treats every later LDS read as
+// dependent on all copies in flight (it waits for vmcnt(0)), which leaves one tile in flight.
+// Callers wait for their own copies with an explicit s_waitcnt vmcnt and keep no other
+// vector-memory operation in flight meanwhile (the compiler does not count these copies).
+// The copy has no destination register, so no register is written after the asm returns.
+__device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+                 : "memory");
+}
+
+// 8-byte store / load at agent scope: performed at the device's coherence point, so data
+// exchanged between workgroups on different XCDs (whose L2 caches are not coherent) is seen
+// by the reader once the writer's arrival at a group_barrier has been observed.
+__device__ __forceinline__ void st_agent_u64(void *p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent_u64(const void *p) {
+    return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // 16-byte global load that the compiler keeps as one dwordx4.
 __device__ __forceinline__ u32x4 ldg16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);

@@ -108,7 +108,18 @@ struct AttnArgs {
     uint16_t *out;      // bf16 [rows][heads_q][dv] (splits == 1)
     uint16_t *part_o;   // bf16 [rows][splits][heads_q][dv], normalised per split (splits > 1)
     float *part_ml;     // [rows][splits][heads_q][2]
+    // latent-row kernel with the split merge inside: per query row a record of kRowSyncWords
+    // words (arrival counter, leave counter, failure flag), zero between launches
+    uint32_t *row_sync;
+    uint32_t *err;
+    int merge_inside;   // > 0: the splits of a row meet at a barrier and merge in the same launch
+                        // (1: row-major grid, 2: splits of a row on one XCD)
 };
+constexpr int kRowSyncWords = 16;
+// latent-row kernel (bf16 576/512 rows, up to 128 query heads)
+hipError_t launch_attn_latent(const AttnArgs &a, hipStream_t st);
+int attn_latent_occupancy(int split_len);
+int lat_grid_host(int rows, int splits, int merge);
 
 // key_fmt: 0 bf16, 1 E4M3 with a row scale, 2 MXFP8 (the values of sa_dtype)
 hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, int key_fmt, int rows,
