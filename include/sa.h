@@ -214,6 +214,32 @@ sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_k
                          size_t workspace_bytes, void *stream);
 
 /*
+ * sa_decode_step_noalloc -- sa_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and results, with the workspace taken from a fixed scratch array inside the library
+ * instead of a caller's buffer. Neither this call nor the kernels it launches allocate (no
+ * hipMalloc, hipFree or allocating library routine).
+ *  - Scratch: 48 MiB of device memory on every device the library runs on (a file-scope device
+ *    array), held until the process ends. Limits: num_seqs <= 64, and the call's workspace,
+ *    laid out with its records sized for 64 sequences, must fit in 48 MiB (with k = 2048 and
+ *    128 query heads over 576/512 latent rows, every batch of up to 64 sequences does). A
+ *    larger call returns SA_ERR_UNSUPPORTED and enqueues nothing.
+ *  - Every call on a device shares that device's scratch, which keeps the last call's contents:
+ *    calls that overlap on one device (on different streams, or from threads without ordering
+ *    between them) race, and their results are undefined. Order them on one stream.
+ *  - The first call on a device (the caller's current device, which must be the stream's) looks
+ *    the scratch up and enqueues one zero fill of it on `stream` (a kernel, no memset).
+ *  - error_out: device int32, or NULL. Once the call's kernels are done it receives the call's
+ *    device error word (as sa_workspace_error reports it for a workspace), which is then
+ *    cleared for the next call.
+ * Other arguments as sa_decode_step.
+ */
+sa_status sa_decode_step_noalloc(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                                 const void *q_idx, const float *w, const void *q, int32_t k,
+                                 int32_t block_k, int32_t *idx_out, void *out,
+                                 int32_t *error_out, void *stream);
+
+/*
  * sa_cache_append -- the cache writes of the step just before the path: every new token's
  * indexer key and KV row go into the paged caches at their slots, quantized into the caches'
  * formats, and the summary of every block that received a token is recomputed ([SameDay] §3.1:

@@ -53,7 +53,7 @@ class sa_kv(C.Structure):
 
 _lib = None
 EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-           "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_prolog_workspace_size",
+           "sa_decode_step", "sa_decode_step_noalloc", "sa_cache_append", "sa_indexer_prolog", "sa_prolog_workspace_size",
            "sa_workspace_size", "sa_pool_create", "sa_pool_destroy", "sa_pool_stats", "sa_seq_new",
            "sa_seq_fork", "sa_seq_reserve", "sa_seq_free", "sa_seq_len", "sa_seq_page_table",
            "sa_pool_refcount", "sa_copy_pages",
@@ -77,6 +77,7 @@ def load(path: str = LIB_PATH):
     lib.sa_index_select.argtypes = [pb, pi, P, P, i32, i32, P, P, sz, P]
     lib.sa_block_select.argtypes = [pb, pi, P, P, i32, P, P, sz, P]
     lib.sa_decode_step.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, sz, P]
+    lib.sa_decode_step_noalloc.argtypes = [pb, pi, pk, P, P, P, i32, i32, P, P, P, P]
     lib.sa_cache_append.argtypes = [pb, pi, pk, P, P, P, P]
     lib.sa_indexer_prolog.argtypes = [C.POINTER(sa_prolog), i32, P, P, P, P, P, P, sz, P]
     lib.sa_prolog_workspace_size.argtypes = [C.POINTER(sa_prolog), i32]
@@ -107,7 +108,7 @@ def load(path: str = LIB_PATH):
     lib.sa_last_error.restype = C.c_char_p
     lib.sa_version.restype = i32
     for fn in ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa_block_select",
-               "sa_decode_step", "sa_cache_append", "sa_indexer_prolog", "sa_workspace_init",
+               "sa_decode_step", "sa_decode_step_noalloc", "sa_cache_append", "sa_indexer_prolog", "sa_workspace_init",
                "sa_workspace_error"):
         getattr(lib, fn).restype = C.c_int
     _lib = lib
@@ -238,6 +239,15 @@ def decode_step(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, ou
     _check(load().sa_decode_step(C.byref(batch.s), C.byref(ix), C.byref(kv), _ptr(q_idx),
                                  _ptr(w), _ptr(q), k, block_k, _ptr(idx_out), _ptr(out),
                                  _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def decode_step_noalloc(batch: Batch, ix: sa_indexer, kv: sa_kv, q_idx, w, q, k: int, out,
+                        block_k: int = 0, idx_out=None, error_out=None, stream=None) -> None:
+    """sa_decode_step with the library's fixed scratch instead of a workspace; ``error_out`` (a
+    device int32 tensor, or None) receives the call's device error word."""
+    _check(load().sa_decode_step_noalloc(C.byref(batch.s), C.byref(ix), C.byref(kv), _ptr(q_idx),
+                                         _ptr(w), _ptr(q), k, block_k, _ptr(idx_out), _ptr(out),
+                                         _ptr(error_out), _stream(stream)))
 
 
 def cache_append(batch: Batch, ix: sa_indexer | None, kv: sa_kv | None, k_idx_new=None,

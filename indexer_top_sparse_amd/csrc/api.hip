@@ -152,9 +152,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WsLayout {
     size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, slots = 0, part_o = 0, part_ml = 0,
            rsync = 0, total = 0;
+    int row_recs = 0;  // per-row merge records at rsync
 };
 
-WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int block_k) {
+// The regions that must hold zeros when a call starts (error word, zero row, selection and merge
+// records; every launch returns its records to zero) come first, the per-call data after them.
+// seq_records / row_records >= 0 size the record regions for a fixed capacity instead of this
+// batch, so that they sit at the same offsets whatever the call's shapes (the fixed scratch of
+// sa_decode_step_noalloc).
+WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int block_k,
+                   int seq_records = -1, int row_records = -1) {
     WsLayout L;
     size_t off = 0;
     L.err = off;
@@ -162,7 +169,15 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
     L.zero = off;  // stays zero: source of empty gathered rows
     off += 2048;
     L.sync = off;
-    off = align256(off + sizeof(SelSync) * (size_t)b->num_seqs);
+    const int nsr = seq_records >= 0 ? seq_records : b->num_seqs;
+    off = align256(off + sizeof(SelSync) * (size_t)nsr);
+    const int rmax = std::max(rows, b->num_seqs);
+    if (kv || row_records >= 0) {
+        L.rsync = off;  // per-row merge records (rows of a merge launch fit the device)
+        const int nrr = row_records >= 0 ? row_records : std::min(rmax, 4096);
+        L.row_recs = nrr;
+        off = align256(off + sizeof(uint32_t) * kRowSyncWords * (size_t)nrr);
+    }
     L.blocks = off;
     off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(block_k, 0));
     L.idx = off;
@@ -170,7 +185,6 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
     if (kv) {
         L.slots = off;  // physical rows of the fused step's index set
         off = align256(off + sizeof(int32_t) * (size_t)b->num_seqs * (size_t)std::max(k, 0));
-        const int rmax = std::max(rows, b->num_seqs);
         // the split count only grows as rows shrink; size for the larger of the two, for
         // either kernel
         int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
@@ -181,8 +195,6 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
         off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * (16 * ((kv->heads_q + 15) / 16)) * kv->dim_v);
         L.part_ml = off;
         off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * kv->heads_q);
-        L.rsync = off;  // per-row merge records (rows of a merge launch fit the device)
-        off = align256(off + sizeof(uint32_t) * kRowSyncWords * (size_t)std::min(rmax, 4096));
     }
     L.total = off;
     return L;
@@ -358,16 +370,16 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     if (latent_shape(kv)) {
         // the splits of a row wait for each other, so a merging grid must fit the device's
         // resident capacity (one workgroup per CU: the tile ring takes most of the LDS)
-        static int occ = 0;
-        if (occ == 0) occ = attn_latent_occupancy(kMaxSplitRows);
+        static const int occ = attn_latent_occupancy(kMaxSplitRows);
         const int cap = std::max(occ, 0) * device_cus();
         AttnPlan p = latent_plan(rows, k, 1 << 30);
-        while (p.merge && lat_grid_host(rows, p.splits, p.merge) > cap) {
+        // (and a merging launch needs one record per row)
+        while (p.merge && (lat_grid_host(rows, p.splits, p.merge) > cap || rows > L.row_recs)) {
             const AttnPlan q2 = latent_plan(rows, k, p.splits - 1);
             if (q2.splits >= p.splits) break;
             p = q2;
         }
-        if (!p.merge || lat_grid_host(rows, p.splits, p.merge) <= cap) {
+        if (!p.merge || (lat_grid_host(rows, p.splits, p.merge) <= cap && rows <= L.row_recs)) {
             a.splits = p.splits;
             a.split_len = split_len(k, p.splits);
             a.merge_inside = p.merge;
@@ -380,6 +392,49 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     hipError_t e = launch_sparse_attn(a, kv->dim_qk, kv->dim_v, kv->v != nullptr,
                                       (int)kv->dtype, st);
     if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    return SA_OK;
+}
+
+// ------------------------------------------------------------ fixed scratch (no allocation)
+// sa_decode_step_noalloc keeps its workspace in this array instead of a caller's buffer; every
+// device the library runs on holds its own copy until the process ends. In host code the
+// array's name is only a stand-in: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+constexpr int kScratchSeqs = 64;    // sequences per call: the selection records at fixed offsets
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Hands the call's device error word to the caller (error_out may be null) and clears it.
+__global__ void k_take_error(uint32_t *err, int32_t *error_out) {
+    if (threadIdx.x == 0) {
+        const uint32_t v = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (error_out) *error_out = (int32_t)v;
+        __hip_atomic_store(err, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+std::mutex g_scratch_mu;
+uint8_t *g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch. The first call on a device looks it up and
+// enqueues one zero fill (a kernel, not a memset) on `st`, ahead of the call's own kernels.
+sa_status scratch_of_current_device(hipStream_t st, uint8_t **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "device ordinal beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return hip_fail(hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        e = launch_zero(ptr, kScratchBytes, st);
+        if (e != hipSuccess) return hip_fail(e, "scratch zero fill");
+        g_scratch[dev] = static_cast<uint8_t *>(ptr);
+    }
+    *out = g_scratch[dev];
     return SA_OK;
 }
 
@@ -581,6 +636,39 @@ sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_k
     if ((st = select_impl(batch, rp, ix, q_idx, w, k, block_k, idx, slots, wsb, L, hs)) != SA_OK)
         return st;
     return run_attn(batch, rp.rows, kv, q, idx, slots, k, out, wsb, L, hs);
+}
+
+sa_status sa_decode_step_noalloc(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,
+                                 const void *q_idx, const float *w, const void *q, int32_t k,
+                                 int32_t block_k, int32_t *idx_out, void *out,
+                                 int32_t *error_out, void *stream) {
+    RowPlan rp;
+    sa_status st = check_select(batch, &rp, ix, q_idx, w, k, block_k);
+    if (st != SA_OK) return st;
+    if ((st = check_kv(kv)) != SA_OK) return st;
+    if (!q || !aligned16(q) || !out || (reinterpret_cast<uintptr_t>(out) & 7u))
+        return fail(SA_ERR_INVALID, "q (16-byte aligned) and out (8-byte aligned) are required");
+    if (batch->num_seqs > kScratchSeqs)
+        return fail(SA_ERR_UNSUPPORTED, "sa_decode_step_noalloc: more than 64 sequences");
+    // the records at fixed offsets: selection records for kScratchSeqs sequences, merge records
+    // for as many rows (decode has one row per sequence)
+    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k, kScratchSeqs, kScratchSeqs);
+    if (L.total > kScratchBytes)
+        return fail(SA_ERR_UNSUPPORTED, "sa_decode_step_noalloc: the call needs more than the 48 MiB scratch "
+                                        "(fewer sequences or a smaller k)");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint8_t *wsb = nullptr;
+    if ((st = scratch_of_current_device(hs, &wsb)) != SA_OK) return st;
+    int32_t *idx = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
+    int32_t *slots = reinterpret_cast<int32_t *>(wsb + L.slots);
+    if ((st = select_impl(batch, rp, ix, q_idx, w, k, block_k, idx, slots, wsb, L, hs)) != SA_OK)
+        return st;
+    if ((st = run_attn(batch, rp.rows, kv, q, idx, slots, k, out, wsb, L, hs)) != SA_OK) return st;
+    hipLaunchKernelGGL(k_take_error, dim3(1), dim3(64), 0, hs, reinterpret_cast<uint32_t *>(wsb + L.err),
+                       error_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "error word launch");
+    return SA_OK;
 }
 
 sa_status sa_cache_append(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,

@@ -179,3 +179,24 @@ def test_prolog_validation(lib):
     assert prolog(ws=100) == B.SA_ERR_WORKSPACE
     p = B.sa_prolog(4, 64, 128, 7168, 0, 0, 0, 0, 0, 1e-6)
     assert lib.sa_prolog_workspace_size(C.byref(p), 3) == 4 * 3 * (64 + 4) * 14
+
+
+def _decode_noalloc(lib, a, k=2048):
+    P = C.c_void_p
+    return lib.sa_decode_step_noalloc(C.byref(a.batch.s), C.byref(a.ix), C.byref(a.kv),
+                                      P(a.keys.data_ptr()), P(a.keys.data_ptr()),
+                                      P(a.kvc.data_ptr()), k, 0, None, P(a.kvc.data_ptr()), None,
+                                      None)
+
+
+def test_noalloc_limits_are_checked_on_the_host(lib):
+    """The fixed-scratch decode step refuses calls beyond its scratch before any device call."""
+    a = _FakeDev(B_=65, ctx=[7] * 65)
+    assert _decode_noalloc(lib, a) == B.SA_ERR_UNSUPPORTED
+    assert b"64 sequences" in lib.sa_last_error()
+    # 64 sequences with k = 65536 need far more than 48 MiB of partials and index sets
+    a = _FakeDev(B_=64, ctx=[7] * 64)
+    assert _decode_noalloc(lib, a, k=65536) == B.SA_ERR_UNSUPPORTED
+    assert b"48 MiB" in lib.sa_last_error()
+    # argument checks come first, as for sa_decode_step
+    assert _decode_noalloc(lib, a, k=0) == B.SA_ERR_INVALID
