@@ -35,7 +35,21 @@
  *    q_len_b tokens (appended causally); row j of b sits at position
  *    ctx_len_b - q_len_b + (j - q_indptr[b]) and sees positions 0..that position inclusive.
  *    With q_indptr == NULL every sequence has exactly one row (decode) at ctx_len_b - 1.
- *  - Calls are re-entrant; calls sharing one workspace must be ordered on one stream.
+ *  - Re-entrancy: the library's only state is a per-thread error message, per-kernel launch
+ *    settings, and the per-device scratch of sa_decode_step_noalloc. Calls from several host
+ *    threads are safe; calls sharing one workspace (or the scratch) must be ordered on one
+ *    stream.
+ *  - Co-residency: the fused selection (sa_index_select, sa_block_select, sa_decode_step) and
+ *    the latent-row attention with its split merge (bf16 576/512 rows in sa_sparse_attn and
+ *    sa_decode_step) have workgroups of one launch wait for each other. The host sizes those
+ *    grids to what the device holds at once, assuming the launch has the device to itself;
+ *    kernels running at the same time (other streams, other processes) can hold compute units
+ *    and keep some workgroups from starting. Every such wait is bounded (2^20 polls, about a
+ *    second; the environment variable SA_SPIN_LIMIT, read per call, overrides the count). When
+ *    one expires, the call still ends with a defined result: every sequence whose selection
+ *    waited too long gets index -1 in every slot (and so output 0), every attention row whose
+ *    split barrier expired gets output 0, and bit 0 of the workspace error word is set
+ *    (sa_workspace_error). The workspace is left ready for the next call.
  */
 #ifndef SA_H_
 #define SA_H_
@@ -363,7 +377,9 @@ size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int3
 sa_status sa_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronizes `stream` and reads the workspace's device error word: 0 = no device-side
- * failure, otherwise a bitmask (1 = a cross-workgroup wait exceeded its spin limit). */
+ * failure, otherwise a bitmask (1 = a cross-workgroup wait exceeded its spin limit; the
+ * affected results are the defined failure results described under co-residency above). The
+ * word is sticky: it keeps its bits until the workspace is initialised again. */
 sa_status sa_workspace_error(const void *workspace, int32_t *error_host, void *stream);
 
 const char *sa_status_string(sa_status status);

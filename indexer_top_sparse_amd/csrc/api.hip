@@ -238,6 +238,15 @@ int occupancy(void *kern, int threads, size_t lds) {
     return occ;
 }
 
+// Polls of a cross-workgroup wait: kSpinLimit, or SA_SPIN_LIMIT when set (read per call).
+uint32_t spin_limit() {
+    const char *e = std::getenv("SA_SPIN_LIMIT");
+    if (!e || !*e) return kSpinLimit;
+    char *end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    return (end && *end == 0 && v <= 0xFFFFFFFFul) ? (uint32_t)v : kSpinLimit;
+}
+
 int ncand_host(int mode, int ctx, int page_size, int block_k) {
     if (mode == 0) return ctx;
     const int nblk = (ctx + page_size - 1) / page_size;
@@ -304,7 +313,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
             if (o >= occ) break;
             occ = o;
         }
-        SelectArgs a;
+        SelectArgs a{};
         a.num_seqs = nb;
         a.lp = lp;
         a.pages_per_seq = b->pages_per_seq;
@@ -324,6 +333,7 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         a.slots_out = slots_out ? slots_out + (int64_t)s0 * k : nullptr;
         a.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
         a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+        a.spin_limit = spin_limit();
         // The grid never exceeds what the device holds at once, so every workgroup becomes
         // resident once the work queued before it has drained, and the waits between
         // workgroups of a sequence end; the waits are also spin-bounded. A plain launch is
@@ -365,6 +375,7 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     a.part_ml = reinterpret_cast<float *>(ws + L.part_ml);
     a.row_sync = reinterpret_cast<uint32_t *>(ws + L.rsync);
     a.err = reinterpret_cast<uint32_t *>(ws + L.err);
+    a.spin_limit = spin_limit();
     a.merge_inside = 0;
     if (rows == 0) return SA_OK;
     if (latent_shape(kv)) {

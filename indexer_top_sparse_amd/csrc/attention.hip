@@ -705,7 +705,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     }
     uint32_t *rs = a.row_sync + (int64_t)row * kRowSyncWords;
     uint32_t nbar = 0;
-    const bool ok = group_barrier(&rs[0], (uint32_t)a.splits, a.err, nbar);
+    const bool ok = group_barrier(&rs[0], (uint32_t)a.splits, a.err, nbar, a.spin_limit);
     // ---- merge: split s combines the units [s U / S, (s + 1) U / S) of every split's block
     //      (U = units per block), one unit per thread at a time, with the loads of up to 8 splits
     //      in flight; consecutive threads read consecutive units
@@ -745,8 +745,10 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
                 }
             }
             const float il = Lsum > 0.f ? 1.f / Lsum : 0.f;
-            *reinterpret_cast<u32x2 *>(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug) =
-                u32x2{pack_bf16x2(acc[0] * il, acc[1] * il), pack_bf16x2(acc[2] * il, acc[3] * il)};
+            // agent scope: a failure fill by the row's last split to leave lands after it
+            st_agent_u64(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug,
+                         (uint64_t)pack_bf16x2(acc[0] * il, acc[1] * il) |
+                             ((uint64_t)pack_bf16x2(acc[2] * il, acc[3] * il) << 32));
         }
     } else if (tid == 0) {
         __hip_atomic_fetch_or(&rs[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -763,8 +765,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     __syncthreads();
     if (s_leave == 2) {  // last to leave, after a failure
         uint16_t *orow = a.out + (int64_t)row * a.heads_q * kLatV;
-        for (int i = tid; i < a.heads_q * kLatV / 8; i += kLatThreads)
-            *reinterpret_cast<u32x4 *>(orow + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+        for (int i = tid; i < a.heads_q * kLatV / 4; i += kLatThreads) st_agent_u64(orow + 4 * i, 0ull);
     }
     if (s_leave >= 1 && tid == 0) {
         st_agent(&rs[0], 0u);

@@ -226,13 +226,13 @@ __device__ __forceinline__ void full_barrier() {
 // `count` only grows during a launch: the j-th barrier (j = 1, 2, ...) of a group of n
 // workgroups is passed once count reaches j n, so the last arrival itself releases the others
 // (no reset and no second atomic on the way). `j` is the caller's barrier number, advanced
-// here; only thread 0's copy is used. group_leave returns count to 0 for the next launch.
-// A bounded spin keeps every wave finite: on expiry bit 0 of *err is set and the call returns
-// false (results of that launch are then undefined, and the host can read the flag).
-constexpr uint32_t kSpinLimit = 1u << 20;
-
+// here; only thread 0's copy is used. The caller's leave step returns count to 0 for the next
+// launch (the last of the n workgroups to leave does it).
+// A bounded spin keeps every wave finite: after spin_limit polls bit 0 of *err is set and the
+// call returns false. The caller then marks its group as failed, and the group's last workgroup
+// to leave writes a defined failure result.
 __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t n, uint32_t *err,
-                                              uint32_t &j) {
+                                              uint32_t &j, uint32_t spin_limit) {
     __shared__ int s_ok;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's atomics and stores have been performed
     __syncthreads();
@@ -246,7 +246,7 @@ __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t n, uint3
             uint32_t spins = 0;
             while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
                 __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
+                if (++spins > spin_limit) {
                     __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     ok = 0;
                     break;
@@ -258,16 +258,6 @@ __device__ __forceinline__ bool group_barrier(uint32_t *count, uint32_t n, uint3
     }
     __syncthreads();
     return s_ok != 0;
-}
-
-// After a workgroup's last barrier of the launch: the last of the n to leave (every other one
-// has passed all its barriers, so nobody reads `count` any more) returns both counters to 0.
-__device__ __forceinline__ void group_leave(uint32_t *count, uint32_t *left, uint32_t n) {
-    if (threadIdx.x == 0 &&
-        __hip_atomic_fetch_add(left, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1) {
-        __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(left, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
 }
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {

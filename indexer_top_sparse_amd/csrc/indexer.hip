@@ -840,7 +840,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             if (pass == 0) s_base[i] = c ? fetch_add_agent(&gh[i], c) : 0u;
             else if (c) add_agent(&gh[i], c);
         }
-        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar, a.spin_limit) && ok;
         // suffix scan of the global histogram: thread t owns bins [nb - 4(t+1), nb - 4t). In
         // pass 0 the same scan runs over this workgroup's own histogram, which gives its count
         // above the threshold bin.
@@ -862,7 +862,12 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             need = min((uint32_t)a.k, tot);
         }
         if (need == 0u) break;
-        if (tid == 0) sh.res[3] = 0xFFFFFFFFu;
+        if (tid == 0) {
+            sh.res[3] = 0xFFFFFFFFu;
+            sh.res[4] = 0u;
+            sh.res[5] = 0u;
+            sh.res[6] = 0u;
+        }
         __syncthreads();
         uint32_t run = above0, lrun = labove0;
 #pragma unroll
@@ -877,7 +882,11 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             lrun += lv[j];
         }
         __syncthreads();
-        const uint32_t T = sh.res[3];
+        uint32_t T = sh.res[3];
+        if (T >= (uint32_t)nb) {  // no threshold bin: only after an expired wait (partial counts)
+            T = 0u;
+            ok = false;
+        }
         need -= sh.res[4];
         prefix = (prefix << bits) | T;
         pbits += bits;
@@ -940,14 +949,19 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                         const uint32_t below = __builtin_amdgcn_mbcnt_hi(
                             (uint32_t)(m[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[u], 0u));
                         const int i = r0 + u * kSelThreads + tid;
-                        st_agent64(&ss->list[lbase + woff + below],
-                                   ((uint64_t)kk[u] << 32) | (uint32_t)~(uint32_t)(c0 + i));
+                        // below kListCap whenever every workgroup's counts are in (the bin holds
+                        // at most kListCap); the test keeps a workgroup whose wait expired, and
+                        // which saw only part of the histogram, inside the list
+                        const uint32_t slot = lbase + woff + below;
+                        if (slot < (uint32_t)kListCap)
+                            st_agent64(&ss->list[slot],
+                                       ((uint64_t)kk[u] << 32) | (uint32_t)~(uint32_t)(c0 + i));
                     }
                     woff += (uint32_t)__popcll(m[u]);
                 }
             }
         }
-        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar, a.spin_limit) && ok;
         // the list (at most kListCap entries) stays in registers: thread tid holds entries
         // tid + kSelThreads r; 0 marks an empty slot (list keys are never 0). All loads are
         // issued before the first is used.
@@ -993,7 +1007,11 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             }
             uint32_t tot;
             const uint32_t abv = block_excl_scan<kSelThreads>(csum, sh.scan, &tot);
-            if (tid == 0) sh.res[3] = 0xFFFFFFFFu;
+            if (tid == 0) {
+                sh.res[3] = 0xFFFFFFFFu;
+                sh.res[4] = 0u;
+                sh.res[5] = 0u;
+            }
             __syncthreads();
             uint32_t run = abv;
 #pragma unroll
@@ -1007,9 +1025,14 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             }
             __syncthreads();
             lneed -= sh.res[4];
-            pre = (pre << bits) | sh.res[3];
+            // (no bin found: only on partial counts, see below)
+            const uint32_t tb = sh.res[3] < (uint32_t)nb ? sh.res[3] : 0u;
+            pre = (pre << bits) | tb;
             pb += bits;
-            const bool whole = sh.res[5] == lneed;  // always true once all 64 bits are used
+            // with complete counts the bin holds exactly what is still needed once all 64 bits
+            // are used (composites are distinct); the bound on pb also ends the loop for a
+            // workgroup whose wait expired and which works on partial counts
+            const bool whole = sh.res[5] == lneed || pb >= 64;
             __syncthreads();
             if (whole) break;
         }
@@ -1067,8 +1090,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 int64_t row;
                 cr.cand(s, c0 + b + u, c0, a.lp, pos, row);
                 if (dst < (uint32_t)K) {
-                    out[dst] = pos;
-                    if (slots) slots[dst] = (int32_t)row;
+                    st_agent(reinterpret_cast<uint32_t *>(out) + dst, (uint32_t)pos);
+                    if (slots) st_agent(reinterpret_cast<uint32_t *>(slots) + dst, (uint32_t)row);
                 }
                 ++dst;
             }
@@ -1101,7 +1124,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             st_agent(&ss->cnt[chunk][0], A);
             st_agent(&ss->cnt[chunk][1], Eq);
         }
-        ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
+        ok = group_barrier(&ss->count, G, a.err, nbar, a.spin_limit) && ok;
         // prefix over the earlier workgroups of this sequence (chunk order = position order);
         // G <= kSelThreads, so thread h reads the record of workgroup h
         uint32_t Ah = 0, Eh = 0;
@@ -1154,8 +1177,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                     int64_t row;
                     cr.cand(s, c0 + i, c0, a.lp, pos, row);
                     if (dst < (uint32_t)K) {
-                        out[dst] = pos;
-                        if (slots) slots[dst] = (int32_t)row;
+                        st_agent(reinterpret_cast<uint32_t *>(out) + dst, (uint32_t)pos);
+                        if (slots) st_agent(reinterpret_cast<uint32_t *>(slots) + dst, (uint32_t)row);
                     }
                     ++dst;
                 }
@@ -1164,8 +1187,8 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     }
     if (chunk == G - 1)
         for (int j = (int)k_eff + tid; j < K; j += kSelThreads) {
-            out[j] = -1;
-            if (slots) slots[j] = -1;
+            st_agent(reinterpret_cast<uint32_t *>(out) + j, 0xFFFFFFFFu);
+            if (slots) st_agent(reinterpret_cast<uint32_t *>(slots) + j, 0xFFFFFFFFu);
         }
 
     // ---- leave the histograms zeroed for the next launch (the list path cleared its one
@@ -1173,12 +1196,39 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     //      that barrier (nothing to select) one more barrier separates the last reads from
     //      the clearing.
     if (!(k_eff > 0 && listn > 0)) {
-        if (k_eff == 0) ok = group_barrier(&ss->count, G, a.err, nbar) && ok;
+        if (k_eff == 0) ok = group_barrier(&ss->count, G, a.err, nbar, a.spin_limit) && ok;
         for (int i = chunk * kSelThreads + tid; i < 3 * kHistBins; i += G * kSelThreads)
             st_agent(&ss->hist[0][0] + i, 0u);
     }
-    group_leave(&ss->count, &ss->left, G);
-    (void)ok;
+
+    // ---- leave. A wait that expired (the workgroups of the launch were not all resident at
+    //      once, e.g. because other kernels held compute units) leaves the sequence's selection
+    //      undefined: the last workgroup to leave, which every other one has left before with
+    //      all its stores performed, then writes the defined failure result (every index -1;
+    //      bit 0 of the error word is already set) and clears all three histograms, since a
+    //      late workgroup may have added to them after the others cleared their slices. It
+    //      also returns the record's counters and flag to zero.
+    if (!ok && tid == 0) __hip_atomic_fetch_or(&ss->fail, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = fetch_add_agent(&ss->left, 1u);
+        sh.res[0] = prev == (uint32_t)G - 1u ? 1u + (ld_agent(&ss->fail) != 0u ? 1u : 0u) : 0u;
+    }
+    __syncthreads();
+    const uint32_t leave = sh.res[0];
+    if (leave == 2u) {
+        for (int j = tid; j < K; j += kSelThreads) {
+            st_agent(reinterpret_cast<uint32_t *>(out) + j, 0xFFFFFFFFu);
+            if (slots) st_agent(reinterpret_cast<uint32_t *>(slots) + j, 0xFFFFFFFFu);
+        }
+        for (int i = tid; i < 3 * kHistBins; i += kSelThreads) st_agent(&ss->hist[0][0] + i, 0u);
+    }
+    if (leave >= 1u && tid == 0) {
+        st_agent(&ss->count, 0u);
+        st_agent(&ss->left, 0u);
+        st_agent(&ss->fail, 0u);
+    }
 }
 
 // ------------------------------------------------------------------ launchers

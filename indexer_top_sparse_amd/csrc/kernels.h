@@ -7,17 +7,24 @@
 
 namespace sa {
 
+// Polls of a cross-workgroup wait before it expires (about a second of waiting); the
+// environment variable SA_SPIN_LIMIT overrides it per call, so that tests can drive the
+// failure path with every kernel still ending normally.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
 constexpr int kMaxGroupsPerSeq = 512;  // workgroups sharing one sequence in a selection
 constexpr int kSelMaxChunk = 32768;     // candidates of one selection workgroup (128 KiB of keys)
 
-// Per-sequence record in the workspace used by the cross-workgroup selection. The counters and
-// the histograms return to zero by the end of every launch.
+// Per-sequence record in the workspace used by the cross-workgroup selection. The counters, the
+// failure flag and the histograms return to zero by the end of every launch, also when a wait
+// expired.
 constexpr int kListCap = 4096;  // threshold-bin candidates resolved through the list
 
 struct SelSync {
     uint32_t count;   // barrier arrivals in the current launch (0 between launches)
     uint32_t left;    // workgroups past their last barrier (0 between launches)
-    uint32_t pad[62];
+    uint32_t fail;    // set when a wait of this launch expired (0 between launches)
+    uint32_t pad[61];
     uint32_t hist[3][2048];
     uint32_t cnt[kMaxGroupsPerSeq][2];
     uint64_t list[kListCap];  // (key << 32 | ~candidate) of the threshold bin's candidates
@@ -80,6 +87,7 @@ struct SelectArgs {
     int32_t *slots_out;  // [num_seqs][k] physical rows of the selected positions, or null
     SelSync *sync;
     uint32_t *err;
+    uint32_t spin_limit;  // polls of a cross-workgroup wait before it expires
 };
 
 struct TopkArgs {
@@ -112,6 +120,7 @@ struct AttnArgs {
     // words (arrival counter, leave counter, failure flag), zero between launches
     uint32_t *row_sync;
     uint32_t *err;
+    uint32_t spin_limit;  // polls of the split barrier before it expires
     int merge_inside;   // > 0: the splits of a row meet at a barrier and merge in the same launch
                         // (1: row-major grid, 2: splits of a row on one XCD)
 };
