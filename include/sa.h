@@ -382,6 +382,34 @@ sa_status sa_workspace_init(void *workspace, size_t workspace_bytes, void *strea
  * word is sticky: it keeps its bits until the workspace is initialised again. */
 sa_status sa_workspace_error(const void *workspace, int32_t *error_host, void *stream);
 
+/*
+ * Launch planning, host only (no device call): the capacity arithmetic that the calls above
+ * use to size grids whose workgroups wait for each other, exposed for inspection and tests.
+ *
+ * sa_plan_selection -- one launch of the fused selection. Sequence s has ncand[s] candidates
+ * (its visible tokens, blocks, or kept-block tokens); `capacity` is the number of selection
+ * workgroups the device holds at once (workgroups per CU x CUs). Writes the chunk (candidates
+ * per workgroup: the smallest multiple of 64 for which every sequence needs at most 512
+ * workgroups, ceil(ncand / chunk) or 1 when empty, and all of them together fit in `capacity`)
+ * and the launch's workgroup count. SA_ERR_INVALID for NULL pointers, num_seqs < 1, a
+ * negative count or capacity < num_seqs.
+ */
+sa_status sa_plan_selection(const int32_t *ncand, int32_t num_seqs, int32_t capacity,
+                            int32_t *chunk_out, int64_t *groups_out);
+
+/*
+ * sa_plan_latent_attention -- the latent-row attention launch (bf16 576/512 rows) for `rows`
+ * query rows of k selected rows each: splits per row, split length (a multiple of 32, at most
+ * 2048), merge mode (0: one split, no merge; 1 or 2: the splits of a row merge inside the
+ * launch, 2 placing them on one XCD) and grid. A merging launch must fit `capacity` resident
+ * workgroups and needs one of `row_records` merge records per row; when no split count
+ * allows that, splits = 0 (the other attention kernel, with a separate merge launch, runs).
+ */
+sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t capacity,
+                                   int32_t row_records, int32_t *splits_out,
+                                   int32_t *split_len_out, int32_t *merge_out,
+                                   int32_t *grid_out);
+
 const char *sa_status_string(sa_status status);
 const char *sa_last_error(void); /* message of the last SA_ERR_HIP on this thread */
 int32_t sa_version(void);

@@ -57,7 +57,8 @@ EXPORTS = ("sa_index_score", "sa_topk", "sa_sparse_attn", "sa_index_select", "sa
            "sa_workspace_size", "sa_pool_create", "sa_pool_destroy", "sa_pool_stats", "sa_seq_new",
            "sa_seq_fork", "sa_seq_reserve", "sa_seq_free", "sa_seq_len", "sa_seq_page_table",
            "sa_pool_refcount", "sa_copy_pages",
-           "sa_workspace_init", "sa_workspace_error", "sa_status_string", "sa_last_error",
+           "sa_workspace_init", "sa_workspace_error", "sa_plan_selection",
+           "sa_plan_latent_attention", "sa_status_string", "sa_last_error",
            "sa_version")
 
 
@@ -103,6 +104,10 @@ def load(path: str = LIB_PATH):
     lib.sa_workspace_size.restype = sz
     lib.sa_workspace_init.argtypes = [P, sz, P]
     lib.sa_workspace_error.argtypes = [P, C.POINTER(C.c_int32), P]
+    lib.sa_plan_selection.argtypes = [P, i32, i32, ip, C.POINTER(i64)]
+    lib.sa_plan_latent_attention.argtypes = [i32, i32, i32, i32, ip, ip, ip, ip]
+    lib.sa_plan_selection.restype = C.c_int
+    lib.sa_plan_latent_attention.restype = C.c_int
     lib.sa_status_string.argtypes = [C.c_int]
     lib.sa_status_string.restype = C.c_char_p
     lib.sa_last_error.restype = C.c_char_p
@@ -183,6 +188,24 @@ def workspace_size(batch: Batch, kv: sa_kv | None, k: int, block_k: int = 0) -> 
     if n == 0:
         _check(SA_ERR_INVALID)
     return int(n)
+
+
+def plan_selection(ncand, capacity: int):
+    """(chunk, workgroups) of one fused-selection launch (host-only planning, no device)."""
+    arr = (C.c_int32 * len(ncand))(*[int(x) for x in ncand])
+    chunk, groups = C.c_int32(0), C.c_int64(0)
+    _check(load().sa_plan_selection(C.cast(arr, C.c_void_p), len(ncand), int(capacity),
+                                    C.byref(chunk), C.byref(groups)))
+    return int(chunk.value), int(groups.value)
+
+
+def plan_latent_attention(rows: int, k: int, capacity: int, row_records: int):
+    """(splits, split_len, merge, grid) of the latent attention launch; splits = 0 when the
+    other attention kernel runs (host-only planning, no device)."""
+    o = [C.c_int32(0) for _ in range(4)]
+    _check(load().sa_plan_latent_attention(int(rows), int(k), int(capacity), int(row_records),
+                                           *[C.byref(x) for x in o]))
+    return tuple(int(x.value) for x in o)
 
 
 def workspace_init(ws: torch.Tensor, stream=None) -> None:

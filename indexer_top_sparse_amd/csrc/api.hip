@@ -147,6 +147,24 @@ AttnPlan latent_plan(int rows, int k, int max_splits) {
     return p;
 }
 
+// The latent kernel's launch for `rows` query rows: a merging launch waits between the splits of
+// a row, so its grid must fit `cap` resident workgroups and each of its rows needs one of
+// `row_recs` merge records. The split count drops until it fits; latent = false when no split
+// count does (the other attention kernel, with a separate merge launch, runs instead).
+AttnPlan latent_launch_plan(int rows, int k, int cap, int row_recs) {
+    AttnPlan p = latent_plan(rows, k, 1 << 30);
+    auto fits = [&](const AttnPlan &q) {
+        return !q.merge || (lat_grid_host(rows, q.splits, q.merge) <= cap && rows <= row_recs);
+    };
+    while (!fits(p)) {
+        const AttnPlan q = latent_plan(rows, k, p.splits - 1);
+        if (q.splits >= p.splits) break;
+        p = q;
+    }
+    p.latent = fits(p);
+    return p;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
@@ -254,6 +272,30 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
     return std::min(block_k, nblk) * page_size;
 }
 
+// The chunk of a selection launch: the smallest multiple of 64 whose workgroups (sel_groups per
+// sequence, at most kMaxGroupsPerSeq each) all fit in `cap` resident workgroups, for n <= cap
+// sequences with nc_of(i) candidates; *groups gets the launch's workgroups.
+template <class F>
+int plan_chunk(F nc_of, int n, int cap, int64_t *groups) {
+    int nc_max = 0;
+    for (int i = 0; i < n; ++i) nc_max = std::max(nc_max, nc_of(i));
+    auto total_groups = [&](int c) {
+        int64_t gsum = 0;
+        for (int i = 0; i < n; ++i) gsum += sel_groups(nc_of(i), c);
+        return gsum;
+    };
+    int lo = std::max(1, (nc_max + kMaxGroupsPerSeq - 1) / kMaxGroupsPerSeq);
+    lo = (lo + 63) / 64;
+    int hi = std::max(lo, (nc_max + 63) / 64);  // in units of 64; one workgroup per sequence fits
+    while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        if (total_groups(64 * mid) <= cap) hi = mid;
+        else lo = mid + 1;
+    }
+    *groups = total_groups(64 * lo);
+    return 64 * lo;
+}
+
 // Launches of the fused selection for one candidate mode. All workgroups of a launch must be
 // resident at once (they wait for each other), so a launch holds at most the device's resident
 // capacity of workgroups; batches with more sequences than half that capacity are split into
@@ -282,25 +324,9 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         for (int iter = 0;; ++iter) {
             const int cap = occ * cus;
             if (nb > cap || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
-            int nc_max = 0;
-            for (int s = s0; s < s0 + nb; ++s)
-                nc_max = std::max(nc_max, ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k));
-            auto total_groups = [&](int c) {
-                int64_t gsum = 0;
-                for (int s = s0; s < s0 + nb; ++s)
-                    gsum += sel_groups(ncand_host(mode, b->ctx_lens_host[s], b->page_size, block_k), c);
-                return gsum;
-            };
-            int lo = std::max(1, (nc_max + kMaxGroupsPerSeq - 1) / kMaxGroupsPerSeq);
-            lo = (lo + 63) / 64;
-            int hi = std::max(lo, (nc_max + 63) / 64);  // in units of 64; hi always fits (nb <= cap)
-            while (lo < hi) {
-                const int mid = (lo + hi) / 2;
-                if (total_groups(64 * mid) <= cap) hi = mid;
-                else lo = mid + 1;
-            }
-            chunk = 64 * lo;
-            groups = total_groups(chunk);
+            chunk = plan_chunk(
+                [&](int i) { return ncand_host(mode, b->ctx_lens_host[s0 + i], b->page_size, block_k); },
+                nb, cap, &groups);
             lds = decode_select_dynamic_lds(mode, chunk, lp);
             const int o = chunk <= kSelMaxChunk ? occupancy(kern, threads, lds) : 0;
             if (o <= 0) {
@@ -382,15 +408,8 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
         // the splits of a row wait for each other, so a merging grid must fit the device's
         // resident capacity (one workgroup per CU: the tile ring takes most of the LDS)
         static const int occ = attn_latent_occupancy(kMaxSplitRows);
-        const int cap = std::max(occ, 0) * device_cus();
-        AttnPlan p = latent_plan(rows, k, 1 << 30);
-        // (and a merging launch needs one record per row)
-        while (p.merge && (lat_grid_host(rows, p.splits, p.merge) > cap || rows > L.row_recs)) {
-            const AttnPlan q2 = latent_plan(rows, k, p.splits - 1);
-            if (q2.splits >= p.splits) break;
-            p = q2;
-        }
-        if (!p.merge || (lat_grid_host(rows, p.splits, p.merge) <= cap && rows <= L.row_recs)) {
+        const AttnPlan p = latent_launch_plan(rows, k, std::max(occ, 0) * device_cus(), L.row_recs);
+        if (p.latent) {
             a.splits = p.splits;
             a.split_len = split_len(k, p.splits);
             a.merge_inside = p.merge;
@@ -472,6 +491,34 @@ size_t sa_workspace_size(const sa_batch *batch, const sa_kv *kv, int32_t k, int3
     RowPlan rp;
     if (check_batch(batch, &rp) != SA_OK) return 0;
     return ws_layout(batch, rp.rows, kv, k, block_k).total;
+}
+
+sa_status sa_plan_selection(const int32_t *ncand, int32_t num_seqs, int32_t capacity,
+                            int32_t *chunk_out, int64_t *groups_out) {
+    if (!ncand || !chunk_out || !groups_out || num_seqs < 1)
+        return fail(SA_ERR_INVALID, "ncand, chunk_out and groups_out are required, num_seqs >= 1");
+    if (capacity < num_seqs) return fail(SA_ERR_INVALID, "capacity below one workgroup per sequence");
+    for (int i = 0; i < num_seqs; ++i)
+        if (ncand[i] < 0) return fail(SA_ERR_INVALID, "negative candidate count");
+    int64_t groups = 0;
+    *chunk_out = plan_chunk([&](int i) { return (int)ncand[i]; }, num_seqs, capacity, &groups);
+    *groups_out = groups;
+    return SA_OK;
+}
+
+sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t capacity,
+                                   int32_t row_records, int32_t *splits_out,
+                                   int32_t *split_len_out, int32_t *merge_out,
+                                   int32_t *grid_out) {
+    if (!splits_out || !split_len_out || !merge_out || !grid_out || rows < 1 || k < 1 ||
+        k > 65536 || capacity < 0 || row_records < 0)
+        return fail(SA_ERR_INVALID, "outputs required; rows >= 1, 1 <= k <= 65536, capacity and row_records >= 0");
+    const AttnPlan p = latent_launch_plan(rows, k, capacity, row_records);
+    *splits_out = p.latent ? p.splits : 0;
+    *split_len_out = p.latent ? split_len(k, p.splits) : 0;
+    *merge_out = p.latent ? p.merge : 0;
+    *grid_out = p.latent ? lat_grid_host(rows, p.splits, p.merge) : 0;
+    return SA_OK;
 }
 
 sa_status sa_workspace_init(void *ws, size_t bytes, void *stream) {
