@@ -44,6 +44,40 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def host_info():
+    """CPU model of the host (the oracle baseline runs there)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
+def step_distribution(step, n, stream, rotate):
+    """Per-step durations (us) of n back-to-back steps, each bracketed by its own pair of events
+    on the launch stream: median, p10 and p90. rotate=False runs every step on replica 0
+    (inputs possibly still in the last-level cache: "warm"), rotate=True rotates the replicas
+    as the headline loop does ("cold")."""
+    import numpy as np
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(n):
+        step(i if rotate else 0)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]) * 1e3
+    return {"steps": n, "median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90)), "min_us": float(t.min()),
+            "max_us": float(t.max())}
+
+
 def algorithmic_bytes(wl):
     """Bytes each kernel must move at least once (inputs read once, outputs written once)."""
     P, K = wl.page_size, wl.topk
@@ -153,9 +187,9 @@ def run_prefill(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    import numpy as np
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    t_s = t_k = t_a = 0.0
-    tot = 0.0
+    per = {"index_score": [], "topk": [], "sparse_attn": [], "step": []}
     for _ in range(args.steps):
         ev[0].record(stream)
         B.index_score(d.batch, d.ix, d.t["q_idx"], d.t["w"], scores)
@@ -165,13 +199,29 @@ def run_prefill(args):
         B.sparse_attn(d.batch, d.kv, d.t["q"], idx, out, ws)
         ev[3].record(stream)
         torch.cuda.synchronize()
-        t_s += ev[0].elapsed_time(ev[1])
-        t_k += ev[1].elapsed_time(ev[2])
-        t_a += ev[2].elapsed_time(ev[3])
-        tot += ev[0].elapsed_time(ev[3])
+        per["index_score"].append(ev[0].elapsed_time(ev[1]))
+        per["topk"].append(ev[1].elapsed_time(ev[2]))
+        per["sparse_attn"].append(ev[2].elapsed_time(ev[3]))
+        per["step"].append(ev[0].elapsed_time(ev[3]))
     n = args.steps
-    t_s, t_k, t_a, tot = t_s / n, t_k / n, t_a / n, tot / n
+    mean = {k: float(np.mean(v)) for k, v in per.items()}
+    t_s, t_k, t_a, tot = mean["index_score"], mean["topk"], mean["sparse_attn"], mean["step"]
     fi, fa = prefill_flops(wl)
+    pos = wl.q_pos()
+    # row Top-K: the visible scores read once, the index rows written once
+    topk_bytes = 4 * int((pos + 1).sum()) + 4 * rows * wl.topk
+    roof = {
+        "index_score": {"bound": "mfma", "achieved": fi / (t_s * 1e-3) / 1e12,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops": fi},
+        "topk": {"bound": "hbm", "achieved": topk_bytes / (t_k * 1e-3) / 1e9,
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": topk_bytes},
+        "sparse_attn": {"bound": "mfma", "achieved": fa / (t_a * 1e-3) / 1e12,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops": fa},
+    }
+    for k, r in roof.items():
+        r["frac"] = r["achieved"] / r["peak"]
+        r["avg_launch_ms"] = mean[k]
+    dominant = max(("index_score", "topk", "sparse_attn"), key=lambda k: mean[k])
     res = {
         "metric": "prefill query tokens/s (indexer GEMM + row Top-K + sparse attn)",
         "value": rows / (tot * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": n,
@@ -179,12 +229,18 @@ def run_prefill(args):
         "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
         "config": {"workload": f"{args.workload}: {rows} query rows after a "
                                f"{max(wl.ctx_lens) - rows}-token prefix, K={wl.topk}"},
+        "roofline": dict(kernel=dominant, traffic=None, **roof[dominant]),
+        "rooflines": roof,
         "kernels_ms": {"index_score": t_s, "topk": t_k, "sparse_attn": t_a},
+        "step_distribution": {"steps": n, "median_ms": float(np.median(per["step"])),
+                              "p10_ms": float(np.percentile(per["step"], 10)),
+                              "p90_ms": float(np.percentile(per["step"], 90))},
         "mfma": {"indexer_tflops": fi / (t_s * 1e-3) / 1e12, "indexer_flops": fi,
                  "attention_tflops": fa / (t_a * 1e-3) / 1e12, "attention_flops": fa,
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                  "indexer_frac": fi / (t_s * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                  "attention_frac": fa / (t_a * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "host": host_info(),
     }
     print(json.dumps(res), flush=True)
 
@@ -199,6 +255,9 @@ def main():
     ap.add_argument("--workload", default="decode32k",
                     help="input preset (decode32k is the headline configuration)")
     ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--dist-steps", type=int, default=200,
+                    help="single steps timed one by one for the median / p10 / p90 (at least "
+                         "--steps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -280,6 +339,13 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f})")
+
+    # ---- distribution of single steps (after the headline, so the GPU is at steady clocks):
+    #      rotated replicas (cold, as timed above) and one replica (warm)
+    nd = max(args.dist_steps, args.steps)
+    dist = {"cold": step_distribution(step, nd, stream, rotate=True),
+            "warm": step_distribution(step, nd, stream, rotate=False)}
+    log(f"[bench] per-step distribution: {dist}")
 
     # ---- per-kernel durations, measured live on the same stream: K launches of the selection
     #      alone, then K launches of the attention (plus its split merge) alone, each loop
@@ -381,21 +447,29 @@ def main():
         if t.get("source_hash") == kernel_source_hash() and dominant in t.get("kernels", {}):
             traffic = t["kernels"][dominant]["hbm_bytes_per_launch"]
 
-    # ---- CPU baseline: the oracle (fp64 C, OpenMP) on a bounded sample of the same workload
+    # ---- CPU baseline: the oracle (plain C, OpenMP) on a bounded sample of the same workload,
+    #      in fp32 (the reported value) and in fp64 beside it
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        t1 = time.perf_counter()
-        oracle.decode_step(wl, rows=[0])
-        one = time.perf_counter() - t1
-        n_rows = max(1, min(wl.num_seqs, int(args.cpu_seconds / max(one, 1e-3))))
-        t1 = time.perf_counter()
-        oracle.decode_step(wl, rows=list(range(n_rows)))
-        el = time.perf_counter() - t1
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-        cpu = {"value": n_rows / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"{n_rows} of {wl.num_seqs} sequences of the same workload, full path "
-                         f"(scores, Top-K, attention) in fp64, {el:.1f}s"}
+
+        def oracle_rate(real):
+            t1 = time.perf_counter()
+            oracle.decode_step(wl, rows=[0], real=real)
+            one = time.perf_counter() - t1
+            n_rows = max(1, min(wl.num_seqs, int(args.cpu_seconds / max(one, 1e-3))))
+            t1 = time.perf_counter()
+            oracle.decode_step(wl, rows=list(range(n_rows)), real=real)
+            return n_rows, time.perf_counter() - t1
+
+        n32, el32 = oracle_rate("f32")
+        n64, el64 = oracle_rate("f64")
+        threads = oracle.max_threads("f32")
+        cpu = {"value": n32 / el32, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n32} of {wl.num_seqs} sequences of the same workload, full path "
+                         f"(scores, Top-K, attention), fp32 oracle, {el32:.1f}s",
+               "fp64": {"value": n64 / el64, "sample": f"{n64} sequences, {el64:.1f}s"},
+               "omp_max_threads": threads, **host_info()}
         log(f"[bench] cpu baseline {cpu}")
 
     res = {
@@ -427,7 +501,9 @@ def main():
                      "avg_launch_us": dom_ms * 1e3},
         "kernels_us": {"select": sel_avg * 1e3, "attention": att_avg * 1e3,
                        "cache_append": app_avg * 1e3, "indexer_prolog": pro_avg * 1e3},
+        "step_distribution": dist,
         "cpu_baseline": cpu,
+        "host": host_info(),
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(res), flush=True)

@@ -43,6 +43,7 @@ def load(real: str = "f64"):
     lib = C.CDLL(path)
     rt = np.float64 if real == "f64" else np.float32
     assert lib.ora_real_bytes() == np.dtype(rt).itemsize
+    lib.ora_max_threads.restype = C.c_int
     P = C.c_void_p
     i32, i64, f32 = C.c_int, C.c_int64, C.c_float
     lib.ora_index_scores.argtypes = [i32, P, P, i32, i32, P, P, i32, P, P, P, i32, i32, i64, P]
@@ -266,6 +267,11 @@ def two_level_select(wl, rows=None, real: str = "f64"):
     blocks = topk(bs, nblk, wl.block_topk, real)
     idx = topk_in_blocks(wl, blocks, rows, wl.topk, real)
     return blocks, idx, bs
+
+
+def max_threads(real: str = "f64") -> int:
+    """OpenMP threads the oracle's loops use (omp_get_max_threads of its library)."""
+    return int(load(real).ora_max_threads())
 
 
 def decode_step(wl, rows=None, real: str = "f64"):

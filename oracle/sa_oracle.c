@@ -39,6 +39,14 @@ typedef double REAL;
 
 int ora_real_bytes(void) { return ORACLE_REAL_BYTES; }
 
+/* Threads the OpenMP loops below run with (for reporting timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int ora_max_threads(void) { return omp_get_max_threads(); }
+#else
+int ora_max_threads(void) { return 1; }
+#endif
+
 /* ---------------------------------------------------------------- storage formats */
 
 /* bf16 is the upper half of an IEEE-754 binary32 word: widen by appending 16 zero bits. */
