@@ -47,8 +47,9 @@
  *    and keep some workgroups from starting. Every such wait is bounded (2^20 polls, about a
  *    second; the environment variable SA_SPIN_LIMIT, read per call, overrides the count). When
  *    one expires, the call still ends with a defined result: every sequence whose selection
- *    waited too long gets index -1 in every slot (and so output 0), every attention row whose
- *    split barrier expired gets output 0, and bit 0 of the workspace error word is set
+ *    waited too long gets index -1 in every slot (and so output 0), every group of a row's
+ *    heads whose split barrier expired (the latent attention merges 64 or 128 heads of a row
+ *    together) gets output 0, and bit 0 of the workspace error word is set
  *    (sa_workspace_error). The workspace is left ready for the next call.
  */
 #ifndef SA_H_
@@ -399,16 +400,18 @@ sa_status sa_plan_selection(const int32_t *ncand, int32_t num_seqs, int32_t capa
 
 /*
  * sa_plan_latent_attention -- the latent-row attention launch (bf16 576/512 rows) for `rows`
- * query rows of k selected rows each: splits per row, split length (a multiple of 32, at most
- * 2048), merge mode (0: one split, no merge; 1 or 2: the splits of a row merge inside the
- * launch, 2 placing them on one XCD) and grid. A merging launch must fit `capacity` resident
- * workgroups and needs one of `row_records` merge records per row; when no split count
- * allows that, splits = 0 (the other attention kernel, with a separate merge launch, runs).
+ * query rows of k selected rows each and heads_q query heads: splits per (row, head group),
+ * split length (a multiple of 32, at most 2048 rows, or 1024 with two head groups), head
+ * groups per row (1, or 2 of 64 heads when a row has more than 64 heads and one workgroup per
+ * row would leave the device partly idle), merge (1: the splits of a (row, head group) merge
+ * inside the launch) and grid. A merging launch must fit `capacity` resident workgroups and
+ * needs one of `row_records` merge records per (row, head group); when no split count allows
+ * that, splits = 0 (the other attention kernel, with a separate merge launch, runs).
  */
-sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t capacity,
+sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t heads_q, int32_t capacity,
                                    int32_t row_records, int32_t *splits_out,
-                                   int32_t *split_len_out, int32_t *merge_out,
-                                   int32_t *grid_out);
+                                   int32_t *split_len_out, int32_t *head_groups_out,
+                                   int32_t *merge_out, int32_t *grid_out);
 
 const char *sa_status_string(sa_status status);
 const char *sa_last_error(void); /* message of the last SA_ERR_HIP on this thread */

@@ -105,7 +105,7 @@ def load(path: str = LIB_PATH):
     lib.sa_workspace_init.argtypes = [P, sz, P]
     lib.sa_workspace_error.argtypes = [P, C.POINTER(C.c_int32), P]
     lib.sa_plan_selection.argtypes = [P, i32, i32, ip, C.POINTER(i64)]
-    lib.sa_plan_latent_attention.argtypes = [i32, i32, i32, i32, ip, ip, ip, ip]
+    lib.sa_plan_latent_attention.argtypes = [i32, i32, i32, i32, i32, ip, ip, ip, ip, ip]
     lib.sa_plan_selection.restype = C.c_int
     lib.sa_plan_latent_attention.restype = C.c_int
     lib.sa_status_string.argtypes = [C.c_int]
@@ -199,12 +199,12 @@ def plan_selection(ncand, capacity: int):
     return int(chunk.value), int(groups.value)
 
 
-def plan_latent_attention(rows: int, k: int, capacity: int, row_records: int):
-    """(splits, split_len, merge, grid) of the latent attention launch; splits = 0 when the
-    other attention kernel runs (host-only planning, no device)."""
-    o = [C.c_int32(0) for _ in range(4)]
-    _check(load().sa_plan_latent_attention(int(rows), int(k), int(capacity), int(row_records),
-                                           *[C.byref(x) for x in o]))
+def plan_latent_attention(rows: int, k: int, heads_q: int, capacity: int, row_records: int):
+    """(splits, split_len, head_groups, merge, grid) of the latent attention launch; splits = 0
+    when the other attention kernel runs (host-only planning, no device)."""
+    o = [C.c_int32(0) for _ in range(5)]
+    _check(load().sa_plan_latent_attention(int(rows), int(k), int(heads_q), int(capacity),
+                                           int(row_records), *[C.byref(x) for x in o]))
     return tuple(int(x.value) for x in o)
 
 

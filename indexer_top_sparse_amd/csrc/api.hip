@@ -124,8 +124,7 @@ int attn_splits(int rows, int k, int heads_q) {
 }
 int split_len(int k, int s) { return (((k + s - 1) / s) + 31) / 32 * 32; }
 
-// Latent-row attention (bf16 rows of 576 entries, V = the first 512, up to 128 query heads):
-// one workgroup per (query row, split) with every head, the splits merged inside the launch.
+// Latent-row attention (bf16 rows of 576 entries, V = the first 512, up to 128 query heads).
 constexpr int kAttnTarget = 256;  // workgroups that fill an MI355X (one per CU)
 bool latent_shape(const sa_kv *kv) {
     return kv->dim_qk == 576 && kv->dim_v == 512 && kv->v == nullptr && kv->dtype == SA_BF16 &&
@@ -133,31 +132,49 @@ bool latent_shape(const sa_kv *kv) {
 }
 struct AttnPlan {
     bool latent;
-    int splits, merge;
+    int tphases;  // 1: 128 heads per workgroup, 2: 64 heads per workgroup in two tile phases
+    int hgroups;  // workgroups per (row, split) that divide the heads
+    int splits;
+    int merge;    // 1: splits merged inside the launch
+    int xcd;      // 1: the workgroups of a row on one XCD
 };
-// Splits of the latent kernel: enough workgroups to fill the device, at least 4 tiles of 32 rows
-// per split, at most kMaxSplitRows rows per split (the per-row tables live in LDS).
-AttnPlan latent_plan(int rows, int k, int max_splits) {
+// Layout and splits of the latent kernel for `rows` query rows, enough workgroups to fill the
+// device. When one workgroup per row would leave compute units idle and a row has more than 64
+// heads, two head groups of 64 (tphases = 2) divide each row before its index set is split: the
+// merge then moves half the partials. Rows of at most 64 heads always take tphases = 2 (all 8
+// waves busy). Splits keep at least 4 tiles of 32 rows and at most the rows whose tables fit
+// the kernel's LDS.
+AttnPlan latent_plan(int rows, int k, int heads_q, int max_splits) {
     const int r = std::max(rows, 1);
+    int T = 1, hg = 1;
     int s = std::max(1, (kAttnTarget + r - 1) / r);
+    if (heads_q <= 64) {
+        T = 2;
+    } else if (s > 1) {
+        T = 2;
+        hg = 2;
+        s = std::max(1, (kAttnTarget + 2 * r - 1) / (2 * r));
+    }
     s = std::min(s, std::max(1, (k + 127) / 128));
     s = std::min(s, std::max(1, max_splits));
-    s = std::max(s, (k + kMaxSplitRows - 1) / kMaxSplitRows);
-    AttnPlan p{true, s, s == 1 ? 0 : (rows % 8 == 0 ? 2 : 1)};
+    const int maxrows = attn_latent_max_rows(T);
+    s = std::max(s, (k + maxrows - 1) / maxrows);
+    AttnPlan p{true, T, hg, s, s > 1 ? 1 : 0, hg * s > 1 ? 1 : 0};
     return p;
 }
 
 // The latent kernel's launch for `rows` query rows: a merging launch waits between the splits of
-// a row, so its grid must fit `cap` resident workgroups and each of its rows needs one of
-// `row_recs` merge records. The split count drops until it fits; latent = false when no split
-// count does (the other attention kernel, with a separate merge launch, runs instead).
-AttnPlan latent_launch_plan(int rows, int k, int cap, int row_recs) {
-    AttnPlan p = latent_plan(rows, k, 1 << 30);
+// a (row, head group), so its grid must fit `cap` resident workgroups and each group needs one
+// of `row_recs` merge records. The split count drops until it fits; latent = false when no
+// split count does (the other attention kernel, with a separate merge launch, runs instead).
+AttnPlan latent_launch_plan(int rows, int k, int heads_q, int cap, int row_recs) {
+    AttnPlan p = latent_plan(rows, k, heads_q, 1 << 30);
     auto fits = [&](const AttnPlan &q) {
-        return !q.merge || (lat_grid_host(rows, q.splits, q.merge) <= cap && rows <= row_recs);
+        return !q.merge || (lat_grid_host(rows, q.hgroups * q.splits, q.xcd) <= cap &&
+                            (int64_t)rows * q.hgroups <= row_recs);
     };
     while (!fits(p)) {
-        const AttnPlan q = latent_plan(rows, k, p.splits - 1);
+        const AttnPlan q = latent_plan(rows, k, heads_q, p.splits - 1);
         if (q.splits >= p.splits) break;
         p = q;
     }
@@ -170,7 +187,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct WsLayout {
     size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, slots = 0, part_o = 0, part_ml = 0,
            rsync = 0, total = 0;
-    int row_recs = 0;  // per-row merge records at rsync
+    int row_recs = 0;  // merge records at rsync, one per (row, head group)
 };
 
 // The regions that must hold zeros when a call starts (error word, zero row, selection and merge
@@ -191,8 +208,8 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
     off = align256(off + sizeof(SelSync) * (size_t)nsr);
     const int rmax = std::max(rows, b->num_seqs);
     if (kv || row_records >= 0) {
-        L.rsync = off;  // per-row merge records (rows of a merge launch fit the device)
-        const int nrr = row_records >= 0 ? row_records : std::min(rmax, 4096);
+        L.rsync = off;  // merge records (the groups of a merging launch fit the device)
+        const int nrr = row_records >= 0 ? row_records : std::min(2 * rmax, 8192);  // (row, head group)
         L.row_recs = nrr;
         off = align256(off + sizeof(uint32_t) * kRowSyncWords * (size_t)nrr);
     }
@@ -206,13 +223,18 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
         // the split count only grows as rows shrink; size for the larger of the two, for
         // either kernel
         int s = std::max(attn_splits(rows, k, kv->heads_q), attn_splits(b->num_seqs, k, kv->heads_q));
-        if (latent_shape(kv))
-            s = std::max(s, std::max(latent_plan(rows, k, 1 << 30).splits,
-                                     latent_plan(b->num_seqs, k, 1 << 30).splits));
-        L.part_o = off;  // (the latent kernel's blocks round the heads up to 16)
-        off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * (16 * ((kv->heads_q + 15) / 16)) * kv->dim_v);
+        // the latent kernel's blocks cover 128 heads per (row, split) at most (head groups
+        // times heads per group, rounded up to 16)
+        int hq = kv->heads_q;
+        if (latent_shape(kv)) {
+            s = std::max(s, std::max(latent_plan(rows, k, kv->heads_q, 1 << 30).splits,
+                                     latent_plan(b->num_seqs, k, kv->heads_q, 1 << 30).splits));
+            hq = 128;
+        }
+        L.part_o = off;
+        off = align256(off + sizeof(uint16_t) * (size_t)rmax * s * hq * kv->dim_v);
         L.part_ml = off;
-        off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * kv->heads_q);
+        off = align256(off + sizeof(float) * 2 * (size_t)rmax * s * hq);
     }
     L.total = off;
     return L;
@@ -407,14 +429,18 @@ sa_status run_attn(const sa_batch *b, int rows, const sa_kv *kv, const void *q,
     if (latent_shape(kv)) {
         // the splits of a row wait for each other, so a merging grid must fit the device's
         // resident capacity (one workgroup per CU: the tile ring takes most of the LDS)
-        static const int occ = attn_latent_occupancy(kMaxSplitRows);
-        const AttnPlan p = latent_launch_plan(rows, k, std::max(occ, 0) * device_cus(), L.row_recs);
+        static const int occ1 = attn_latent_occupancy(1, attn_latent_max_rows(1));
+        static const int occ2 = attn_latent_occupancy(2, attn_latent_max_rows(2));
+        const AttnPlan p0 = latent_plan(rows, k, kv->heads_q, 1 << 30);
+        const int cap = std::max(p0.tphases == 1 ? occ1 : occ2, 0) * device_cus();
+        const AttnPlan p = latent_launch_plan(rows, k, kv->heads_q, cap, L.row_recs);
         if (p.latent) {
             a.splits = p.splits;
             a.split_len = split_len(k, p.splits);
             a.merge_inside = p.merge;
-            a.hgroups = 1;
-            hipError_t e = launch_attn_latent(a, st);
+            a.hgroups = p.hgroups;
+            a.xcd_align = p.xcd;
+            hipError_t e = launch_attn_latent(a, p.tphases, st);
             if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
             return SA_OK;
         }
@@ -506,18 +532,20 @@ sa_status sa_plan_selection(const int32_t *ncand, int32_t num_seqs, int32_t capa
     return SA_OK;
 }
 
-sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t capacity,
+sa_status sa_plan_latent_attention(int32_t rows, int32_t k, int32_t heads_q, int32_t capacity,
                                    int32_t row_records, int32_t *splits_out,
-                                   int32_t *split_len_out, int32_t *merge_out,
-                                   int32_t *grid_out) {
-    if (!splits_out || !split_len_out || !merge_out || !grid_out || rows < 1 || k < 1 ||
-        k > 65536 || capacity < 0 || row_records < 0)
-        return fail(SA_ERR_INVALID, "outputs required; rows >= 1, 1 <= k <= 65536, capacity and row_records >= 0");
-    const AttnPlan p = latent_launch_plan(rows, k, capacity, row_records);
+                                   int32_t *split_len_out, int32_t *head_groups_out,
+                                   int32_t *merge_out, int32_t *grid_out) {
+    if (!splits_out || !split_len_out || !head_groups_out || !merge_out || !grid_out || rows < 1 ||
+        k < 1 || k > 65536 || heads_q < 1 || heads_q > 128 || capacity < 0 || row_records < 0)
+        return fail(SA_ERR_INVALID, "outputs required; rows >= 1, 1 <= k <= 65536, 1 <= heads_q <= 128, "
+                                    "capacity and row_records >= 0");
+    const AttnPlan p = latent_launch_plan(rows, k, heads_q, capacity, row_records);
     *splits_out = p.latent ? p.splits : 0;
     *split_len_out = p.latent ? split_len(k, p.splits) : 0;
+    *head_groups_out = p.latent ? p.hgroups : 0;
     *merge_out = p.latent ? p.merge : 0;
-    *grid_out = p.latent ? lat_grid_host(rows, p.splits, p.merge) : 0;
+    *grid_out = p.latent ? lat_grid_host(rows, p.hgroups * p.splits, p.xcd) : 0;
     return SA_OK;
 }
 
@@ -709,8 +737,8 @@ sa_status sa_decode_step_noalloc(const sa_batch *batch, const sa_indexer *ix, co
     if (batch->num_seqs > kScratchSeqs)
         return fail(SA_ERR_UNSUPPORTED, "sa_decode_step_noalloc: more than 64 sequences");
     // the records at fixed offsets: selection records for kScratchSeqs sequences, merge records
-    // for as many rows (decode has one row per sequence)
-    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k, kScratchSeqs, kScratchSeqs);
+    // for two head groups of as many rows (decode has one row per sequence)
+    const WsLayout L = ws_layout(batch, rp.rows, kv, k, block_k, kScratchSeqs, 2 * kScratchSeqs);
     if (L.total > kScratchBytes)
         return fail(SA_ERR_UNSUPPORTED, "sa_decode_step_noalloc: the call needs more than the 48 MiB scratch "
                                         "(fewer sequences or a smaller k)");

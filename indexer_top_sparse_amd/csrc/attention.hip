@@ -407,62 +407,72 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         *reinterpret_cast<uint32_t *>(orow + e) = pack_bf16x2(acc[e] * inv, acc[e + 1] * inv);
 }
 
-// ================================================== latent rows, all query heads per workgroup
+// ================================================== latent rows, many query heads per workgroup
 // bf16 latent rows (576 entries: the first 512 are V) and up to 128 query heads sharing them
 // (MLA-style decode and prefill; [CANN] §1 and §2.1). One workgroup of 8 waves per (query row,
-// split of its index set); wave w owns heads 16 w .. 16 w + 15 with the whole 576-wide
-// contraction, so each gathered row is staged once per split and serves every head, and no
-// partial score crosses waves:
+// head group, split of its index set). Each wave owns 16 heads with the whole 576-wide
+// contraction, so a staged row serves all the workgroup's heads and no partial score crosses
+// waves:
 //   S^T[row][head] = K[row][:] . Q[head][:]       (16x16x32 bf16 MFMA, 2 x 18 per 32-row tile)
 //   online softmax per head                        (a lane holds 8 rows of one head)
 //   O^T[d][head] += V^T[d][row] . P^T[row][head]  (32 MFMAs per tile, V^T by transposing reads)
+// Two tile-phase layouts (template T):
+//   T = 1: 8 waves x 16 heads = 128 heads; every wave computes every tile. One head group.
+//   T = 2: 4 groups of 16 heads x 2 phases = 64 heads; phase p computes the tiles t = p mod 2,
+//          and at the end phase 1 hands its (max, sum, output) to phase 0 through LDS. With more
+//          than 64 heads a row has two head groups; they gather the same rows, the second from
+//          the L2 of the XCD they share.
+// T = 2 halves what a split publishes for the merge (64 heads instead of 128), which is what
+// decode, with few rows and many splits, pays most for.
 // Two waves per SIMD keep the 16x16x32 MFMA at its full rate. A wave's query fragments (72
 // registers) and output accumulators (128) take most of its 256, so addresses are rebuilt per
 // tile and LDS reads run only a few fragments ahead of their MFMAs.
-// Rows move from HBM straight into LDS (global_load_lds_dwordx4) through a ring of three 32-row
-// tiles: while tile t is computed, tiles t + 1 and t + 2 are in flight, and the copies use no
-// registers. Each wave issues kLatCopies copies of 1 KiB per tile (36 KiB per tile; waves 4..7
-// repeat blocks 32..35 in their last copy, writing the same bytes twice), so every wave waits
-// for an exact count.
+// Rows move from HBM straight into LDS (global_load_lds_dwordx4) through a ring of tiles of 32
+// rows (T = 1: three, two in flight while one is computed; T = 2: four, one step of two tiles
+// in flight while the other is computed), and the copies use no registers. With T = 2 a step's
+// copies are issued as soon as a barrier shows the slots they overwrite free, before the wait
+// for the step about to be computed, so that its single step ahead never drains. Every wave
+// issues the same number of 1 KiB copies per step, so every wave waits for an exact count.
 //
 // Index sets split over several workgroups (few query rows, as in decode) are merged inside the
 // same launch: each split publishes its output normalised by its own sum (bf16) with its
-// (max, sum) per head through agent-scope stores, the splits of a row meet at a barrier, and
-// then split s merges the heads [s H / S, (s + 1) H / S) for all splits, in split order (the
-// result does not depend on timing). This needs every split of a row resident at once: the
+// (max, sum) per head through agent-scope stores, the splits of a (row, head group) meet at a
+// barrier, and then split s merges the units [s U / S, (s + 1) U / S) of all splits, in split
+// order (the result does not depend on timing). This needs every split resident at once: the
 // host only chooses it when the grid fits the device's resident capacity. Workgroup b runs on
-// XCD b mod 8 (round-robin dispatch), so with a multiple of 8 rows the splits of a row are given
-// indices of one residue mod 8: their merge then reads partials written on the same XCD.
+// XCD b mod 8 (round-robin dispatch), so the workgroups of a row are given indices of one
+// residue mod 8: they share that XCD's L2.
 constexpr int kLatQK = 576, kLatV = 512;
 constexpr int kLatRowB = 2 * kLatQK;          // bytes per staged row
 constexpr int kLatTileB = kTile * kLatRowB;   // 36864 bytes per tile
-constexpr int kLatRing = 3;
 constexpr int kLatWaves = 8;
 constexpr int kLatThreads = 64 * kLatWaves;
-constexpr int kLatCopies = 5;                 // 1 KiB copies per wave per tile
 constexpr int kLatKS = kLatQK / 32;           // 18 k-steps of 32 entries
 constexpr int kLatDT = kLatV / 16;            // 32 d_v tiles of 16 entries
 static_assert(kLatTileB == 36 * 1024, "36 one-KiB copies per tile");
 
-// Workgroup b -> (query row, split). merge_inside 0: one workgroup per row. 1: row b % rows,
-// split b / rows. 2 (rows a multiple of 8): the splits of row r get indices of residue r mod 8.
-__device__ __forceinline__ void lat_row_of(int b, int rows, int splits, int merge, int &r,
-                                           int &split) {
-    if (merge == 0) {
-        r = b;
-        split = 0;
-    } else if (merge == 1) {
-        r = b % rows;
-        split = b / rows;
-    } else {
+// Workgroup b -> (query row, head group, split). A row has U = hgroups * splits workgroups. With
+// xcd_align the U workgroups of row r get indices of one residue mod 8 (r mod 8), so they run on
+// one XCD: the head groups of a split then share that XCD's L2 for the gathered rows, and the
+// merge reads partials written on the same XCD. Padding workgroups (row >= rows) exit at once.
+__device__ __forceinline__ void lat_unit_of(int b, const AttnArgs &a, int &r, int &hgi,
+                                            int &split) {
+    const int U = a.hgroups * a.splits;
+    int u;
+    if (a.xcd_align) {
         const int local = b >> 3;
-        r = 8 * (local / splits) + (b & 7);
-        split = local % splits;
+        r = 8 * (local / U) + (b & 7);
+        u = local % U;
+    } else {
+        r = b / U;
+        u = b % U;
     }
+    hgi = u % a.hgroups;
+    split = u / a.hgroups;
 }
 
-__host__ __device__ inline int lat_grid(int rows, int splits, int merge) {
-    return merge == 2 ? 8 * splits * ((rows + 7) / 8) : rows * splits;
+__host__ __device__ inline int lat_grid(int rows, int units, int xcd_align) {
+    return xcd_align ? 8 * units * ((rows + 7) / 8) : rows * units;
 }
 
 // A value the compiler may not take apart (so that it keeps a base register and folds
@@ -472,18 +482,33 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     return x;
 }
 
+// Per tile-phase count T: T = 1 runs 8 waves x 16 heads (128 heads) on every tile; T = 2 runs 4
+// head groups x 2 phases (64 heads), the phases taking alternate tiles.
+template <int T>
+struct LatCfg {
+    static constexpr int kRing = T == 1 ? 3 : 4;   // staged tiles
+    static constexpr int kAhead = T == 1 ? 2 : 1;  // steps in flight while one is computed
+    static constexpr int kCPW = T == 1 ? 5 : 9;    // 1 KiB copies per wave per step
+    static constexpr int kHPW = 128 / T;           // query heads per workgroup
+    static constexpr int kHW = 8 / T;              // groups of 16 heads per workgroup
+    static constexpr int kMaxRows = T == 1 ? 2048 : 1024;  // selected rows per split
+};
+
+template <int T>
 __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
+    using C = LatCfg<T>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // dynamic LDS: ring [3][36864] | slots [split_len] int32 | logit bias [split_len] fp32
+    // dynamic LDS: ring [kRing][36864] | slots [split_len] int32 | logit bias [split_len] fp32
     uint8_t *ring = lds;
-    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + kLatRing * kLatTileB);
+    int32_t *s_slot = reinterpret_cast<int32_t *>(lds + C::kRing * kLatTileB);
     float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
     __shared__ int s_leave;
 
     const int tid = threadIdx.x, l = lane_id(), g = l >> 4, L = l & 15;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int row, split;
-    lat_row_of(blockIdx.x, a.rows, a.splits, a.merge_inside, row, split);
+    const int hsub = w % C::kHW, tp = w / C::kHW;  // head group of 16, tile phase
+    int row, hgi, split;
+    lat_unit_of(blockIdx.x, a, row, hgi, split);
     if (row >= a.rows) return;  // padding of the XCD-aligned grid: no barrier counts on it
     int seq, qoff, qlen;
     row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
@@ -491,13 +516,15 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     const int j0 = split * a.split_len;
     const int j1 = min(a.k, j0 + a.split_len);
     const int ntiles = j1 > j0 ? (j1 - j0 + kTile - 1) / kTile : 0;
+    const int nsteps = (ntiles + T - 1) / T;
     const int P = 1 << a.lp;
 
-    // ---- query fragments (B operand of S^T = K Q^T): head 16 w + L, entries 32 s + 8 g + e.
+    // ---- query fragments (B operand of S^T = K Q^T): head head0 + L, entries 32 s + 8 g + e.
     //      A lane past the last head reads head 0; its column is never stored. Issued first,
     //      so that their latency overlaps the slot-table loads below.
-    const int head = 16 * w + L;
-    const bool live_wave = 16 * w < a.heads_q;
+    const int head0 = C::kHPW * hgi + 16 * hsub;
+    const int head = head0 + L;
+    const bool live_wave = head0 < a.heads_q;
     const bool live = head < a.heads_q;
     u32x4 qf[kLatKS];
     {
@@ -529,14 +556,26 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     //      row, each group holding the 32 rows. Copy block b (1 KiB) fills group b / 4, rows
     //      8 (b % 4) .. + 7: lane j takes row 8 (b % 4) + j / 8 and position j % 8.
     const uint32_t ring_lds = (uint32_t)(uintptr_t)ring;
-    auto issue = [&](int t) {  // copies of tile min(t, ntiles - 1) into ring slot t % 3
-        const int tt = min(t, ntiles - 1);
-        const uint32_t base = ring_lds + (uint32_t)(t % kLatRing) * kLatTileB;
+    // copies of step st (tiles T st .. T st + T - 1, the last tile repeated past the end) into
+    // their ring slots. T = 1: 36 blocks per tile over 8 waves, waves 4..7 repeating blocks
+    // 32..35 in their fifth copy (the same bytes written twice); T = 2: 72 blocks, 9 per wave.
+    auto issue = [&](int st) {
         // recomputed from an opaque lane id: held across the loop these would take registers
         const int lc = (int)opaque((uint32_t)l);
 #pragma unroll
-        for (int k = 0; k < kLatCopies; ++k) {
-            const int blk = k < 4 ? w + 8 * k : 32 + (w & 3);
+        for (int k = 0; k < C::kCPW; ++k) {
+            int blk, tin;
+            if constexpr (T == 1) {
+                blk = k < 4 ? w + 8 * k : 32 + (w & 3);
+                tin = 0;
+            } else {
+                const int q = w + 8 * k;
+                tin = q / 36;
+                blk = q - 36 * tin;
+            }
+            const int t = T * st + tin;
+            const int tt = min(t, ntiles - 1);
+            const uint32_t base = ring_lds + (uint32_t)(t % C::kRing) * kLatTileB;
             const int r = 8 * (blk & 3) + (lc >> 3);
             const int c = 8 * (blk >> 2) + ((lc & 7) ^ swz(r));
             const int32_t slot = s_slot[tt * kTile + r];
@@ -550,17 +589,26 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     for (int n = 0; n < kLatDT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff(), l_run = 0.f;
 
-    if (ntiles > 0) {
-        issue(0);
-        issue(1);
-    }
-    for (int t = 0; t < ntiles; ++t) {
-        // tile t has landed once at most the copies of tile t + 1 are outstanding
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLatCopies));
-        lds_barrier();  // every wave's copies of tile t landed; tile t - 1 fully read
-        issue(t + 2);   // into the slot tile t - 1 occupied
-        if (!live_wave) continue;
-        const uint32_t kb = ring_lds + (uint32_t)(t % kLatRing) * kLatTileB;
+    if (nsteps > 0)
+#pragma unroll
+        for (int st = 0; st < C::kAhead; ++st) issue(st);
+    for (int st = 0; st < nsteps; ++st) {
+        if constexpr (T == 1) {
+            // step st has landed once at most the copies of step st + 1 are outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kCPW));
+            lds_barrier();            // every wave's copies of step st landed; st - 1 fully read
+            issue(st + C::kAhead);    // into the slots step st - 1 occupied
+        } else {
+            // one step ahead only: its copies go out before this step's wait, so that the pipe
+            // never drains
+            lds_barrier();            // step st - 1 fully read: its slots are free
+            issue(st + C::kAhead);    // into the slots step st - 1 occupied
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kAhead * C::kCPW));
+            lds_barrier();            // every wave's copies of step st landed
+        }
+        const int t = T * st + tp;
+        if (!live_wave || t >= ntiles) continue;
+        const uint32_t kb = ring_lds + (uint32_t)(t % C::kRing) * kLatTileB;
         // ---- S^T over the 576-wide contraction: two 16-row M tiles. Key fragment of k-step s,
         //      M tile mt: row 16 mt + L, chunk 4 s + g = 8 (s / 2) + (4 (s % 2) + g): column group
         //      s / 2 is an immediate offset, the swizzle touches the second part only. The bases
@@ -667,15 +715,47 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the copies issued past the last tile land before this workgroup's LDS is released
+    // the copies issued past the last step land before the ring is reused or released
     __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- T = 2: phase 1 hands its (max, sum, output) to phase 0 of the same head group through
+    //      the ring (free now), which combines the two with the usual rescaling. Both phases hold
+    //      the same entries per lane, so the combination is lane by lane.
+    if constexpr (T == 2) {
+        float *xo = reinterpret_cast<float *>(ring);      // [4 groups][32 n][64 lanes][4]
+        float *xm = xo + C::kHW * kLatDT * 64 * 4;        // [4 groups][64 lanes] max, then sum
+        __syncthreads();  // every wave has finished reading the ring
+        if (tp == 1 && live_wave) {
+#pragma unroll
+            for (int n = 0; n < kLatDT; ++n)
+                *reinterpret_cast<f32x4 *>(xo + ((hsub * kLatDT + n) * 64 + l) * 4) = o[n];
+            xm[hsub * 64 + l] = m_run;
+            xm[C::kHW * 64 + hsub * 64 + l] = l_run;
+        }
+        __syncthreads();
+        if (tp == 0 && live_wave) {
+            const float m1 = xm[hsub * 64 + l], l1 = xm[C::kHW * 64 + hsub * 64 + l];
+            const float M = fmaxf(m_run, m1);
+            const bool none = M == -__builtin_inff();
+            const float a0 = none || m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+            const float a1 = none || m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+            l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+            for (int n = 0; n < kLatDT; ++n) {
+                const f32x4 v1 = *reinterpret_cast<const f32x4 *>(xo + ((hsub * kLatDT + n) * 64 + l) * 4);
+                o[n] = o[n] * a0 + v1 * a1;
+            }
+            m_run = M;
+        }
+    }
+    const bool owner = tp == 0;  // the waves that hold the workgroup's result
 
     // ---- epilogue: lane (g, L) holds entries 16 n + 4 g + i of head L
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot = sum_xor32(l_tot);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (!a.merge_inside) {
-        if (live) {
+        if (owner && live) {
             uint16_t *orow = a.out + ((int64_t)row * a.heads_q + head) * kLatV;
 #pragma unroll
             for (int n = 0; n < kLatDT; ++n)
@@ -685,76 +765,103 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
         }
         return;
     }
-    // ---- split partials (agent scope, see st_agent_u64), then the row's barrier. A split's
-    //      partial output is a block of 8-byte units (four bf16), unit
-    //      u = ((w * 32 + n) * 4 + g) * 16 + L holding entries 16 n + 4 g .. + 3 of head
-    //      16 w + L: each store instruction of a wave writes 512 contiguous bytes.
-    const int hq16 = 16 * ((a.heads_q + 15) / 16);
-    const int64_t blk_elems = (int64_t)hq16 * kLatV;
-    if (live_wave) {
-        uint16_t *pblk = a.part_o + ((int64_t)row * a.splits + split) * blk_elems;
+    // ---- split partials (agent scope, see st_agent_u64), then the barrier of the (row, head
+    //      group). A split's partial output is a block of 8-byte units (four bf16), unit
+    //      u = ((hsub * 32 + n) * 4 + g) * 16 + L holding entries 16 n + 4 g .. + 3 of head
+    //      head0 + L: each store instruction of a wave writes 512 contiguous bytes. Blocks of
+    //      one head group hold blk_heads heads (the head count rounded up to 16 when there is
+    //      one group).
+    const int blk_heads = a.hgroups == 1 ? 16 * ((a.heads_q + 15) / 16) : C::kHPW;
+    const int64_t blk_elems = (int64_t)blk_heads * kLatV;
+    const int64_t grp = (int64_t)row * a.hgroups + hgi;  // (row, head group)
+    if (owner && live_wave) {
+        uint16_t *pblk = a.part_o + (grp * a.splits + split) * blk_elems;
 #pragma unroll
         for (int n = 0; n < kLatDT; ++n) {
             const uint64_t v = (uint64_t)pack_bf16x2(o[n][0] * inv, o[n][1] * inv) |
                                ((uint64_t)pack_bf16x2(o[n][2] * inv, o[n][3] * inv) << 32);
-            st_agent_u64(pblk + 4 * (((w * kLatDT + n) * 4 + g) * 16 + L), v);
+            st_agent_u64(pblk + 4 * (((hsub * kLatDT + n) * 4 + g) * 16 + L), v);
         }
         if (g == 0 && live)
-            st_agent_u64(a.part_ml + 2 * (((int64_t)row * a.splits + split) * a.heads_q + head),
+            st_agent_u64(a.part_ml + 2 * ((grp * a.splits + split) * C::kHPW + 16 * hsub + L),
                          (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_tot) << 32));
     }
-    uint32_t *rs = a.row_sync + (int64_t)row * kRowSyncWords;
+    uint32_t *rs = a.row_sync + grp * kRowSyncWords;
     uint32_t nbar = 0;
     const bool ok = group_barrier(&rs[0], (uint32_t)a.splits, a.err, nbar, a.spin_limit);
     // ---- merge: split s combines the units [s U / S, (s + 1) U / S) of every split's block
-    //      (U = units per block), one unit per thread at a time, with the loads of up to 8 splits
-    //      in flight; consecutive threads read consecutive units
-    const int units = hq16 * kLatV / 4;
+    //      (U = units per block). A thread takes up to 4 units kLatThreads apart (consecutive
+    //      threads read consecutive units) and issues the loads of all of them, for up to 4
+    //      splits, before it combines any: one memory round trip per 4 splits.
+    const int units = blk_heads * kLatV / 4;
     const int u0 = (int)((int64_t)units * split / a.splits);
     const int u1 = (int)((int64_t)units * (split + 1) / a.splits);
-    constexpr int kMS = 8;  // splits whose loads are in flight together
+    constexpr int kMS = 4;  // splits whose loads are in flight together
+    constexpr int kMU = 4;  // units per thread whose loads are in flight together
     if (ok) {
-        for (int u = u0 + tid; u < u1; u += kLatThreads) {
-            const int uw = u >> 11, un = (u >> 6) & 31, ug = (u >> 4) & 3, uL = u & 15;
-            const int hh = 16 * uw + uL;
-            if (hh >= a.heads_q) continue;
-            float M = -__builtin_inff(), Lsum = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int s0 = 0; s0 < a.splits; s0 += kMS) {
-                uint64_t ml[kMS], v[kMS];
+        for (int ub = u0 + tid; ub < u1; ub += kMU * kLatThreads) {
+            int hl[kMU];
+            bool on[kMU];
+            float M[kMU], Lsum[kMU], acc[kMU][4];
 #pragma unroll
-                for (int x = 0; x < kMS; ++x) {
-                    const int64_t rs_ = (int64_t)row * a.splits + min(s0 + x, a.splits - 1);
-                    ml[x] = ld_agent_u64(a.part_ml + 2 * (rs_ * a.heads_q + hh));
-                    v[x] = ld_agent_u64(a.part_o + rs_ * blk_elems + 4 * (int64_t)u);
-                }
-#pragma unroll
-                for (int x = 0; x < kMS; ++x) {
-                    const float ms = __uint_as_float((uint32_t)ml[x]);
-                    const float ls = __uint_as_float((uint32_t)(ml[x] >> 32));
-                    if (s0 + x >= a.splits || !(ls > 0.f)) continue;
-                    const float mn = fmaxf(M, ms);
-                    const float c = __builtin_amdgcn_exp2f(M - mn);  // 0 while nothing is summed
-                    const float wgt = __builtin_amdgcn_exp2f(ms - mn) * ls;
-                    Lsum = fmaf(Lsum, c, wgt);
-                    const uint32_t lo32 = (uint32_t)v[x], hi32 = (uint32_t)(v[x] >> 32);
-                    acc[0] = fmaf(acc[0], c, wgt * bf16_lo(lo32));
-                    acc[1] = fmaf(acc[1], c, wgt * bf16_hi(lo32));
-                    acc[2] = fmaf(acc[2], c, wgt * bf16_lo(hi32));
-                    acc[3] = fmaf(acc[3], c, wgt * bf16_hi(hi32));
-                    M = mn;
-                }
+            for (int i = 0; i < kMU; ++i) {
+                const int u = ub + i * kLatThreads;
+                hl[i] = 16 * (u >> 11) + (u & 15);  // head inside the group
+                on[i] = u < u1 && C::kHPW * hgi + hl[i] < a.heads_q;
+                if (!on[i]) hl[i] = 0;  // (loads stay in bounds; results unused)
+                M[i] = -__builtin_inff();
+                Lsum[i] = 0.f;
+                acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.f;
             }
-            const float il = Lsum > 0.f ? 1.f / Lsum : 0.f;
-            // agent scope: a failure fill by the row's last split to leave lands after it
-            st_agent_u64(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug,
-                         (uint64_t)pack_bf16x2(acc[0] * il, acc[1] * il) |
-                             ((uint64_t)pack_bf16x2(acc[2] * il, acc[3] * il) << 32));
+            for (int s0 = 0; s0 < a.splits; s0 += kMS) {
+                uint64_t ml[kMU][kMS], v[kMU][kMS];
+#pragma unroll
+                for (int x = 0; x < kMS; ++x) {
+                    const int64_t gs = grp * a.splits + min(s0 + x, a.splits - 1);
+#pragma unroll
+                    for (int i = 0; i < kMU; ++i) {
+                        const int u = on[i] ? ub + i * kLatThreads : u0;
+                        ml[i][x] = ld_agent_u64(a.part_ml + 2 * (gs * C::kHPW + hl[i]));
+                        v[i][x] = ld_agent_u64(a.part_o + gs * blk_elems + 4 * (int64_t)u);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kMU; ++i)
+#pragma unroll
+                    for (int x = 0; x < kMS; ++x) {
+                        const float ms = __uint_as_float((uint32_t)ml[i][x]);
+                        const float ls = __uint_as_float((uint32_t)(ml[i][x] >> 32));
+                        if (s0 + x >= a.splits || !(ls > 0.f)) continue;
+                        const float mn = fmaxf(M[i], ms);
+                        const float c = __builtin_amdgcn_exp2f(M[i] - mn);  // 0 while nothing is summed
+                        const float wgt = __builtin_amdgcn_exp2f(ms - mn) * ls;
+                        Lsum[i] = fmaf(Lsum[i], c, wgt);
+                        const uint32_t lo32 = (uint32_t)v[i][x], hi32 = (uint32_t)(v[i][x] >> 32);
+                        acc[i][0] = fmaf(acc[i][0], c, wgt * bf16_lo(lo32));
+                        acc[i][1] = fmaf(acc[i][1], c, wgt * bf16_hi(lo32));
+                        acc[i][2] = fmaf(acc[i][2], c, wgt * bf16_lo(hi32));
+                        acc[i][3] = fmaf(acc[i][3], c, wgt * bf16_hi(hi32));
+                        M[i] = mn;
+                    }
+            }
+#pragma unroll
+            for (int i = 0; i < kMU; ++i) {
+                if (!on[i]) continue;
+                const int u = ub + i * kLatThreads;
+                const int un = (u >> 6) & 31, ug = (u >> 4) & 3;
+                const int hh = C::kHPW * hgi + hl[i];
+                const float il = Lsum[i] > 0.f ? 1.f / Lsum[i] : 0.f;
+                // agent scope: a failure fill by the group's last split to leave lands after it
+                st_agent_u64(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug,
+                             (uint64_t)pack_bf16x2(acc[i][0] * il, acc[i][1] * il) |
+                                 ((uint64_t)pack_bf16x2(acc[i][2] * il, acc[i][3] * il) << 32));
+            }
         }
     } else if (tid == 0) {
         __hip_atomic_fetch_or(&rs[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // ---- leave: the last split to leave (all others have written everything) resets the
-    //      record; if any split's wait expired, it also zeroes the row's whole output, so a
+    //      record; if any split's wait expired, it also zeroes the group's whole output, so a
     //      failed call leaves a defined result (zeros, with bit 0 of the error word set)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -764,8 +871,9 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     }
     __syncthreads();
     if (s_leave == 2) {  // last to leave, after a failure
-        uint16_t *orow = a.out + (int64_t)row * a.heads_q * kLatV;
-        for (int i = tid; i < a.heads_q * kLatV / 4; i += kLatThreads) st_agent_u64(orow + 4 * i, 0ull);
+        const int h0 = C::kHPW * hgi, h1 = min(a.heads_q, h0 + C::kHPW);
+        uint16_t *orow = a.out + ((int64_t)row * a.heads_q + h0) * kLatV;
+        for (int i = tid; i < (h1 - h0) * kLatV / 4; i += kLatThreads) st_agent_u64(orow + 4 * i, 0ull);
     }
     if (s_leave >= 1 && tid == 0) {
         st_agent(&rs[0], 0u);
@@ -774,31 +882,46 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     }
 }
 
-size_t attn_latent_lds(int split_len) {
-    return (size_t)kLatRing * kLatTileB + (size_t)split_len * 8;
+size_t attn_latent_lds(int tphases, int split_len) {
+    const int ring = tphases == 1 ? LatCfg<1>::kRing : LatCfg<2>::kRing;
+    return (size_t)ring * kLatTileB + (size_t)split_len * 8;
 }
 
-hipError_t launch_attn_latent(const AttnArgs &a, hipStream_t st) {
-    const size_t lds = attn_latent_lds(a.split_len);
+int attn_latent_max_rows(int tphases) {
+    return tphases == 1 ? LatCfg<1>::kMaxRows : LatCfg<2>::kMaxRows;
+}
+
+template <int T>
+static hipError_t launch_latent_t(const AttnArgs &a, hipStream_t st) {
+    const size_t lds = attn_latent_lds(T, a.split_len);
     static std::atomic<int> granted{-1};
     hipError_t e = hipSuccess;
     if ((int)lds > granted.load(std::memory_order_relaxed)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_latent),
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_attn_latent<T>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         granted.store((int)lds, std::memory_order_relaxed);
     }
-    hipLaunchKernelGGL(k_attn_latent, dim3((unsigned)lat_grid(a.rows, a.splits, a.merge_inside)),
+    hipLaunchKernelGGL(k_attn_latent<T>,
+                       dim3((unsigned)lat_grid(a.rows, a.hgroups * a.splits, a.xcd_align)),
                        dim3(kLatThreads), lds, st, a);
     return hipGetLastError();
 }
 
-int lat_grid_host(int rows, int splits, int merge) { return lat_grid(rows, splits, merge); }
+hipError_t launch_attn_latent(const AttnArgs &a, int tphases, hipStream_t st) {
+    if (tphases == 1) return launch_latent_t<1>(a, st);
+    if (tphases == 2) return launch_latent_t<2>(a, st);
+    return hipErrorInvalidValue;
+}
 
-int attn_latent_occupancy(int split_len) {
+int lat_grid_host(int rows, int units, int xcd_align) { return lat_grid(rows, units, xcd_align); }
+
+int attn_latent_occupancy(int tphases, int split_len) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(&k_attn_latent),
-                                                     kLatThreads, attn_latent_lds(split_len)) != hipSuccess)
+    const void *kern = tphases == 1 ? reinterpret_cast<const void *>(&k_attn_latent<1>)
+                                    : reinterpret_cast<const void *>(&k_attn_latent<2>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, kLatThreads,
+                                                     attn_latent_lds(tphases, split_len)) != hipSuccess)
         return -1;
     return occ;
 }

@@ -116,19 +116,22 @@ struct AttnArgs {
     uint16_t *out;      // bf16 [rows][heads_q][dv] (splits == 1)
     uint16_t *part_o;   // bf16 [rows][splits][heads_q][dv], normalised per split (splits > 1)
     float *part_ml;     // [rows][splits][heads_q][2]
-    // latent-row kernel with the split merge inside: per query row a record of kRowSyncWords
-    // words (arrival counter, leave counter, failure flag), zero between launches
+    // latent-row kernel with the split merge inside: per (query row, head group) a record of
+    // kRowSyncWords words (arrival counter, leave counter, failure flag), zero between launches
     uint32_t *row_sync;
     uint32_t *err;
     uint32_t spin_limit;  // polls of the split barrier before it expires
-    int merge_inside;   // > 0: the splits of a row meet at a barrier and merge in the same launch
-                        // (1: row-major grid, 2: splits of a row on one XCD)
+    int merge_inside;     // 1: the splits of a (row, head group) meet at a barrier and merge in
+                          // the same launch
+    int xcd_align;        // 1: the workgroups of a row get indices of one residue mod 8
 };
 constexpr int kRowSyncWords = 16;
-// latent-row kernel (bf16 576/512 rows, up to 128 query heads)
-hipError_t launch_attn_latent(const AttnArgs &a, hipStream_t st);
-int attn_latent_occupancy(int split_len);
-int lat_grid_host(int rows, int splits, int merge);
+// latent-row kernel (bf16 576/512 rows, up to 128 query heads); tphases 1 or 2 (128 or 64
+// heads per workgroup), hgroups = head groups per row
+hipError_t launch_attn_latent(const AttnArgs &a, int tphases, hipStream_t st);
+int attn_latent_occupancy(int tphases, int split_len);
+int attn_latent_max_rows(int tphases);  // selected rows per split (LDS tables)
+int lat_grid_host(int rows, int units, int xcd_align);
 
 // key_fmt: 0 bf16, 1 E4M3 with a row scale, 2 MXFP8 (the values of sa_dtype)
 hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, int key_fmt, int rows,

@@ -2,7 +2,8 @@
 
 SA_SPIN_LIMIT=0 lets every wait of the fused selection and of the latent attention's split
 barrier expire after one poll; every kernel still runs to its end. Then each sequence's result
-must be either the normal one or the defined failure result (every index -1, output 0), the
+must be either the normal one or the defined failure result (every index -1, output 0; a group
+of heads whose split barrier expired gets output 0), the
 error word must say so, the per-sequence records must be back at zero, and the next call with
 the normal limit must give the normal result on the same workspace.
 """
@@ -37,7 +38,8 @@ class _SpinLimit:
 
 
 def _records_are_zero(ws, num_seqs, rows):
-    """Selection records (counters, flag, histograms) and merge records are all zero."""
+    """Selection records (counters, flag, histograms) and the merge records (one per row and
+    head group, two head groups at most) are all zero."""
     h = ws.cpu().numpy()
     base = 256 + 2048
     for b in range(num_seqs):
@@ -45,7 +47,7 @@ def _records_are_zero(ws, num_seqs, rows):
         if rec.any():
             return f"selection record {b} not zero"
     rs = (base + num_seqs * SEL_BYTES + 255) // 256 * 256
-    if h[rs: rs + rows * 64].any():
+    if h[rs: rs + 2 * rows * 64].any():
         return "merge records not zero"
     return ""
 
@@ -74,10 +76,16 @@ def test_expired_waits_give_the_defined_result_and_leave_the_workspace_clean():
         zero = bool((out_f[b].float() == 0).all())
         if sel_failed:
             assert zero, f"seq {b}: selection failed but the output is not zero"
-        if not zero:
-            assert torch.equal(out_f[b].view(torch.int16), out_ref[b].view(torch.int16)), \
-                f"seq {b}: output neither normal nor zero"
-        failed += sel_failed or zero
+        # a row's heads merge in groups of 64 or 128: each 64-head block is zero or exact
+        any_zero = False
+        for h0 in range(0, wl.heads_q, 64):
+            got, ref = out_f[b, h0:h0 + 64], out_ref[b, h0:h0 + 64]
+            if bool((got.float() == 0).all()):
+                any_zero = True
+            else:
+                assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), \
+                    f"seq {b}, heads {h0}..: output neither normal nor zero"
+        failed += sel_failed or any_zero
     _say(f"sequences with the failure result: {failed} of {wl.num_seqs}; error word {err}")
     assert failed > 0, "no wait expired with a spin limit of 0"
     assert err & 1
@@ -94,8 +102,8 @@ def test_expired_waits_give_the_defined_result_and_leave_the_workspace_clean():
 
 
 def test_expired_split_barrier_in_attention_alone():
-    """sa_sparse_attn on a given index set: rows whose split barrier expired are all zero, the
-    others exact, and the next normal call is exact again."""
+    """sa_sparse_attn on a given index set: head groups whose split barrier expired are all
+    zero, the others exact, and the next normal call is exact again."""
     torch.cuda.set_device(0)
     wl = inputs.make("decode32k", num_seqs=8, seed_offset=43)
     _say("decode32k B=8: sparse attention with a forced barrier failure")
@@ -112,14 +120,18 @@ def test_expired_split_barrier_in_attention_alone():
         B.sparse_attn(dw.batch, dw.kv, dw.t["q"], idx, out_f, ws)
         torch.cuda.synchronize()
     err = B.workspace_error(ws)
-    zero_rows = 0
+    # a row's heads merge in groups of 64 (two head groups per row) or 128: each 64-head block
+    # is either the failure result (all zero) or exact
+    zero_blocks = 0
     for b in range(wl.num_seqs):
-        if bool((out_f[b].float() == 0).all()):
-            zero_rows += 1
-        else:
-            assert torch.equal(out_f[b].view(torch.int16), out_ref[b].view(torch.int16)), b
-    _say(f"rows with the failure result: {zero_rows}; error word {err}")
-    assert zero_rows > 0 and err & 1
+        for h0 in range(0, wl.heads_q, 64):
+            got, ref = out_f[b, h0:h0 + 64], out_ref[b, h0:h0 + 64]
+            if bool((got.float() == 0).all()):
+                zero_blocks += 1
+            else:
+                assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), (b, h0)
+    _say(f"64-head blocks with the failure result: {zero_blocks}; error word {err}")
+    assert zero_blocks > 0 and err & 1
     msg = _records_are_zero(ws, wl.num_seqs, wl.num_seqs)
     assert msg == "", msg
     ws[:4].zero_()

@@ -64,38 +64,48 @@ def test_selection_plan_rejects_what_cannot_fit(lib):
         B.plan_selection([-1], 8)
 
 
-def _check_latent(rows, k, cap, recs):
-    splits, slen, merge, grid = B.plan_latent_attention(rows, k, cap, recs)
+def _check_latent(rows, k, cap, recs, heads=128):
+    splits, slen, hg, merge, grid = B.plan_latent_attention(rows, k, heads, cap, recs)
     if splits == 0:
         return None
-    assert slen % 32 == 0 and 32 <= slen <= 2048
+    assert hg in (1, 2) and (hg == 1 or heads > 64)
+    # 64 heads per workgroup (a row of at most 64 heads, or two head groups) hold at most 1024
+    # rows per split in LDS, 128 heads per workgroup 2048
+    two_phase = heads <= 64 or hg == 2
+    assert slen % 32 == 0 and 32 <= slen <= (1024 if two_phase else 2048)
     assert splits * slen >= k
     assert (merge == 0) == (splits == 1)
-    if merge == 2:
-        assert rows % 8 == 0
-        assert grid == 8 * splits * (rows // 8)
+    units = hg * splits
+    if units > 1:  # the workgroups of a row share an XCD: row r's indices are r mod 8
+        assert grid == 8 * units * -(-rows // 8)
     else:
-        assert grid == rows * splits
+        assert grid == rows
     if merge:
-        assert grid <= cap and rows <= recs
-    return splits, slen, merge, grid
+        assert grid <= cap and rows * hg <= recs
+    return splits, slen, hg, merge, grid
 
 
 def test_latent_attention_plan_for_the_workloads(lib):
-    # decode: 32 rows x 2048 selected rows, 256 CUs: 8 splits of 256 rows, on one XCD per row
-    assert _check_latent(32, 2048, 256, 32) == (8, 256, 2, 256)
-    # prefill: 4096 rows, one split each, no merge
-    assert _check_latent(4096, 2048, 256, 4096) == (1, 2048, 0, 4096)
+    # decode: 32 rows x 2048 selected rows, 128 heads, 256 CUs: two head groups of 64 and 4
+    # splits of 512 rows per row, the 8 workgroups of a row on one XCD
+    assert _check_latent(32, 2048, 256, 64) == (4, 512, 2, 1, 256)
+    # prefill: 4096 rows, one workgroup of 128 heads each, no merge
+    assert _check_latent(4096, 2048, 256, 8192) == (1, 2048, 1, 0, 4096)
     # more selected rows than one split holds, and too many rows to merge resident: the other
     # kernel runs
-    assert _check_latent(300, 4096, 256, 4096) is None
-    # no merge records: only an unsplit launch qualifies
-    assert _check_latent(32, 2048, 256, 0) == (1, 2048, 0, 32)
+    assert _check_latent(300, 4096, 256, 8192) is None
+    # no merge records: only an unsplit launch qualifies, and 2048 rows need two splits of 64
+    # heads, so the other kernel runs; 1024 rows fit one split
+    assert _check_latent(32, 2048, 256, 0) is None
+    assert _check_latent(32, 1024, 256, 0) == (1, 1024, 2, 0, 64)
+    # at most 64 heads: one head group, all waves busy in two tile phases
+    assert _check_latent(32, 2048, 256, 64, heads=64) == (8, 256, 1, 1, 256)
 
 
 def test_latent_attention_plan_properties(lib):
     for rows in list(range(1, 40)) + [64, 100, 128, 255, 256, 257, 4096]:
-        for k in (1, 31, 100, 128, 129, 2047, 2048, 2049, 4096, 65536):
+        for k in (1, 31, 100, 128, 129, 1025, 2047, 2048, 2049, 4096, 65536):
             for cap in (0, 100, 256, 512):
-                for recs in (0, rows, 4096):
-                    _check_latent(rows, k, cap, recs)
+                for recs in (0, rows, 2 * rows, 8192):
+                    for heads in (16, 64, 65, 128):
+                        _check_latent(rows, k, cap, recs, heads)
