@@ -130,7 +130,22 @@ def test_index_score_matches_oracle():
         assert np.all(np.isneginf(s[b, n:]))
 
 
-def test_topk_exact_on_shared_scores():
+# Row Top-K runs the register-resident kernel when the row stride is at most 65536 and the
+# streaming kernel above that: the exact tests below run at both strides (the wider one pads
+# the rows with -inf, which no row's visible range reaches).
+TOPK_STRIDES = (None, 70000)
+
+
+def _at_stride(s, ld):
+    if ld is None:
+        return s
+    wide = np.full((s.shape[0], ld), -np.inf, dtype=np.float32)
+    wide[:, :s.shape[1]] = s
+    return wide
+
+
+@pytest.mark.parametrize("ld", TOPK_STRIDES)
+def test_topk_exact_on_shared_scores(ld):
     """Both sides select from identical fp32 scores: identical sets, including ties."""
     rng = np.random.default_rng(0)
     wl = inputs.make("decode32k", num_seqs=4, ctx=[9000, 2048, 100, 3000])
@@ -140,18 +155,18 @@ def test_topk_exact_on_shared_scores():
     s[2, :] = 0.0
     s[2, ::3] = -0.0                             # +-0 ties
     s[3, :3000] = rng.integers(-3, 3, 3000)      # ties at the threshold
-    st = torch.from_numpy(s).cuda()
+    st = torch.from_numpy(_at_stride(s, ld)).cuda()
     idx = device.topk(dw, st, k=2048).cpu().numpy()
     ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
     np.testing.assert_array_equal(idx, ref)
 
 
-def test_topk_crowded_threshold_bin():
-    """Row Top-K when the first threshold bin and above hold more keys than the LDS list takes
-    (row 0: 20000 distinct scores in [1, 1.02), one bin of the first digit, so the further passes
-    re-read the row), when they fit (row 1: N(0,1) scores, ties broken by position in LDS), and
-    at the list's capacity of 7168 keys (row 2: exactly 7168 in the bin, the LDS path; row 3: one
-    more, the re-reading path)."""
+@pytest.mark.parametrize("ld", TOPK_STRIDES)
+def test_topk_crowded_threshold_bin(ld):
+    """Row Top-K when one bin of the first digit holds a whole row (row 0: 20000 distinct scores
+    in [1, 1.02), so all three digits are needed), with N(0,1) scores and ties broken by position
+    (row 1), and with 7168 and 7169 keys in the first threshold bin (rows 2 and 3: the streaming
+    kernel's LDS list capacity and one past it, where it re-reads the row)."""
     rng = np.random.default_rng(5)
     wl = inputs.make("decode32k", num_seqs=4, ctx=[20000, 12000, 9000, 9000])
     dw = device.to_device(wl)
@@ -163,10 +178,29 @@ def test_topk_crowded_threshold_bin():
         s[r, :9000] = (0.5 * rng.random(9000)).astype(np.float32)          # bins below [2, 2.5)
         sel = rng.permutation(9000)[:m]
         s[r, sel] = (2.0 + 0.4 * rng.permutation(m) / m).astype(np.float32)  # one first-digit bin
-    st = torch.from_numpy(s).cuda()
+    st = torch.from_numpy(_at_stride(s, ld)).cuda()
     idx = device.topk(dw, st, k=2048).cpu().numpy()
     ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
     np.testing.assert_array_equal(idx, ref)
+
+
+def test_topk_rows_at_the_register_kernel_limit():
+    """Rows of exactly 65536 visible scores (the register-resident kernel's limit), one of them
+    with a crowded threshold bin and ties, one short row, and the same rows through the
+    streaming kernel (stride 65537)."""
+    rng = np.random.default_rng(9)
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[65536, 65536, 5], seed_offset=9)
+    dw = device.to_device(wl)
+    s = np.full((3, 65536), -np.inf, dtype=np.float32)
+    s[0] = rng.standard_normal(65536).astype(np.float32)
+    s[1] = np.round(rng.standard_normal(65536) * 4).astype(np.float32)  # few distinct values
+    s[1, -3000:] = 1.0 + 1e-3 * rng.random(3000).astype(np.float32)     # the top bins, at the end
+    s[2, :5] = rng.standard_normal(5).astype(np.float32)
+    ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
+    for ld in (65536, 65537):
+        st = torch.from_numpy(_at_stride(s, ld if ld > 65536 else None)).cuda()
+        idx = device.topk(dw, st, k=2048).cpu().numpy()
+        np.testing.assert_array_equal(idx, ref, err_msg=f"stride {ld}")
 
 
 def test_sparse_attn_on_oracle_indices():
