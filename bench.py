@@ -102,8 +102,10 @@ def algorithmic_bytes(wl):
     return {"select": sel, "attention": attn, "step": step}
 
 
-# kernels of each launch the bench times (a launch may consist of several kernels)
-LAUNCH_KERNELS = {"select": ("k_decode_select",), "attention": ("k_sparse_attn", "k_attn_merge")}
+# kernels of each launch the bench times (a launch may consist of several kernels; the latent
+# attention kernel merges inside the launch, the other one is followed by k_attn_merge)
+LAUNCH_KERNELS = {"select": ("k_decode_select",),
+                  "attention": ("k_attn_latent", "k_sparse_attn", "k_attn_merge")}
 
 
 def write_traffic(workload, csvs, copy_gib):
@@ -126,13 +128,13 @@ def write_traffic(workload, csvs, copy_gib):
         res["calibration"][counter] = {"copy_bytes": known, "counter_kib": max(copies),
                                        "factor": factor}
         for launch, names in LAUNCH_KERNELS.items():
-            tot = 0.0
-            for n in names:
+            tot, seen = 0.0, False
+            for n in names:  # the kernels of this launch that the run dispatched
                 vals = [float(r["Counter_Value"]) for r in rows if n in r["Kernel_Name"]]
-                if not vals:
-                    break
-                tot += sum(vals) / len(vals) * 1024.0 * factor
-            else:
+                if vals:
+                    tot += sum(vals) / len(vals) * 1024.0 * factor
+                    seen = True
+            if seen:
                 per.setdefault(launch, {})[counter] = tot
     for launch, d in per.items():
         if len(d) == 2:
