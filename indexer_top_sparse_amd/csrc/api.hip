@@ -188,6 +188,8 @@ struct WsLayout {
     size_t err = 0, zero = 0, sync = 0, blocks = 0, idx = 0, slots = 0, part_o = 0, part_ml = 0,
            rsync = 0, total = 0;
     int row_recs = 0;  // merge records at rsync, one per (row, head group)
+    int seq_recs = 0;  // selection records per stage at sync; the fused two-stage selection's
+                       // token stage uses the records [seq_recs, 2 seq_recs)
 };
 
 // The regions that must hold zeros when a call starts (error word, zero row, selection and merge
@@ -205,7 +207,11 @@ WsLayout ws_layout(const sa_batch *b, int rows, const sa_kv *kv, int k, int bloc
     off += 2048;
     L.sync = off;
     const int nsr = seq_records >= 0 ? seq_records : b->num_seqs;
-    off = align256(off + sizeof(SelSync) * (size_t)nsr);
+    L.seq_recs = nsr;
+    // two stages' records when the selection is hierarchical (always with a fixed capacity, so
+    // that the offsets do not depend on the call)
+    const int stages = (block_k > 0 || seq_records >= 0) ? 2 : 1;
+    off = align256(off + sizeof(SelSync) * (size_t)nsr * stages);
     const int rmax = std::max(rows, b->num_seqs);
     if (kv || row_records >= 0) {
         L.rsync = off;  // merge records (the groups of a merging launch fit the device)
@@ -390,6 +396,86 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         void *args[] = {&a};
         hipError_t e = hipLaunchKernel(kern, dim3((unsigned)groups), dim3(threads), args, lds, st);
         if (e != hipSuccess) return hip_fail(e, "selection launch");
+    }
+    return SA_OK;
+}
+
+// Both stages of the hierarchical selection in one launch (k_decode_select_2l). The token
+// stage's chunk is planned as for a single-stage launch; the block stage's chunk is the
+// smallest multiple of 64 that needs no more workgroups per sequence than the token stage, so
+// the sequence's workgroups are the token stage's (host and kernel evaluate the same max).
+// Returns SA_ERR_UNSUPPORTED (nothing enqueued) when the fused kernel does not apply.
+sa_status run_select2l(const sa_batch *b, const sa_indexer *ix, const void *q_idx, const float *w,
+                       int k, int block_k, int32_t *blocks, int32_t *idx_out, int32_t *slots_out,
+                       uint8_t *ws, const WsLayout &L, hipStream_t st) {
+    void *kern = decode_select2l_kernel(ix->dim, ix->heads, (int)ix->key_dtype);
+    if (!kern) return SA_ERR_UNSUPPORTED;
+    const int threads = 512;
+    const int lp = log2i(b->page_size);
+    const int cus = device_cus();
+    auto lds_of = [&](int chunk1, int chunk2) {
+        return std::max(decode_select_dynamic_lds(1, chunk1, lp), decode_select_dynamic_lds(2, chunk2, lp));
+    };
+    const int occ0 = occupancy(kern, threads, lds_of(64, 64));
+    if (occ0 <= 0) return hip_fail(hipErrorInvalidValue, "occupancy query");
+    const int per_launch = std::max(1, occ0 * cus / 2);
+    for (int s0 = 0, nb = 0; s0 < b->num_seqs; s0 += nb) {
+        nb = std::min(per_launch, b->num_seqs - s0);
+        auto nc1 = [&](int i) { return ncand_host(1, b->ctx_lens_host[s0 + i], b->page_size, block_k); };
+        auto nc2 = [&](int i) { return ncand_host(2, b->ctx_lens_host[s0 + i], b->page_size, block_k); };
+        int occ = occ0, chunk1 = 64, chunk2 = 64;
+        int64_t groups = 0;
+        size_t lds = 0;
+        for (int iter = 0;; ++iter) {
+            const int cap = occ * cus;
+            if (nb > cap || iter > 8) return SA_ERR_UNSUPPORTED;
+            chunk2 = plan_chunk(nc2, nb, cap, &groups);
+            int need1 = 1;  // block-stage candidates per workgroup
+            for (int i = 0; i < nb; ++i)
+                need1 = std::max(need1, (nc1(i) + sel_groups(nc2(i), chunk2) - 1) / sel_groups(nc2(i), chunk2));
+            chunk1 = (need1 + 63) / 64 * 64;
+            lds = lds_of(chunk1, chunk2);
+            const int o = (chunk1 <= kSelMaxChunk && chunk2 <= kSelMaxChunk) ? occupancy(kern, threads, lds) : 0;
+            if (o <= 0) {
+                if (nb == 1) return SA_ERR_UNSUPPORTED;
+                nb = (nb + 1) / 2;
+                occ = occ0;
+                iter = -1;
+                continue;
+            }
+            if (o >= occ) break;
+            occ = o;
+        }
+        SelectArgs ab{}, ac{};
+        for (SelectArgs *a : {&ab, &ac}) {
+            a->num_seqs = nb;
+            a->lp = lp;
+            a->pages_per_seq = b->pages_per_seq;
+            a->heads = ix->heads;
+            a->block_k = block_k;
+            a->page_table = b->page_table + (int64_t)s0 * b->pages_per_seq;
+            a->ctx_lens = b->ctx_lens + s0;
+            a->q_idx = static_cast<const uint16_t *>(q_idx) + (int64_t)s0 * ix->heads * ix->dim;
+            a->w = w + (int64_t)s0 * ix->heads;
+            a->err = reinterpret_cast<uint32_t *>(ws + L.err);
+            a->spin_limit = spin_limit();
+        }
+        ab.chunk = chunk1;
+        ab.k = block_k;
+        ab.keys = static_cast<const uint8_t *>(ix->pooled);
+        ab.idx_out = blocks + (int64_t)s0 * block_k;
+        ab.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
+        ac.chunk = chunk2;
+        ac.k = k;
+        ac.keys = static_cast<const uint8_t *>(ix->keys);
+        ac.key_scale = ix->key_scale;
+        ac.blocks = blocks + (int64_t)s0 * block_k;
+        ac.idx_out = idx_out + (int64_t)s0 * k;
+        ac.slots_out = slots_out ? slots_out + (int64_t)s0 * k : nullptr;
+        ac.sync = reinterpret_cast<SelSync *>(ws + L.sync) + L.seq_recs + s0;
+        void *args[] = {&ab, &ac};
+        hipError_t e = hipLaunchKernel(kern, dim3((unsigned)groups), dim3(threads), args, lds, st);
+        if (e != hipSuccess) return hip_fail(e, "two-stage selection launch");
     }
     return SA_OK;
 }
@@ -649,6 +735,9 @@ static sa_status select_impl(const sa_batch *batch, const RowPlan &rp, const sa_
     sa_status st;
     if (block_k > 0) {
         int32_t *blocks = reinterpret_cast<int32_t *>(wsb + L.blocks);
+        // one launch for both stages when the fused kernel applies
+        st = run_select2l(batch, ix, q_idx, w, k, block_k, blocks, idx, slots, wsb, L, hs);
+        if (st != SA_ERR_UNSUPPORTED) return st;
         if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks, nullptr, wsb, L,
                              hs)) != SA_OK)
             return st;

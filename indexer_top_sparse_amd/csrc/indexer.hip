@@ -620,15 +620,12 @@ __host__ __device__ inline int chunk_table_entries(int mode, int chunk, int lp) 
     return mode == kBlocks ? chunk : (chunk >> lp) + 2;
 }
 
-template <int DIM, int HT, int KF, int MODE>
-__global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
-    constexpr bool FP8 = KF != kKeyBf16, MX = KF == kKeyMx;
-    extern __shared__ uint32_t s_key[];  // [chunk] keys, then the chunk address table
-    __shared__ SelShared sh;
-    __shared__ u32x4 s_stage[kSelWaves][256];  // per-wave key-tile transpose area (4 KiB)
+// ---- locate a workgroup's (sequence, chunk): chunk counts prefix over sequences, groups_of(ctx)
+//      giving a sequence's workgroups. Returns false for grid padding (never co-waited on).
+template <class GF>
+__device__ __forceinline__ bool select_locate(const SelectArgs &a, GF groups_of, SelShared &sh,
+                                              int &seq, int &chunk, int &G, int &ctx) {
     const int tid = threadIdx.x, l = lane_id();
-
-    // ---- locate this workgroup's (sequence, chunk): chunk counts prefix over sequences
     if (tid < 64) {
         uint32_t base = 0;
         int found_seq = -1, found_chunk = 0, found_G = 0, found_ctx = 0;
@@ -638,7 +635,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
             int ctx_b = 0;
             if (b < a.num_seqs) {
                 ctx_b = a.ctx_lens[b];
-                nchunks = sel_groups(ncand_of(MODE, ctx_b, a.lp, a.block_k), a.chunk);
+                nchunks = (uint32_t)groups_of(ctx_b);
             }
             const uint32_t incl = wave_incl_scan(nchunks);
             const uint32_t excl = base + incl - nchunks;
@@ -665,12 +662,26 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
         }
     }
     __syncthreads();
-    if (sh.res[0] == 0xFFFFFFFFu) return;  // grid padding (never co-waited on)
-    const int seq = sh.res[0], chunk = sh.res[1], G = sh.res[2], ctx = (int)sh.res[3];
+    if (sh.res[0] == 0xFFFFFFFFu) return false;
+    seq = sh.res[0];
+    chunk = sh.res[1];
+    G = sh.res[2];
+    ctx = (int)sh.res[3];
+    __syncthreads();  // sh.res is reused after this
+    return true;
+}
+
+// Everything a workgroup does once it knows its (sequence, chunk): the chunk's address table,
+// its scores as keys in LDS, the radix select across the G workgroups of the sequence (record
+// ss, barriers numbered from nbar on), the ordered emission and the leave step. ok0 = false
+// carries an expired wait of an earlier phase into this one's failure flag.
+template <int DIM, int HT, int KF, int MODE>
+__device__ __forceinline__ void select_run(const SelectArgs &a, int seq, int chunk, int G, int ctx,
+                                          SelSync *ss, uint32_t &nbar, bool ok0, uint32_t *s_key,
+                                          SelShared &sh, u32x4 (*s_stage)[256]) {
+    constexpr bool FP8 = KF != kKeyBf16, MX = KF == kKeyMx;
+    const int tid = threadIdx.x, l = lane_id();
     const int clen = a.chunk;
-    __syncthreads();  // sh.res is reused below
-    SelSync *ss = a.sync + seq;
-    uint32_t nbar = 0;  // barriers passed (see group_barrier)
     SeqCtx s;
     s.seq = seq;
     s.ctx = ctx;
@@ -697,7 +708,9 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
                 if (MODE == kTokens) {
                     cr.row[j] = s.pt[pg] * P;
                 } else {
-                    const int b = s.blocks[pg];
+                    // agent scope: in the fused two-stage launch the list was written by
+                    // workgroups on other XCDs moments ago
+                    const int b = (int)ld_agent(reinterpret_cast<const uint32_t *>(s.blocks + pg));
                     cr.blk[j] = b;
                     cr.row[j] = b >= 0 ? s.pt[b] * P : -1;
                 }
@@ -815,7 +828,7 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     uint32_t need = 0, total = 0;
     bool exact = false;  // every candidate in the threshold bin is selected
     uint32_t listn = 0;  // > 0: the threshold bin of the first pass is resolved through the list
-    bool ok = true;
+    bool ok = ok0;  // false: a wait of an earlier stage expired
     for (int pass = 0; pass < 3; ++pass) {
         const int bits = pass < 2 ? 11 : 10;
         const int shift = 32 - pbits - bits;
@@ -1231,6 +1244,52 @@ __global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) 
     }
 }
 
+template <int DIM, int HT, int KF, int MODE>
+__global__ __launch_bounds__(kSelThreads, 1) void k_decode_select(SelectArgs a) {
+    extern __shared__ uint32_t s_key[];  // [chunk] keys, then the chunk address table
+    __shared__ SelShared sh;
+    __shared__ u32x4 s_stage[kSelWaves][256];  // per-wave key-tile transpose area (4 KiB)
+    int seq, chunk, G, ctx;
+    if (!select_locate(
+            a, [&](int c) { return sel_groups(ncand_of(MODE, c, a.lp, a.block_k), a.chunk); }, sh,
+            seq, chunk, G, ctx))
+        return;
+    uint32_t nbar = 0;  // barriers passed (see group_barrier)
+    select_run<DIM, HT, KF, MODE>(a, seq, chunk, G, ctx, a.sync + seq, nbar, true, s_key, sh,
+                                  s_stage);
+}
+
+// Both stages of the hierarchical selection in one launch: the same workgroups score the block
+// summaries and keep the block_k best blocks (ab: mode kBlocks, bf16 summaries), meet once more,
+// then score the tokens of the kept blocks and keep the k best (ac: mode kCandidates). A
+// sequence has the workgroups of its larger stage; the host picks the block stage's chunk so
+// that this is the token stage. Each stage has its own record per sequence. The block list is
+// written with agent-scope stores and read back with agent-scope loads.
+template <int DIM, int HT, int KF>
+__global__ __launch_bounds__(kSelThreads, 1) void k_decode_select_2l(SelectArgs ab, SelectArgs ac) {
+    extern __shared__ uint32_t s_key[];  // the larger stage's keys and address table
+    __shared__ SelShared sh;
+    __shared__ u32x4 s_stage[kSelWaves][256];
+    int seq, chunk, G, ctx;
+    if (!select_locate(
+            ac,
+            [&](int c) {
+                return max(sel_groups(ncand_of(kBlocks, c, ab.lp, ab.block_k), ab.chunk),
+                           sel_groups(ncand_of(kCandidates, c, ac.lp, ac.block_k), ac.chunk));
+            },
+            sh, seq, chunk, G, ctx))
+        return;
+    uint32_t nb1 = 0;
+    select_run<DIM, HT, kKeyBf16, kBlocks>(ab, seq, chunk, G, ctx, ab.sync + seq, nb1, true, s_key,
+                                           sh, s_stage);
+    // every workgroup of the sequence is past its block stage (the block list, or the failure
+    // fill of its last workgroup, is complete) before any reads the list
+    uint32_t nb2 = 0;
+    const bool ok = group_barrier(&ac.sync[seq].count, (uint32_t)G, ac.err, nb2, ac.spin_limit);
+    select_run<DIM, HT, KF, kCandidates>(ac, seq, chunk, G, ctx, ac.sync + seq, nb2, ok, s_key, sh,
+                                         s_stage);
+}
+
 // ------------------------------------------------------------------ launchers
 template <int DIM, int HT, int KF>
 static hipError_t launch_score_t(const ScoreArgs &a, int rows, int64_t max_cols, hipStream_t st) {
@@ -1300,6 +1359,20 @@ void *decode_select_kernel(int dim, int heads, int key_fmt, int mode) {
     const bool small = heads <= 16;
     if (dim == 128) return small ? select_kernel_mode<128, 1>(key_fmt, mode) : select_kernel_mode<128, 4>(key_fmt, mode);
     return small ? select_kernel_mode<64, 1>(key_fmt, mode) : select_kernel_mode<64, 4>(key_fmt, mode);
+}
+
+// the fused two-stage selection (bf16 or E4M3 keys; MXFP8 keys have no two-level path)
+template <int DIM, int HT>
+static void *select2l_kernel_fmt(int key_fmt) {
+    if (key_fmt == kKeyE4M3) return reinterpret_cast<void *>(&k_decode_select_2l<DIM, HT, kKeyE4M3>);
+    if (key_fmt == kKeyBf16) return reinterpret_cast<void *>(&k_decode_select_2l<DIM, HT, kKeyBf16>);
+    return nullptr;
+}
+
+void *decode_select2l_kernel(int dim, int heads, int key_fmt) {
+    const bool small = heads <= 16;
+    if (dim == 128) return small ? select2l_kernel_fmt<128, 1>(key_fmt) : select2l_kernel_fmt<128, 4>(key_fmt);
+    return small ? select2l_kernel_fmt<64, 1>(key_fmt) : select2l_kernel_fmt<64, 4>(key_fmt);
 }
 
 size_t decode_select_static_lds() { return sizeof(SelShared); }

@@ -137,6 +137,8 @@ int lat_grid_host(int rows, int units, int xcd_align);
 hipError_t launch_index_score(const ScoreArgs &a, int dim, int heads, int key_fmt, int rows,
                               int64_t max_cols, hipStream_t st);
 void *decode_select_kernel(int dim, int heads, int key_fmt, int mode);  // null: unsupported
+// both stages of the hierarchical selection in one launch, arguments (blocks stage, tokens stage)
+void *decode_select2l_kernel(int dim, int heads, int key_fmt);        // null: unsupported
 size_t decode_select_static_lds();
 size_t decode_select_dynamic_lds(int mode, int chunk, int lp);
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);

@@ -37,16 +37,17 @@ class _SpinLimit:
         os.environ.pop("SA_SPIN_LIMIT", None)
 
 
-def _records_are_zero(ws, num_seqs, rows):
-    """Selection records (counters, flag, histograms) and the merge records (one per row and
-    head group, two head groups at most) are all zero."""
+def _records_are_zero(ws, num_seqs, rows, stages=1):
+    """Selection records (counters, flag, histograms; one per sequence and stage of the
+    selection) and the merge records (one per row and head group, two head groups at most) are
+    all zero."""
     h = ws.cpu().numpy()
     base = 256 + 2048
-    for b in range(num_seqs):
+    for b in range(stages * num_seqs):
         rec = h[base + b * SEL_BYTES: base + b * SEL_BYTES + SEL_RECORD]
         if rec.any():
             return f"selection record {b} not zero"
-    rs = (base + num_seqs * SEL_BYTES + 255) // 256 * 256
+    rs = (base + stages * num_seqs * SEL_BYTES + 255) // 256 * 256
     if h[rs: rs + 2 * rows * 64].any():
         return "merge records not zero"
     return ""
@@ -141,3 +142,41 @@ def test_expired_split_barrier_in_attention_alone():
     assert B.workspace_error(ws) == 0
     assert torch.equal(out2.view(torch.int16), out_ref.view(torch.int16))
     np.testing.assert_array_equal(idx.cpu().numpy()[:, :1] >= 0, True)
+
+
+def test_expired_waits_in_the_two_stage_selection():
+    """The fused block-then-token selection with every wait expiring: each sequence's index set
+    is the normal one or all -1, the records of both stages return to zero, and the next call is
+    exact."""
+    torch.cuda.set_device(0)
+    wl = inputs.make("long1m", num_seqs=2, ctx=[200000, 3000], seed_offset=47)
+    _say("two-level B=2 block_k=512: reference, forced failure, then normal again")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out_ref, idx_ref = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert B.workspace_error(ws) == 0
+    out_ref, idx_ref = out_ref.cpu(), idx_ref.cpu()
+    with _SpinLimit(0):
+        out_f, idx_f = device.decode_step(dw, ws)
+        torch.cuda.synchronize()
+    err = B.workspace_error(ws)
+    out_f, idx_f = out_f.cpu(), idx_f.cpu()
+    failed = 0
+    for b in range(wl.num_seqs):
+        sel_failed = bool((idx_f[b] == -1).all())
+        if sel_failed:
+            failed += 1
+            assert bool((out_f[b].float() == 0).all()), f"seq {b}: failed selection, output not 0"
+        else:
+            assert torch.equal(idx_f[b], idx_ref[b]), f"seq {b}: index set neither normal nor -1"
+    _say(f"sequences with the failure result: {failed} of {wl.num_seqs}; error word {err}")
+    assert failed > 0 and err & 1
+    msg = _records_are_zero(ws, wl.num_seqs, wl.num_seqs, stages=2)
+    assert msg == "", msg
+    ws[:4].zero_()
+    out2, idx2 = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert B.workspace_error(ws) == 0
+    assert torch.equal(idx2.cpu(), idx_ref)
+    assert torch.equal(out2.cpu().view(torch.int16), out_ref.view(torch.int16))
