@@ -482,6 +482,74 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     return x;
 }
 
+// The merge of a (row, head group): units [u0, u1) of every split's partial block combined in
+// split order (running max and rescale, as an online softmax over the splits), written to the
+// output with agent-scope stores. MU units per thread and MS splits have their loads in flight
+// together (MU * MS <= 16 keeps the loads' registers below the kernel's budget).
+template <int HPW, int MU, int MS>
+__device__ __forceinline__ void lat_merge_units(const AttnArgs &a, int row, int hgi, int64_t grp,
+                                                int64_t blk_elems, int u0, int u1) {
+    const int tid = threadIdx.x;
+    for (int ub = u0 + tid; ub < u1; ub += MU * kLatThreads) {
+        int hl[MU];
+        bool on[MU];
+        float M[MU], Lsum[MU], acc[MU][4];
+#pragma unroll
+        for (int i = 0; i < MU; ++i) {
+            const int u = ub + i * kLatThreads;
+            hl[i] = 16 * (u >> 11) + (u & 15);  // head inside the group
+            on[i] = u < u1 && HPW * hgi + hl[i] < a.heads_q;
+            if (!on[i]) hl[i] = 0;  // (loads stay in bounds; results unused)
+            M[i] = -__builtin_inff();
+            Lsum[i] = 0.f;
+            acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.f;
+        }
+        for (int s0 = 0; s0 < a.splits; s0 += MS) {
+            uint64_t ml[MU][MS], v[MU][MS];
+#pragma unroll
+            for (int x = 0; x < MS; ++x) {
+                const int64_t gs = grp * a.splits + min(s0 + x, a.splits - 1);
+#pragma unroll
+                for (int i = 0; i < MU; ++i) {
+                    const int u = on[i] ? ub + i * kLatThreads : u0;
+                    ml[i][x] = ld_agent_u64(a.part_ml + 2 * (gs * HPW + hl[i]));
+                    v[i][x] = ld_agent_u64(a.part_o + gs * blk_elems + 4 * (int64_t)u);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MU; ++i)
+#pragma unroll
+                for (int x = 0; x < MS; ++x) {
+                    const float ms = __uint_as_float((uint32_t)ml[i][x]);
+                    const float ls = __uint_as_float((uint32_t)(ml[i][x] >> 32));
+                    if (s0 + x >= a.splits || !(ls > 0.f)) continue;
+                    const float mn = fmaxf(M[i], ms);
+                    const float c = __builtin_amdgcn_exp2f(M[i] - mn);  // 0 while nothing is summed
+                    const float wgt = __builtin_amdgcn_exp2f(ms - mn) * ls;
+                    Lsum[i] = fmaf(Lsum[i], c, wgt);
+                    const uint32_t lo32 = (uint32_t)v[i][x], hi32 = (uint32_t)(v[i][x] >> 32);
+                    acc[i][0] = fmaf(acc[i][0], c, wgt * bf16_lo(lo32));
+                    acc[i][1] = fmaf(acc[i][1], c, wgt * bf16_hi(lo32));
+                    acc[i][2] = fmaf(acc[i][2], c, wgt * bf16_lo(hi32));
+                    acc[i][3] = fmaf(acc[i][3], c, wgt * bf16_hi(hi32));
+                    M[i] = mn;
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < MU; ++i) {
+            if (!on[i]) continue;
+            const int u = ub + i * kLatThreads;
+            const int un = (u >> 6) & 31, ug = (u >> 4) & 3;
+            const int hh = HPW * hgi + hl[i];
+            const float il = Lsum[i] > 0.f ? 1.f / Lsum[i] : 0.f;
+            // agent scope: a failure fill by the group's last split to leave lands after it
+            st_agent_u64(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug,
+                         (uint64_t)pack_bf16x2(acc[i][0] * il, acc[i][1] * il) |
+                             ((uint64_t)pack_bf16x2(acc[i][2] * il, acc[i][3] * il) << 32));
+        }
+    }
+}
+
 // Per tile-phase count T: T = 1 runs 8 waves x 16 heads (128 heads) on every tile; T = 2 runs 4
 // head groups x 2 phases (64 heads), the phases taking alternate tiles.
 template <int T>
@@ -526,8 +594,10 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     const int head = head0 + L;
     const bool live_wave = head0 < a.heads_q;
     const bool live = head < a.heads_q;
+    //      With T = 2 the two phases of a head group need the same fragments: phase 0 loads
+    //      them and hands them to phase 1 through LDS (below).
     u32x4 qf[kLatKS];
-    {
+    if (T == 1 || tp == 0) {
         const uint16_t *qr = a.q + ((int64_t)row * a.heads_q + (live ? head : 0)) * kLatQK + 8 * g;
 #pragma unroll
         for (int s = 0; s < kLatKS; ++s) qf[s] = ldg16(qr + 32 * s);
@@ -550,7 +620,17 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     // only vector-memory operations in flight are this wave's tile copies, which the waits
     // below count exactly
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // the slot table is complete
+    // T = 2: the query fragments through the ring's slots 2 and 3 ([head group][k-step][lane],
+    // 73,728 bytes = two tiles), which the copies of step 1 overwrite only after the loop's first
+    // barrier, when every wave has read them
+    u32x4 *qx = reinterpret_cast<u32x4 *>(lds + 2 * kLatTileB) + (hsub * kLatKS) * 64 + l;
+    if (T == 2 && tp == 0 && live_wave)
+#pragma unroll
+        for (int s = 0; s < kLatKS; ++s) qx[64 * s] = qf[s];
+    __syncthreads();  // the slot table (and the handed-over query fragments) are complete
+    if (T == 2 && tp == 1 && live_wave)
+#pragma unroll
+        for (int s = 0; s < kLatKS; ++s) qf[s] = qx[64 * s];
     // ---- staged tile layout: 16-byte chunk c of row r lives at byte
     //      4096 (c / 8) + 128 r + 16 ((c % 8) ^ swz(r)), i.e. nine column groups of 128 bytes per
     //      row, each group holding the 32 rows. Copy block b (1 KiB) fills group b / 4, rows
@@ -790,73 +870,18 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     uint32_t nbar = 0;
     const bool ok = group_barrier(&rs[0], (uint32_t)a.splits, a.err, nbar, a.spin_limit);
     // ---- merge: split s combines the units [s U / S, (s + 1) U / S) of every split's block
-    //      (U = units per block). A thread takes up to 4 units kLatThreads apart (consecutive
-    //      threads read consecutive units) and issues the loads of all of them, for up to 4
-    //      splits, before it combines any: one memory round trip per 4 splits.
+    //      (U = units per block). Consecutive threads take consecutive units; a thread issues
+    //      the loads of MU units (kLatThreads apart) for MS splits before it combines any: with
+    //      few splits 4 units x 4 splits, with many 1 unit x 16 splits, so that one memory round
+    //      trip usually covers everything a thread merges.
     const int units = blk_heads * kLatV / 4;
     const int u0 = (int)((int64_t)units * split / a.splits);
     const int u1 = (int)((int64_t)units * (split + 1) / a.splits);
-    constexpr int kMS = 4;  // splits whose loads are in flight together
-    constexpr int kMU = 4;  // units per thread whose loads are in flight together
     if (ok) {
-        for (int ub = u0 + tid; ub < u1; ub += kMU * kLatThreads) {
-            int hl[kMU];
-            bool on[kMU];
-            float M[kMU], Lsum[kMU], acc[kMU][4];
-#pragma unroll
-            for (int i = 0; i < kMU; ++i) {
-                const int u = ub + i * kLatThreads;
-                hl[i] = 16 * (u >> 11) + (u & 15);  // head inside the group
-                on[i] = u < u1 && C::kHPW * hgi + hl[i] < a.heads_q;
-                if (!on[i]) hl[i] = 0;  // (loads stay in bounds; results unused)
-                M[i] = -__builtin_inff();
-                Lsum[i] = 0.f;
-                acc[i][0] = acc[i][1] = acc[i][2] = acc[i][3] = 0.f;
-            }
-            for (int s0 = 0; s0 < a.splits; s0 += kMS) {
-                uint64_t ml[kMU][kMS], v[kMU][kMS];
-#pragma unroll
-                for (int x = 0; x < kMS; ++x) {
-                    const int64_t gs = grp * a.splits + min(s0 + x, a.splits - 1);
-#pragma unroll
-                    for (int i = 0; i < kMU; ++i) {
-                        const int u = on[i] ? ub + i * kLatThreads : u0;
-                        ml[i][x] = ld_agent_u64(a.part_ml + 2 * (gs * C::kHPW + hl[i]));
-                        v[i][x] = ld_agent_u64(a.part_o + gs * blk_elems + 4 * (int64_t)u);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < kMU; ++i)
-#pragma unroll
-                    for (int x = 0; x < kMS; ++x) {
-                        const float ms = __uint_as_float((uint32_t)ml[i][x]);
-                        const float ls = __uint_as_float((uint32_t)(ml[i][x] >> 32));
-                        if (s0 + x >= a.splits || !(ls > 0.f)) continue;
-                        const float mn = fmaxf(M[i], ms);
-                        const float c = __builtin_amdgcn_exp2f(M[i] - mn);  // 0 while nothing is summed
-                        const float wgt = __builtin_amdgcn_exp2f(ms - mn) * ls;
-                        Lsum[i] = fmaf(Lsum[i], c, wgt);
-                        const uint32_t lo32 = (uint32_t)v[i][x], hi32 = (uint32_t)(v[i][x] >> 32);
-                        acc[i][0] = fmaf(acc[i][0], c, wgt * bf16_lo(lo32));
-                        acc[i][1] = fmaf(acc[i][1], c, wgt * bf16_hi(lo32));
-                        acc[i][2] = fmaf(acc[i][2], c, wgt * bf16_lo(hi32));
-                        acc[i][3] = fmaf(acc[i][3], c, wgt * bf16_hi(hi32));
-                        M[i] = mn;
-                    }
-            }
-#pragma unroll
-            for (int i = 0; i < kMU; ++i) {
-                if (!on[i]) continue;
-                const int u = ub + i * kLatThreads;
-                const int un = (u >> 6) & 31, ug = (u >> 4) & 3;
-                const int hh = C::kHPW * hgi + hl[i];
-                const float il = Lsum[i] > 0.f ? 1.f / Lsum[i] : 0.f;
-                // agent scope: a failure fill by the group's last split to leave lands after it
-                st_agent_u64(a.out + ((int64_t)row * a.heads_q + hh) * kLatV + 16 * un + 4 * ug,
-                             (uint64_t)pack_bf16x2(acc[i][0] * il, acc[i][1] * il) |
-                                 ((uint64_t)pack_bf16x2(acc[i][2] * il, acc[i][3] * il) << 32));
-            }
-        }
+        if (a.splits <= 4)
+            lat_merge_units<C::kHPW, 4, 4>(a, row, hgi, grp, blk_elems, u0, u1);
+        else
+            lat_merge_units<C::kHPW, 1, 16>(a, row, hgi, grp, blk_elems, u0, u1);
     } else if (tid == 0) {
         __hip_atomic_fetch_or(&rs[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
