@@ -94,6 +94,18 @@ typedef struct sa_batch {
     const int32_t *ctx_lens_host; /* host   [num_seqs]: the same values (planning, validation) */
     const int32_t *q_indptr;      /* device [num_seqs+1] query-row offsets, or NULL (decode) */
     const int32_t *q_indptr_host; /* host copy of q_indptr; NULL exactly when q_indptr is NULL */
+    /* Selection reuse for requests that share a history ([SameDay] §3.1: requests sharing a
+     * history prefix can reuse selection results). NULL, or device [num_seqs] with a host copy:
+     * reuse[s] = -1, or the index of an earlier sequence whose index set sequence s takes over.
+     * The caller guarantees what makes the two selections equal: the same context length, the
+     * same key cache contents at every position (typically the same pages), and the same
+     * indexer query row and head weights. The fused selection (sa_index_select,
+     * sa_block_select, sa_decode_step, sa_decode_step_noalloc) then scores and selects only
+     * the other sequences and copies the index sets (and, in the fused step, the physical rows)
+     * to the reusing ones; the attention still runs for every sequence. Other entry points
+     * ignore it. Host-checked: -1 <= reuse[s] < s, reuse[reuse[s]] = -1, equal lengths. */
+    const int32_t *reuse;
+    const int32_t *reuse_host;
 } sa_batch;
 
 /* The lightweight indexer's cache ([CANN] §1 and §2.1). One key row of `dim` entries per token,

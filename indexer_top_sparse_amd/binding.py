@@ -29,7 +29,8 @@ class sa_batch(C.Structure):
                 ("pages_per_seq", C.c_int32), ("num_pages", C.c_int32),
                 ("page_table", C.c_void_p), ("ctx_lens", C.c_void_p),
                 ("ctx_lens_host", C.c_void_p), ("q_indptr", C.c_void_p),
-                ("q_indptr_host", C.c_void_p)]
+                ("q_indptr_host", C.c_void_p), ("reuse", C.c_void_p),
+                ("reuse_host", C.c_void_p)]
 
 
 class sa_indexer(C.Structure):
@@ -143,7 +144,7 @@ class Batch:
 
     def __init__(self, page_table: torch.Tensor, ctx_lens: torch.Tensor, ctx_lens_host,
                  page_size: int, num_pages: int, q_indptr: torch.Tensor | None = None,
-                 q_indptr_host=None):
+                 q_indptr_host=None, reuse: torch.Tensor | None = None, reuse_host=None):
         self._pt = page_table
         self._ctx = ctx_lens
         self._ctx_host = (C.c_int32 * len(ctx_lens_host))(*[int(x) for x in ctx_lens_host])
@@ -151,11 +152,18 @@ class Batch:
         self._qi_host = None
         if q_indptr is not None:
             self._qi_host = (C.c_int32 * len(q_indptr_host))(*[int(x) for x in q_indptr_host])
+        self._reuse = reuse
+        self._reuse_host = None
+        if reuse is not None:
+            self._reuse_host = (C.c_int32 * len(reuse_host))(*[int(x) for x in reuse_host])
         self.s = sa_batch(len(ctx_lens_host), page_size, page_table.shape[1], num_pages,
                           page_table.data_ptr(), ctx_lens.data_ptr(),
                           C.cast(self._ctx_host, C.c_void_p),
                           q_indptr.data_ptr() if q_indptr is not None else None,
                           C.cast(self._qi_host, C.c_void_p) if self._qi_host is not None
+                          else None,
+                          reuse.data_ptr() if reuse is not None else None,
+                          C.cast(self._reuse_host, C.c_void_p) if self._reuse_host is not None
                           else None)
 
 

@@ -43,6 +43,9 @@ struct RowPlan {
     int64_t max_pos = -1;
 };
 
+// Sequence s takes over another sequence's selection (sa_batch.reuse).
+bool reuses(const sa_batch *b, int s) { return b->reuse_host && b->reuse_host[s] >= 0; }
+
 sa_status check_batch(const sa_batch *b, RowPlan *rp) {
     if (!b) return fail(SA_ERR_INVALID, "batch is NULL");
     if (b->num_seqs < 1) return fail(SA_ERR_INVALID, "num_seqs must be >= 1");
@@ -56,6 +59,16 @@ sa_status check_batch(const sa_batch *b, RowPlan *rp) {
         return fail(SA_ERR_INVALID, "page_table, ctx_lens and ctx_lens_host are required");
     if ((b->q_indptr == nullptr) != (b->q_indptr_host == nullptr))
         return fail(SA_ERR_INVALID, "q_indptr and q_indptr_host must both be set or both NULL");
+    if ((b->reuse == nullptr) != (b->reuse_host == nullptr))
+        return fail(SA_ERR_INVALID, "reuse and reuse_host must both be set or both NULL");
+    if (b->reuse_host)
+        for (int s = 0; s < b->num_seqs; ++s) {
+            const int r = b->reuse_host[s];
+            if (r < -1 || r >= s)
+                return fail(SA_ERR_INVALID, "reuse[s] must be -1 or an earlier sequence");
+            if (r >= 0 && (b->reuse_host[r] != -1 || b->ctx_lens_host[r] != b->ctx_lens_host[s]))
+                return fail(SA_ERR_INVALID, "reuse[s] must name a sequence that selects itself, of the same length");
+        }
     const int64_t cap = (int64_t)b->pages_per_seq * b->page_size;
     RowPlan p;
     for (int s = 0; s < b->num_seqs; ++s) {
@@ -302,14 +315,18 @@ int ncand_host(int mode, int ctx, int page_size, int block_k) {
 
 // The chunk of a selection launch: the smallest multiple of 64 whose workgroups (sel_groups per
 // sequence, at most kMaxGroupsPerSeq each) all fit in `cap` resident workgroups, for n <= cap
-// sequences with nc_of(i) candidates; *groups gets the launch's workgroups.
+// sequences with nc_of(i) candidates (< 0: a sequence that reuses another's selection, with no
+// workgroups); *groups gets the launch's workgroups.
 template <class F>
 int plan_chunk(F nc_of, int n, int cap, int64_t *groups) {
     int nc_max = 0;
     for (int i = 0; i < n; ++i) nc_max = std::max(nc_max, nc_of(i));
     auto total_groups = [&](int c) {
         int64_t gsum = 0;
-        for (int i = 0; i < n; ++i) gsum += sel_groups(nc_of(i), c);
+        for (int i = 0; i < n; ++i) {
+            const int nc = nc_of(i);
+            gsum += nc < 0 ? 0 : sel_groups(nc, c);
+        }
         return gsum;
     };
     int lo = std::max(1, (nc_max + kMaxGroupsPerSeq - 1) / kMaxGroupsPerSeq);
@@ -353,7 +370,9 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
             const int cap = occ * cus;
             if (nb > cap || iter > 8) return fail(SA_ERR_UNSUPPORTED, "selection does not fit co-resident on this device");
             chunk = plan_chunk(
-                [&](int i) { return ncand_host(mode, b->ctx_lens_host[s0 + i], b->page_size, block_k); },
+                [&](int i) {
+                    return reuses(b, s0 + i) ? -1 : ncand_host(mode, b->ctx_lens_host[s0 + i], b->page_size, block_k);
+                },
                 nb, cap, &groups);
             lds = decode_select_dynamic_lds(mode, chunk, lp);
             const int o = chunk <= kSelMaxChunk ? occupancy(kern, threads, lds) : 0;
@@ -388,6 +407,8 @@ sa_status run_select(const sa_batch *b, const sa_indexer *ix, const void *q_idx,
         a.sync = reinterpret_cast<SelSync *>(ws + L.sync) + s0;
         a.err = reinterpret_cast<uint32_t *>(ws + L.err);
         a.spin_limit = spin_limit();
+        a.reuse = b->reuse ? b->reuse + s0 : nullptr;
+        if (groups == 0) continue;  // every sequence of this launch reuses another's selection
         // The grid never exceeds what the device holds at once, so every workgroup becomes
         // resident once the work queued before it has drained, and the waits between
         // workgroups of a sequence end; the waits are also spin-bounded. A plain launch is
@@ -422,7 +443,9 @@ sa_status run_select2l(const sa_batch *b, const sa_indexer *ix, const void *q_id
     for (int s0 = 0, nb = 0; s0 < b->num_seqs; s0 += nb) {
         nb = std::min(per_launch, b->num_seqs - s0);
         auto nc1 = [&](int i) { return ncand_host(1, b->ctx_lens_host[s0 + i], b->page_size, block_k); };
-        auto nc2 = [&](int i) { return ncand_host(2, b->ctx_lens_host[s0 + i], b->page_size, block_k); };
+        auto nc2 = [&](int i) {
+            return reuses(b, s0 + i) ? -1 : ncand_host(2, b->ctx_lens_host[s0 + i], b->page_size, block_k);
+        };
         int occ = occ0, chunk1 = 64, chunk2 = 64;
         int64_t groups = 0;
         size_t lds = 0;
@@ -431,8 +454,11 @@ sa_status run_select2l(const sa_batch *b, const sa_indexer *ix, const void *q_id
             if (nb > cap || iter > 8) return SA_ERR_UNSUPPORTED;
             chunk2 = plan_chunk(nc2, nb, cap, &groups);
             int need1 = 1;  // block-stage candidates per workgroup
-            for (int i = 0; i < nb; ++i)
-                need1 = std::max(need1, (nc1(i) + sel_groups(nc2(i), chunk2) - 1) / sel_groups(nc2(i), chunk2));
+            for (int i = 0; i < nb; ++i) {
+                if (nc2(i) < 0) continue;
+                const int g2 = sel_groups(nc2(i), chunk2);
+                need1 = std::max(need1, (nc1(i) + g2 - 1) / g2);
+            }
             chunk1 = (need1 + 63) / 64 * 64;
             lds = lds_of(chunk1, chunk2);
             const int o = (chunk1 <= kSelMaxChunk && chunk2 <= kSelMaxChunk) ? occupancy(kern, threads, lds) : 0;
@@ -459,7 +485,9 @@ sa_status run_select2l(const sa_batch *b, const sa_indexer *ix, const void *q_id
             a->w = w + (int64_t)s0 * ix->heads;
             a->err = reinterpret_cast<uint32_t *>(ws + L.err);
             a->spin_limit = spin_limit();
+            a->reuse = b->reuse ? b->reuse + s0 : nullptr;
         }
+        if (groups == 0) continue;  // every sequence of this launch reuses another's selection
         ab.chunk = chunk1;
         ab.k = block_k;
         ab.keys = static_cast<const uint8_t *>(ix->pooled);
@@ -727,11 +755,29 @@ sa_status sa_sparse_attn(const sa_batch *batch, const sa_kv *kv, const void *q,
                     static_cast<hipStream_t>(stream));
 }
 
+static sa_status select_impl_sources(const sa_batch *batch, const sa_indexer *ix,
+                                     const void *q_idx, const float *w, int32_t k,
+                                     int32_t block_k, int32_t *idx, int32_t *slots, uint8_t *wsb,
+                                     const WsLayout &L, hipStream_t hs);
+
+// The selection of every sequence: the sequences that select themselves, then (sa_batch.reuse)
+// the copies to those that reuse their selection.
 static sa_status select_impl(const sa_batch *batch, const RowPlan &rp, const sa_indexer *ix,
                              const void *q_idx, const float *w, int32_t k, int32_t block_k,
                              int32_t *idx, int32_t *slots, uint8_t *wsb, const WsLayout &L,
                              hipStream_t hs) {
     (void)rp;
+    sa_status st = select_impl_sources(batch, ix, q_idx, w, k, block_k, idx, slots, wsb, L, hs);
+    if (st != SA_OK || !batch->reuse) return st;
+    hipError_t e = launch_reuse_copy(batch->reuse, batch->num_seqs, k, idx, slots, hs);
+    if (e != hipSuccess) return hip_fail(e, "selection reuse copy");
+    return SA_OK;
+}
+
+static sa_status select_impl_sources(const sa_batch *batch, const sa_indexer *ix,
+                                     const void *q_idx, const float *w, int32_t k,
+                                     int32_t block_k, int32_t *idx, int32_t *slots, uint8_t *wsb,
+                                     const WsLayout &L, hipStream_t hs) {
     sa_status st;
     if (block_k > 0) {
         int32_t *blocks = reinterpret_cast<int32_t *>(wsb + L.blocks);
@@ -786,8 +832,13 @@ sa_status sa_block_select(const sa_batch *batch, const sa_indexer *ix, const voi
     if (!blocks_out) return fail(SA_ERR_INVALID, "blocks_out is required");
     const WsLayout L = ws_layout(batch, rp.rows, nullptr, block_k, block_k);
     if ((st = check_ws(ws, ws_bytes, L.total)) != SA_OK) return st;
-    return run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks_out, nullptr,
-                      static_cast<uint8_t *>(ws), L, static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = run_select(batch, ix, q_idx, w, 1, block_k, block_k, nullptr, blocks_out, nullptr,
+                         static_cast<uint8_t *>(ws), L, hs)) != SA_OK || !batch->reuse)
+        return st;
+    hipError_t e = launch_reuse_copy(batch->reuse, batch->num_seqs, block_k, blocks_out, nullptr, hs);
+    if (e != hipSuccess) return hip_fail(e, "selection reuse copy");
+    return SA_OK;
 }
 
 sa_status sa_decode_step(const sa_batch *batch, const sa_indexer *ix, const sa_kv *kv,

@@ -635,7 +635,8 @@ __device__ __forceinline__ bool select_locate(const SelectArgs &a, GF groups_of,
             int ctx_b = 0;
             if (b < a.num_seqs) {
                 ctx_b = a.ctx_lens[b];
-                nchunks = (uint32_t)groups_of(ctx_b);
+                // a sequence that reuses another's selection has no workgroups
+                nchunks = (a.reuse && a.reuse[b] >= 0) ? 0u : (uint32_t)groups_of(ctx_b);
             }
             const uint32_t incl = wave_incl_scan(nchunks);
             const uint32_t excl = base + incl - nchunks;
@@ -1359,6 +1360,24 @@ void *decode_select_kernel(int dim, int heads, int key_fmt, int mode) {
     const bool small = heads <= 16;
     if (dim == 128) return small ? select_kernel_mode<128, 1>(key_fmt, mode) : select_kernel_mode<128, 4>(key_fmt, mode);
     return small ? select_kernel_mode<64, 1>(key_fmt, mode) : select_kernel_mode<64, 4>(key_fmt, mode);
+}
+
+// Selection reuse: sequence s with reuse[s] >= 0 takes row reuse[s] (index set, and physical
+// rows when given) once the selection of the other sequences is complete.
+__global__ __launch_bounds__(256) void k_reuse_copy(const int32_t *reuse, int k, int32_t *idx,
+                                                    int32_t *slots) {
+    const int s = blockIdx.x, r = reuse[s];
+    if (r < 0) return;
+    for (int j = threadIdx.x; j < k; j += 256) {
+        idx[(int64_t)s * k + j] = idx[(int64_t)r * k + j];
+        if (slots) slots[(int64_t)s * k + j] = slots[(int64_t)r * k + j];
+    }
+}
+
+hipError_t launch_reuse_copy(const int32_t *reuse, int num_seqs, int k, int32_t *idx,
+                             int32_t *slots, hipStream_t st) {
+    hipLaunchKernelGGL(k_reuse_copy, dim3((unsigned)num_seqs), dim3(256), 0, st, reuse, k, idx, slots);
+    return hipGetLastError();
 }
 
 // the fused two-stage selection (bf16 or E4M3 keys; MXFP8 keys have no two-level path)

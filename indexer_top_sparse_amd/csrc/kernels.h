@@ -88,6 +88,8 @@ struct SelectArgs {
     SelSync *sync;
     uint32_t *err;
     uint32_t spin_limit;  // polls of a cross-workgroup wait before it expires
+    const int32_t *reuse; // [num_seqs] >= 0: the sequence reuses another's selection (no
+                          // workgroups here), or null
 };
 
 struct TopkArgs {
@@ -142,6 +144,10 @@ void *decode_select2l_kernel(int dim, int heads, int key_fmt);        // null: u
 size_t decode_select_static_lds();
 size_t decode_select_dynamic_lds(int mode, int chunk, int lp);
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st);
+// rows of sequences with reuse[s] >= 0 copied from row reuse[s] (rows of k entries; slots may
+// be null)
+hipError_t launch_reuse_copy(const int32_t *reuse, int num_seqs, int k, int32_t *idx,
+                             int32_t *slots, hipStream_t st);
 // kv_fmt: 0 bf16, 1 E4M3 with a row scale, 3 E4M3 with a scale per 128-entry tile (sa_dtype)
 hipError_t launch_sparse_attn(const AttnArgs &a, int dqk, int dv, bool sep_v, int kv_fmt,
                               hipStream_t st);

@@ -200,3 +200,31 @@ def test_noalloc_limits_are_checked_on_the_host(lib):
     assert b"48 MiB" in lib.sa_last_error()
     # argument checks come first, as for sa_decode_step
     assert _decode_noalloc(lib, a, k=0) == B.SA_ERR_INVALID
+
+
+def test_selection_reuse_is_validated_on_the_host(lib):
+    """sa_batch.reuse: -1 or an earlier sequence that selects itself, of the same length."""
+    a = _FakeDev(B_=3, ctx=[100, 7, 100])
+
+    def with_reuse(r):
+        t = torch.tensor(r, dtype=torch.int32)
+        return B.Batch(a.pt, a.ctx, [100, 7, 100], 64, 8, reuse=t, reuse_host=r)
+
+    for bad in ([-1, 2, -1],   # names a later sequence
+                [-1, -1, 2],   # names itself
+                [-1, 0, -1],   # different lengths (100 and 7)
+                [-1, -1, -2]):
+        b = with_reuse(bad)
+        assert _decode(lib, a, batch=C.byref(b.s)) == B.SA_ERR_INVALID, bad
+        assert b"reuse" in lib.sa_last_error()
+    a2 = _FakeDev(B_=3, ctx=[100, 100, 100])
+    t = torch.tensor([-1, 0, 1], dtype=torch.int32)  # 2 names 1, which itself reuses 0
+    b = B.Batch(a2.pt, a2.ctx, [100, 100, 100], 64, 8, reuse=t, reuse_host=[-1, 0, 1])
+    assert _decode(lib, a2, batch=C.byref(b.s)) == B.SA_ERR_INVALID
+    # a valid reuse passes validation (the call then stops at the missing workspace)
+    b = with_reuse([-1, -1, 0])
+    assert _decode(lib, a, batch=C.byref(b.s)) == B.SA_ERR_WORKSPACE
+    # one of the two pointers alone
+    b = with_reuse([-1, -1, 0])
+    b.s.reuse_host = None
+    assert _decode(lib, a, batch=C.byref(b.s)) == B.SA_ERR_INVALID
