@@ -237,6 +237,34 @@ def test_prefill_path_small():
     assert msg == "", msg
 
 
+def test_prefill_batch_of_sequences():
+    # several sequences in one prefill call: a short one, one with no new rows, a long one,
+    # and one made only of new rows (no prefix); row blocks of the indexer GEMM never span two
+    # sequences, and every row sees its own sequence's history only
+    wl = inputs.make("prefill64k", num_seqs=4, ctx=[700, 500, 3000, 129], q_len=[5, 0, 40, 129],
+                     seed_offset=21)
+    _say(f"prefill batch: ctx {wl.ctx_lens}, rows {wl.q_lens}")
+    dw = device.to_device(wl)
+    s = device.index_score(dw).cpu().numpy()
+    ref_s = oracle.index_scores(wl, ncols=s.shape[1])
+    pos = wl.q_pos().numpy()
+    assert s.shape[0] == wl.num_queries == 174
+    for r in range(wl.num_queries):
+        n = pos[r] + 1
+        err = np.abs(s[r, :n] - ref_s[r, :n]).max()
+        assert err <= 1e-4 * np.abs(ref_s[r, :n]).max(), r
+        assert np.all(np.isneginf(s[r, n:])), r  # past the row's own position
+    idx = device.topk(dw, torch.from_numpy(s).cuda()).cpu().numpy()
+    ref_idx = oracle.topk(s.astype(np.float64), pos + 1, wl.topk)
+    np.testing.assert_array_equal(idx, ref_idx)
+    ws = device.new_workspace(dw)
+    out = device.sparse_attn(dw, torch.from_numpy(idx).cuda(), ws).float().cpu().numpy()
+    ref_out = oracle.sparse_attn(wl, idx)
+    err, msg = output_error(out, ref_out, 2e-2)
+    _say(f"  prefill batch attention max abs error {err:.3e}")
+    assert msg == "", msg
+
+
 def test_fp8_ragged_small():
     wl = inputs.make("fp8ragged", num_seqs=5, ctx=[4096, 9000, 300, 2048, 5000])
     _say("fp8 ragged B=5")
