@@ -118,6 +118,23 @@ def test_decode_mla_ragged_and_edges(ctx):
             assert np.all(out.float().cpu().numpy()[b] == 0)
 
 
+@pytest.mark.parametrize("heads_q", [16, 40, 100])
+def test_decode_latent_head_counts(heads_q):
+    # latent rows with fewer query heads than a full workgroup, or than two full head groups:
+    # waves past the last head load head 0 and store nothing, and the merge leaves those
+    # heads alone (40: one head group of 64 with 24 idle heads; 100: a second group of 36)
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[5000, 700, 2048], heads_q=heads_q,
+                     seed_offset=200 + heads_q)
+    _say(f"decode latent rows, {heads_q} query heads")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out = torch.full((wl.num_seqs, heads_q, wl.dim_v), 7.0, dtype=torch.bfloat16, device="cuda")
+    out, idx = device.decode_step(dw, ws, out=out)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2)
+
+
 def test_index_score_matches_oracle():
     wl = inputs.make("decode32k", num_seqs=3, ctx=[4000, 100, 1500])
     _say("index_score decode B=3")
