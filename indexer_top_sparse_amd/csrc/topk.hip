@@ -388,23 +388,24 @@ __global__ __launch_bounds__(kRgT) void k_topk_rows_reg(TopkArgs a) {
         rg_radix<kRgSample, 1>([&](int j) { return key[16 * j]; }, hist, scan, res, pre_s, pb_s,
                                need_s, ex_s);
         const uint32_t bound = pre_s << (32 - pb_s);  // >= 1: the sampled keys are non-zero
+        // the list in thread order (its order does not matter: the emission below goes through
+        // a position bitmap): a count per thread and one block scan place every thread's keys
+        uint32_t mine = 0;
+#pragma unroll
+        for (int m = 0; m < kRgM; ++m) {
+            const uint32_t k = opaque_u32(key[m]);
+            mine += (k != 0u && k >= bound) ? 1u : 0u;
+        }
         uint32_t c_tot;
-        const uint32_t off = rg_round_offsets(
-            [&](int m) {
-                const uint32_t k = opaque_u32(key[m]);
-                return k != 0u && k >= bound;
-            },
-            cnt[0], scan, &c_tot);
+        uint32_t dst = block_excl_scan<kRgT>(mine, scan, &c_tot);
         if (c_tot >= k_eff && c_tot <= (uint32_t)kRgList) {
 #pragma unroll
             for (int m = 0; m < kRgM; ++m) {
                 const uint32_t k = opaque_u32(key[m]);
-                const bool in = k != 0u && k >= bound;
-                const uint64_t b = __ballot(in);
-                if (in) {
-                    const uint32_t dst = (uint32_t)__builtin_amdgcn_readlane((int)off, m) + lanes_below(b);
+                if (k != 0u && k >= bound) {
                     lkey[dst] = k;
                     lpos[dst] = kRgT * m + tid;
+                    ++dst;
                 }
             }
             len = (int)c_tot;
@@ -457,21 +458,37 @@ __global__ __launch_bounds__(kRgT) void k_topk_rows_reg(TopkArgs a) {
             __syncthreads();
             if (whole) break;
         }
-        // emission from the list (in position order): a key is taken when its composite reaches
-        // the threshold composite; thread t walks the entries [E t, E t + E)
+        // emission in position order: a key is taken when its composite reaches the threshold
+        // composite. The taken positions go into a bitmap of the row (2048 words, the round-count
+        // area); thread t then owns positions [64 t, 64 t + 64), two words, and one block scan
+        // of their population counts gives each thread its first output slot.
         const uint64_t thr = pb < 64 ? pre << (64 - pb) : pre;
-        const int E = (len + kRgT - 1) / kRgT;
-        const int e0 = min(len, tid * E), e1 = min(len, e0 + E);
-        uint32_t mine = 0;
-        for (int j = e0; j < e1; ++j)
-            mine += ((((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)lpos[j]) >= thr) ? 1u : 0u;
+        uint32_t *bits = &cnt[0][0];  // 2 kRgM kRgW = 2048 words = 65536 positions
+        static_assert(2 * kRgM * kRgW * 32 >= kRgMax && kRgMax / 64 == kRgT, "bitmap covers the row");
+        bits[2 * tid] = 0u;
+        bits[2 * tid + 1] = 0u;
+        __syncthreads();
+        for (int j = tid; j < len; j += kRgT) {
+            const int pos = lpos[j];
+            if ((((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)pos) >= thr)
+                atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+        }
+        __syncthreads();
+        uint32_t w0 = bits[2 * tid], w1 = bits[2 * tid + 1];
         uint32_t tot;
-        uint32_t dst = block_excl_scan<kRgT>(mine, scan, &tot);
-        for (int j = e0; j < e1; ++j)
-            if ((((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)lpos[j]) >= thr) {
-                if (dst < k_eff) out[dst] = lpos[j];
-                ++dst;
-            }
+        uint32_t dst = block_excl_scan<kRgT>((uint32_t)(__popc(w0) + __popc(w1)), scan, &tot);
+        while (w0) {
+            const int b = __ffs(w0) - 1;
+            if (dst < k_eff) out[dst] = 64 * tid + b;
+            ++dst;
+            w0 &= w0 - 1u;
+        }
+        while (w1) {
+            const int b = __ffs(w1) - 1;
+            if (dst < k_eff) out[dst] = 64 * tid + 32 + b;
+            ++dst;
+            w1 &= w1 - 1u;
+        }
     } else if (k_eff > 0) {
         // ---- all keys in registers: threshold by radix passes, then the emission in position
         //      order. A key is taken when its prefix is above the threshold prefix, or equal to
