@@ -135,6 +135,21 @@ def test_decode_latent_head_counts(heads_q):
     _check_decode(wl, out, idx, 2e-2)
 
 
+@pytest.mark.parametrize("topk", [1, 1000, 8192])
+def test_decode_unusual_k(topk):
+    # K of one, K not a multiple of the 32-row tile, and K above both the candidate list and
+    # the context of two of the sequences (every visible position, then -1)
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[20000, 5000, 700], topk=topk,
+                     seed_offset=300 + topk)
+    _say(f"decode K={topk}, ctx {wl.ctx_lens}")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2)
+
+
 def test_index_score_matches_oracle():
     wl = inputs.make("decode32k", num_seqs=3, ctx=[4000, 100, 1500])
     _say("index_score decode B=3")
