@@ -120,8 +120,11 @@ typedef struct sa_batch {
  * library quantizes each head's bf16 query row the same way before the dot products: for every
  * 32 consecutive entries, X = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 when all are
  * zero), code = E4M3(v / 2^X) rounded to nearest with ties to even and saturated at +-448. The
- * dot products then use the decoded values (fp32 accumulation). Two-level selection with MXFP8
- * keys is not supported (SA_ERR_UNSUPPORTED). */
+ * dot products then use the decoded values (fp32 accumulation).
+ *
+ * Two-level selection (block_k > 0) needs bf16 keys: its block summaries are bf16 means of the
+ * block's bf16 keys, which an E4M3 or MXFP8 cache no longer holds; with other key types the
+ * calls return SA_ERR_UNSUPPORTED. */
 typedef struct sa_indexer {
     int32_t heads;            /* H_I: 1..64 */
     int32_t dim;              /* d_I: 64 or 128 */

@@ -802,8 +802,10 @@ static sa_status check_select(const sa_batch *batch, RowPlan *rp, const sa_index
     if (!q_idx || !aligned16(q_idx) || !w) return fail(SA_ERR_INVALID, "q_idx (16-byte aligned) and w are required");
     if (k < 1 || k > 65536) return fail(SA_ERR_INVALID, "k must be in [1, 65536]");
     if (block_k < 0 || block_k > 65536) return fail(SA_ERR_INVALID, "block_k must be in [0, 65536]");
-    if (block_k > 0 && ix->key_dtype == SA_MXFP8)
-        return fail(SA_ERR_UNSUPPORTED, "two-level selection with MXFP8 keys");
+    if (block_k > 0 && ix->key_dtype != SA_BF16)
+        return fail(SA_ERR_UNSUPPORTED,
+                    "two-level selection needs bf16 indexer keys (its block summaries are bf16 "
+                    "means of bf16 keys)");
     if (block_k > 0 && !ix->pooled) return fail(SA_ERR_INVALID, "two-level selection needs ix->pooled");
     return SA_OK;
 }

@@ -1383,7 +1383,7 @@ hipError_t launch_reuse_copy(const int32_t *reuse, int num_seqs, int k, int32_t 
 // the fused two-stage selection (bf16 or E4M3 keys; MXFP8 keys have no two-level path)
 template <int DIM, int HT>
 static void *select2l_kernel_fmt(int key_fmt) {
-    if (key_fmt == kKeyE4M3) return reinterpret_cast<void *>(&k_decode_select_2l<DIM, HT, kKeyE4M3>);
+    // bf16 keys only: the block summaries are bf16 means of bf16 keys (the host rejects others)
     if (key_fmt == kKeyBf16) return reinterpret_cast<void *>(&k_decode_select_2l<DIM, HT, kKeyBf16>);
     return nullptr;
 }

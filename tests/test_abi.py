@@ -88,6 +88,15 @@ def test_invalid_arguments_are_rejected_on_the_host(lib):
     assert _decode(lib, a, ix=C.byref(bad)) == B.SA_ERR_UNSUPPORTED
     bad = B.kv_desc(128, 576, 512, a.kvc, softmax_scale=0.0)
     assert _decode(lib, a, kv=C.byref(bad)) == B.SA_ERR_INVALID
+    # two-level selection needs bf16 keys: E4M3 keys with summaries are rejected before any launch
+    codes = torch.zeros((8, 64, 128), dtype=torch.uint8)
+    scale = torch.ones((8, 64), dtype=torch.float32)
+    pooled = torch.zeros((8, 128), dtype=torch.bfloat16)
+    e4 = B.indexer_desc(64, 128, codes, key_scale=scale, pooled=pooled)
+    assert _decode(lib, a, ix=C.byref(e4), block_k=2) == B.SA_ERR_UNSUPPORTED
+    assert b"bf16 indexer keys" in lib.sa_last_error()
+    bf = B.indexer_desc(64, 128, a.keys, pooled=pooled)
+    assert _decode(lib, a, ix=C.byref(bf), block_k=2) == B.SA_ERR_WORKSPACE  # accepted, no workspace
     # context longer than the page table can address
     b2 = B.Batch(a.pt, a.ctx, [100, 257], 64, 8)
     assert _decode(lib, a, batch=C.byref(b2.s)) == B.SA_ERR_INVALID
