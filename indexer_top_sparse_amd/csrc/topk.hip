@@ -16,13 +16,14 @@ constexpr int kTkUnroll = 8;   // histogram passes: keys per thread whose loads 
 constexpr int kTkPer = 16;     // emission: consecutive keys per thread per round
 constexpr int kTkList = 7168;  // LDS list of (key, position) for the one-more-read path (56 KiB)
 
-__global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t scan[2 * kTkWaves + 1];
-    __shared__ uint32_t res[4];
-    __shared__ uint32_t lkey[kTkList];
-    __shared__ int32_t lpos[kTkList];
-    const int row = blockIdx.x, tid = threadIdx.x;
+// The selection of one row by a workgroup of kTkThreads threads, reading the row from HBM (in
+// shared memory: hist[2048], scan[2 kTkWaves + 1], res[4], lkey and lpos[CAP]).
+// Block-uniform; contains barriers.
+template <int CAP>
+__device__ __forceinline__ void topk_row_stream(const TopkArgs &a, int row, uint32_t *hist,
+                                                uint32_t *scan, uint32_t *res, uint32_t *lkey,
+                                                int32_t *lpos) {
+    const int tid = threadIdx.x;
     int seq, qoff, qlen;
     row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
     const int64_t pos_q = (int64_t)a.ctx_lens[seq] - qlen + qoff;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
         }
         // the keys above the first threshold bin plus those in it fit in LDS: one more read
         // collects them, and the rest happens there
-        if (pass == 0 && res[1] + res[2] <= (uint32_t)kTkList) {
+        if (pass == 0 && res[1] + res[2] <= (uint32_t)CAP) {
             listed = res[1] + res[2];
             break;
         }
@@ -228,6 +229,15 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
         }
     }
     for (int j = (int)k_eff + tid; j < a.k; j += kTkThreads) out[j] = -1;
+}
+
+__global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t scan[2 * kTkWaves + 1];
+    __shared__ uint32_t res[4];
+    __shared__ uint32_t lkey[kTkList];
+    __shared__ int32_t lpos[kTkList];
+    topk_row_stream<kTkList>(a, blockIdx.x, hist, scan, res, lkey, lpos);
 }
 
 // ---------------------------------------------------------------- rows of up to 65536 keys
@@ -523,11 +533,296 @@ __global__ __launch_bounds__(kRgT) void k_topk_rows_reg(TopkArgs a) {
     for (int j = (int)k_eff + tid; j < a.k; j += kRgT) out[j] = -1;
 }
 
+// ------------------------------------------------- rows of up to 65536 keys, one read
+// Two 512-thread workgroups share a CU, so that the selection of one overlaps the loads of the
+// other, and the row is read from HBM once:
+//  1. A strided sample of 4096 positions, loaded ahead of the row, gives a lower bound of the
+//     threshold: the lower edge of the first-digit bin of its ks-th largest key, ks a quarter
+//     above the sample's share of k. It is found while the row's first loads are in flight.
+//  2. The row streams through registers in groups of 16 scores per thread, kTqDepth groups in
+//     flight; every score whose key reaches the bound goes with its position to an LDS list
+//     (per group one block-wide slot range per wave, from one LDS atomic). The listed set is
+//     closed upwards in the key order, so when it holds at least k positions it holds the Top-K.
+//  3. The exact Top-K of the list by (key, position) composites, radix passes in LDS, and the
+//     emission through a bitmap of the row (positions 128 t .. 128 t + 127 belong to thread t).
+// Rows shorter than 8192, with k above an eighth of the row, or whose list is too short or too
+// long take the streaming selection. VEC = 4 reads 16 bytes per load (the row start 16-byte
+// aligned), VEC = 1 four bytes.
+// PERCU resident workgroups per CU: four (k up to 2048: a list of 4000 candidates, 64 registers,
+// two groups in flight) or two (larger k: 7168 candidates, three groups in flight).
+constexpr int kTqT = kTkThreads;             // 512 threads, the streaming selection's block
+constexpr int kTqMax = 65536;                // longest row
+constexpr int kTqGroups = kTqMax / (16 * kTqT);  // groups of 16 scores per thread
+constexpr int kTqSample = 8;                 // sampled positions per thread: 8192 i + t
+constexpr int kTqSmallK = 2048;              // largest k of the four-per-CU form
+static_assert(kTqGroups == 8 && kTqMax / 128 == kTqT && kTqSample * kTqT * 16 == kTqMax, "");
+template <int PERCU>
+struct TqCfg {
+    static constexpr int kList = PERCU == 4 ? 4000 : 7168;  // candidates
+    static constexpr int kDepth = PERCU == 4 ? 2 : 3;       // groups in flight
+};
+
+// position of score e (0..15) of group g, thread t
+template <int VEC>
+__device__ __forceinline__ int tq_pos(int g, int e, int t) {
+    return VEC == 4 ? 2048 * (4 * g + (e >> 2)) + 4 * t + (e & 3)
+                    : 1024 * (8 * g + (e >> 1)) + 512 * (e & 1) + t;
+}
+
+template <int VEC, int PERCU>
+__global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkArgs a) {
+    constexpr int kTqList = TqCfg<PERCU>::kList, kTqDepth = TqCfg<PERCU>::kDepth;
+    __shared__ uint32_t hist[2048];  // also the emission's bitmap of the row
+    __shared__ uint32_t scan[2 * kTkWaves + 1];
+    __shared__ uint32_t res[4];
+    __shared__ uint32_t lkey[kTqList];
+    __shared__ int32_t lpos[kTqList];
+    __shared__ uint32_t lcount;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    int seq, qoff, qlen;
+    row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
+    const int64_t pos_q = (int64_t)a.ctx_lens[seq] - qlen + qoff;
+    const int n = (int)min(pos_q + 1, a.ld);  // n <= kTqMax (the host checks ld)
+    const uint32_t k_eff = (uint32_t)min(a.k, max(n, 0));
+    const float *sc = a.scores + (int64_t)row * a.ld;
+    int32_t *out = a.idx + (int64_t)row * a.k;
+
+    int len = 0;
+    if (k_eff > 0 && n >= 8192 && 8 * (int64_t)k_eff <= n) {
+        // ---- the sample's loads, then the row's first groups (every load issued, clamped to
+        //      the last visible position; positions past the row are masked when used). The
+        //      thread index passes through an opaque copy per group and every group's last
+        //      use through one as well: the compiler keeps those in program order, so it can
+        //      neither hoist later groups' loads nor sink a group's work past them.
+        float smp[kTqSample];
+#pragma unroll
+        for (int i = 0; i < kTqSample; ++i) smp[i] = sc[min(8192 * i + tid, n - 1)];
+        float gb[kTqDepth][16];
+        auto issue = [&](int g, float (&b)[16]) {
+            const int t = (int)opaque_u32((uint32_t)threadIdx.x);
+            if constexpr (VEC == 4) {
+                const float4 *s4 = reinterpret_cast<const float4 *>(sc);
+                const int last = (n - 1) >> 2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = s4[min(kTqT * (4 * g + i) + t, last)];
+                    b[4 * i] = v.x;
+                    b[4 * i + 1] = v.y;
+                    b[4 * i + 2] = v.z;
+                    b[4 * i + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) b[e] = sc[min(tq_pos<1>(g, e, t), n - 1)];
+            }
+        };
+#pragma unroll
+        for (int g = 0; g < kTqDepth - 1; ++g) issue(g, gb[g]);
+        // ---- 1. the bound, from two 11-bit digits of the sample's keys (LDS-only barriers: the
+        //      row's loads stay in flight): the sample's ks-th largest key lies in bin b1 of the
+        //      first digit and then in bin b2 of the second, and the bound is that bin's lower edge
+        const int w = wave_id();
+        uint32_t skey[kTqSample];
+#pragma unroll
+        for (int i = 0; i < kTqSample; ++i) {
+            const uint32_t k = float_key(smp[i]);
+            skey[i] = 8192 * i + tid < n ? k : 0u;  // 0: outside the row (or the NaN keyed 0)
+        }
+        // block-wide suffix scan of hist (thread t owns bins 2047 - 4 t - j, j < 4): the bin
+        // holding the need-th largest entry goes to res[0], the count above it to res[1]
+        auto find_bin = [&](uint32_t need) {
+            uint32_t hv[4], csum = 0;
+            const int top = 2048 - 4 * tid - 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hv[j] = hist[top - j];
+                csum += hv[j];
+            }
+            const uint32_t incl = wave_incl_scan(csum);
+            if (lane_id() == 63) scan[w] = incl;
+            lds_barrier();
+            uint32_t run = incl - csum;
+#pragma unroll
+            for (int i = 0; i < kTkWaves; ++i) run += i < w ? scan[i] : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (run < need && run + hv[j] >= need) {
+                    res[0] = (uint32_t)(top - j);
+                    res[1] = run;
+                }
+                run += hv[j];
+            }
+        };
+        for (int i = tid; i < 2048; i += kTqT) hist[i] = 0u;
+        if (tid == 0) {
+            lcount = 0u;
+            res[0] = 0u;
+            res[1] = 0u;
+        }
+        uint32_t mine_s = 0;
+#pragma unroll
+        for (int i = 0; i < kTqSample; ++i) mine_s += skey[i] != 0u ? 1u : 0u;
+        const uint32_t ws = wave_incl_scan(mine_s);
+        if (lane_id() == 63) scan[kTkWaves + w] = ws;
+        lds_barrier();
+        uint32_t ns = 0;  // sampled keys inside the row
+#pragma unroll
+        for (int i = 0; i < kTkWaves; ++i) ns += scan[kTkWaves + i];
+#pragma unroll
+        for (int i = 0; i < kTqSample; ++i)
+            if (skey[i] != 0u) atomicAdd(&hist[skey[i] >> 21], 1u);
+        lds_barrier();
+        const uint32_t need_s =
+            (uint32_t)min<int64_t>(ns, ((int64_t)k_eff * ns + n - 1) / n * 5 / 4 + 16);
+        find_bin(need_s);
+        lds_barrier();
+        const uint32_t b1 = res[0], above1 = res[1];
+        for (int i = tid; i < 2048; i += kTqT) hist[i] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < kTqSample; ++i)
+            if (skey[i] != 0u && (skey[i] >> 21) == b1) atomicAdd(&hist[(skey[i] >> 10) & 2047u], 1u);
+        lds_barrier();
+        find_bin(need_s - above1);
+        lds_barrier();
+        // keys at or above the lower edge of that bin (never 0: positions past the row and the
+        // one NaN pattern whose key is 0 stay out)
+        const uint32_t bound = max((b1 << 21) | (res[0] << 10), 1u);
+        // ---- 2. the row, group by group, listing the keys at or above the bound
+#pragma unroll
+        for (int g = 0; g < kTqGroups; ++g) {
+            if (g + kTqDepth - 1 < kTqGroups)
+                issue(g + kTqDepth - 1, gb[(g + kTqDepth - 1) % kTqDepth]);
+            const int t = (int)opaque_u32((uint32_t)threadIdx.x);
+            uint32_t key[16], mine = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                // opaque: the group's work cannot move above the next group's loads
+                const uint32_t k = float_key(__uint_as_float(opaque_u32(__float_as_uint(gb[g % kTqDepth][e]))));
+                key[e] = tq_pos<VEC>(g, e, t) < n ? k : 0u;
+                mine += key[e] >= bound ? 1u : 0u;
+            }
+            // one slot range per wave: an LDS atomic by the last lane, broadcast
+            const uint32_t wincl = wave_incl_scan(mine);
+            uint32_t base = 0;
+            if (__builtin_amdgcn_readlane((int)wincl, 63) != 0) {
+                if (lane_id() == 63) base = atomicAdd(&lcount, wincl);
+                base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+            }
+            uint32_t dst = base + wincl - mine;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                if (key[e] >= bound) {
+                    if (dst < (uint32_t)kTqList) {
+                        lkey[dst] = key[e];
+                        lpos[dst] = tq_pos<VEC>(g, e, t);
+                    }
+                    ++dst;
+                }
+            }
+            dst = opaque_u32(dst);
+        }
+        lds_barrier();
+        const uint32_t c_tot = lcount;
+        if (c_tot >= k_eff && c_tot <= (uint32_t)kTqList) len = (int)c_tot;
+        __syncthreads();  // every thread has read lcount
+    }
+
+    if (len == 0) {  // block-uniform
+        topk_row_stream<kTqList>(a, row, hist, scan, res, lkey, lpos);
+        return;
+    }
+    // ---- 3. exact Top-K of the list by composites (key << 32 | ~position: a larger composite
+    //      is a larger score or, for equal scores, a lower position), radix passes in LDS
+    uint64_t pre = 0;
+    int pb = 0;
+    uint32_t lneed = k_eff;
+    while (pb < 64) {
+        const int nbits = min(11, 64 - pb);
+        const int shift = 64 - pb - nbits;
+        const int nb = 1 << nbits;
+        for (int i = tid; i < 2048; i += kTqT) hist[i] = 0u;
+        __syncthreads();
+        for (int j = tid; j < len; j += kTqT) {
+            const uint64_t c = ((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)lpos[j];
+            if (pb == 0 || (c >> (64 - pb)) == pre)
+                atomicAdd(&hist[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t hv[4], csum = 0;
+        const int top = nb - 4 * tid - 1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            hv[j] = top - j >= 0 ? hist[top - j] : 0u;
+            csum += hv[j];
+        }
+        if (tid == 0) res[0] = 0u;
+        uint32_t tot;
+        uint32_t run = block_excl_scan<kTqT>(csum, scan, &tot);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (run < lneed && run + hv[j] >= lneed) {
+                res[0] = (uint32_t)(top - j);
+                res[1] = run;
+                res[2] = hv[j];
+            }
+            run += hv[j];
+        }
+        __syncthreads();
+        lneed -= res[1];
+        pre = (pre << nbits) | res[0];
+        pb += nbits;
+        const bool whole = res[2] == lneed;  // always true once all 64 bits are used
+        __syncthreads();
+        if (whole) break;
+    }
+    // ---- emission in position order through the bitmap (in the histogram's words, free since
+    //      the last pass's final barrier): thread t owns words 4 t .. 4 t + 3
+    const uint64_t thr = pb < 64 ? pre << (64 - pb) : pre;
+    uint32_t *bits = hist;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bits[4 * tid + i] = 0u;
+    __syncthreads();
+    for (int j = tid; j < len; j += kTqT) {
+        const int pos = lpos[j];
+        if ((((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)pos) >= thr)
+            atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+    }
+    __syncthreads();
+    uint32_t wv[4], cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        wv[i] = bits[4 * tid + i];
+        cnt += (uint32_t)__popc(wv[i]);
+    }
+    uint32_t tot;
+    uint32_t dst = block_excl_scan<kTqT>(cnt, scan, &tot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x = wv[i];
+        while (x) {
+            const int b = __ffs(x) - 1;
+            if (dst < k_eff) out[dst] = 128 * tid + 32 * i + b;
+            ++dst;
+            x &= x - 1u;
+        }
+    }
+    for (int j = (int)k_eff + tid; j < a.k; j += kTqT) out[j] = -1;
+}
+
 hipError_t launch_topk_rows(const TopkArgs &a, int rows, hipStream_t st) {
-    if (a.ld <= kRgMax)
-        hipLaunchKernelGGL(k_topk_rows_reg, dim3(rows), dim3(kRgT), 0, st, a);
-    else
+    if (a.ld <= kTqMax) {
+        const bool v4 = a.ld % 4 == 0 && reinterpret_cast<uintptr_t>(a.scores) % 16 == 0;
+        const bool small_k = a.k <= kTqSmallK;
+        const void *kern = v4 ? (small_k ? reinterpret_cast<const void *>(&k_topk_rows_1r<4, 4>)
+                                         : reinterpret_cast<const void *>(&k_topk_rows_1r<4, 2>))
+                              : (small_k ? reinterpret_cast<const void *>(&k_topk_rows_1r<1, 4>)
+                                         : reinterpret_cast<const void *>(&k_topk_rows_1r<1, 2>));
+        void *args[] = {const_cast<TopkArgs *>(&a)};
+        return hipLaunchKernel(kern, dim3(rows), dim3(kTqT), args, 0, st);
+    } else {
         hipLaunchKernelGGL(k_topk_rows, dim3(rows), dim3(kTkThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -165,7 +165,9 @@ def test_index_score_matches_oracle():
 # Row Top-K runs the register-resident kernel when the row stride is at most 65536 and the
 # streaming kernel above that: the exact tests below run at both strides (the wider one pads
 # the rows with -inf, which no row's visible range reaches).
-TOPK_STRIDES = (None, 70000)
+# row strides: the scores' own width (16-byte loads), 20001 (not a multiple of four: 4-byte
+# loads) and 70000 (rows longer than 65536 take the streaming kernel)
+TOPK_STRIDES = (None, 20001, 70000)
 
 
 def _at_stride(s, ld):
@@ -217,9 +219,9 @@ def test_topk_crowded_threshold_bin(ld):
 
 
 def test_topk_rows_at_the_register_kernel_limit():
-    """Rows of exactly 65536 visible scores (the register-resident kernel's limit), one of them
-    with a crowded threshold bin and ties, one short row, and the same rows through the
-    streaming kernel (stride 65537)."""
+    """Rows of exactly 65536 visible scores (the one-read kernel's limit), one of them with a
+    crowded threshold bin and ties, one short row, and the same rows through the streaming kernel
+    (stride 65537)."""
     rng = np.random.default_rng(9)
     wl = inputs.make("decode32k", num_seqs=3, ctx=[65536, 65536, 5], seed_offset=9)
     dw = device.to_device(wl)
@@ -232,6 +234,26 @@ def test_topk_rows_at_the_register_kernel_limit():
     for ld in (65536, 65537):
         st = torch.from_numpy(_at_stride(s, ld if ld > 65536 else None)).cuda()
         idx = device.topk(dw, st, k=2048).cpu().numpy()
+        np.testing.assert_array_equal(idx, ref, err_msg=f"stride {ld}")
+
+
+@pytest.mark.parametrize("k", [2048, 2049, 4096, 8192])
+def test_topk_full_rows_large_k(k):
+    """Rows of 65536 scores on both sides of the one-read kernel's switch at k = 2048 (four
+    workgroups per CU up to it, two above), and rows whose candidate list overflows the larger
+    list, which take the streaming selection (k = 8192); with 16-byte and 4-byte loads."""
+    rng = np.random.default_rng(40 + k)
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[65536, 65536, 40000], seed_offset=40)
+    dw = device.to_device(wl)
+    s = np.full((3, 65536), -np.inf, dtype=np.float32)
+    s[0] = rng.standard_normal(65536).astype(np.float32)
+    s[1] = (rng.standard_normal(65536) * np.linspace(0.5, 2.0, 65536)).astype(np.float32)
+    s[2, :40000] = np.round(rng.standard_normal(40000) * 8).astype(np.float32)  # ties
+    # stride 65536: 16-byte loads; 65533 (not a multiple of four; the rows cut there): 4-byte loads
+    for ld in (65536, 65533):
+        sl = np.ascontiguousarray(s[:, :ld])
+        ref = oracle.topk(sl.astype(np.float64), np.minimum(np.array(wl.ctx_lens), ld), k)
+        idx = device.topk(dw, torch.from_numpy(sl).cuda(), k=k).cpu().numpy()
         np.testing.assert_array_equal(idx, ref, err_msg=f"stride {ld}")
 
 
