@@ -103,9 +103,12 @@ def algorithmic_bytes(wl):
 
 
 # kernels of each launch the bench times (a launch may consist of several kernels; the latent
-# attention kernel merges inside the launch, the other one is followed by k_attn_merge)
-LAUNCH_KERNELS = {"select": ("k_decode_select",),
-                  "attention": ("k_attn_latent", "k_sparse_attn", "k_attn_merge")}
+# attention kernel merges inside the launch, the other one is followed by k_attn_merge). Decode
+# times select and attention, prefill index_score, topk and sparse_attn.
+_ATTN_KERNELS = ("k_attn_latent", "k_sparse_attn", "k_attn_merge")
+LAUNCH_KERNELS = {"select": ("k_decode_select",), "attention": _ATTN_KERNELS,
+                  "index_score": ("k_prefill_score", "k_index_score"),
+                  "topk": ("k_topk_rows",), "sparse_attn": _ATTN_KERNELS}
 
 
 def write_traffic(workload, csvs, copy_gib):
@@ -180,6 +183,13 @@ def run_prefill(args):
     idx = torch.empty((rows, wl.topk), dtype=torch.int32, device="cuda")
     out = torch.empty((rows, wl.heads_q, wl.dim_v), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_gib > 0:  # the counters' reference copy (see write_traffic)
+        nc = int(args.copy_calibration_gib * 2**30) // 4
+        ca = torch.empty(nc, dtype=torch.float32, device="cuda").fill_(1.0)
+        cb = torch.empty_like(ca)
+        cb.copy_(ca)
+        torch.cuda.synchronize()
+        del ca, cb
 
     def step():
         B.index_score(d.batch, d.ix, d.t["q_idx"], d.t["w"], scores)
@@ -220,9 +230,17 @@ def run_prefill(args):
         "sparse_attn": {"bound": "mfma", "achieved": fa / (t_a * 1e-3) / 1e12,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops": fa},
     }
+    # measured HBM bytes per launch, when the counters were taken on the current sources
+    tr = {}
+    tfile = os.path.join(PROFILES, f"traffic_{args.workload}.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_hash") == kernel_source_hash():
+            tr = {k: v["hbm_bytes_per_launch"] for k, v in t["kernels"].items()}
     for k, r in roof.items():
         r["frac"] = r["achieved"] / r["peak"]
         r["avg_launch_ms"] = mean[k]
+        r["traffic"] = tr.get(k)
     dominant = max(("index_score", "topk", "sparse_attn"), key=lambda k: mean[k])
     res = {
         "metric": "prefill query tokens/s (indexer GEMM + row Top-K + sparse attn)",
@@ -231,7 +249,7 @@ def run_prefill(args):
         "scaling": "weak", "vs_baseline": None, "dtype": wl.kv_dtype, "data": "synthetic",
         "config": {"workload": f"{args.workload}: {rows} query rows after a "
                                f"{max(wl.ctx_lens) - rows}-token prefix, K={wl.topk}"},
-        "roofline": dict(kernel=dominant, traffic=None, **roof[dominant]),
+        "roofline": dict(kernel=dominant, **roof[dominant]),
         "rooflines": roof,
         "kernels_ms": {"index_score": t_s, "topk": t_k, "sparse_attn": t_a},
         "step_distribution": {"steps": n, "median_ms": float(np.median(per["step"])),

@@ -77,11 +77,13 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 524288.0),
                                        ("sa::k_decode_select<128, 4, 0, 0>", 1000.0),
                                        ("sa::k_decode_select<128, 4, 0, 0>", 3000.0),
-                                       ("sa::k_attn_latent<2>", 500.0)])
+                                       ("sa::k_attn_latent<2>", 500.0),
+                                       ("sa::k_topk_rows_1r<4, 4>", 7000.0)])
     _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1048576.0),
                                        ("sa::k_decode_select<128, 4, 0, 0>", 10.0),
                                        ("sa::k_decode_select<128, 4, 0, 0>", 30.0),
-                                       ("sa::k_attn_latent<2>", 40.0)])
+                                       ("sa::k_attn_latent<2>", 40.0),
+                                       ("sa::k_topk_rows_1r<4, 4>", 8.0)])
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     bench.write_traffic("unit", [str(fetch), str(write)], 1.0)
     res = json.load(open(tmp_path / "traffic_unit.json"))
@@ -95,6 +97,10 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     att = res["kernels"]["attention"]
     assert att["fetch_bytes"] == pytest.approx(500.0 * 1024 * 2)
     assert att["write_bytes"] == pytest.approx(40.0 * 1024)
+    tk = res["kernels"]["topk"]  # prefill's row Top-K
+    assert tk["fetch_bytes"] == pytest.approx(7000.0 * 1024 * 2)
+    assert tk["write_bytes"] == pytest.approx(8.0 * 1024)
+    assert "index_score" not in res["kernels"]  # no dispatch of it in these counters
 
 
 def test_kernel_hash_ignores_comments(tmp_path, monkeypatch):
