@@ -1,10 +1,14 @@
-// Row-wise Top-K over scores in HBM (the unfused selection used by Prefill and by tests):
-// one workgroup per query row, radix select on order-preserving keys (three digits of
-// 11/11/10 bits, stopping as soon as the threshold bin is taken whole), then an ordered
-// emission that keeps ascending positions and gives ties at the threshold to the lower
-// positions. When the keys of the first digit's threshold bin and above fit in LDS, one more
-// read collects them and the selection ends there (two reads of the row instead of three). "Top-K filtering ... custom operator" of "Engineering Path for Day-0 Adaptation of
-// Trillion-Scale Sparse Models on Domestic AI Accelerators" §3.1.
+// Row-wise Top-K over scores in HBM: the selection step of Prefill, whose scores are
+// materialised, and of sa_topk. Ties at the threshold go to the lower positions and the indices
+// come out in ascending order. The Top-K filtering operator of "Engineering Path for Day-0
+// Adaptation of Trillion-Scale Sparse Models on Domestic AI Accelerators" §3.1.
+//  - Rows of up to 65536 scores: k_topk_rows_1r reads each row once (a sampled lower bound of
+//    the threshold, the candidates at or above it listed as the row streams, an exact selection
+//    over them).
+//  - Longer rows, and rows whose candidates do not fit its list: the streaming selection, radix
+//    passes over the row (digits of 11/11/10 bits, stopping as soon as the threshold bin is
+//    taken whole); when the first digit's threshold bin and above fit in LDS, one more read
+//    collects them and the selection ends there.
 #include "common.h"
 #include "kernels.h"
 
@@ -240,297 +244,11 @@ __global__ __launch_bounds__(kTkThreads) void k_topk_rows(TopkArgs a) {
     topk_row_stream<kTkList>(a, blockIdx.x, hist, scan, res, lkey, lpos);
 }
 
-// ---------------------------------------------------------------- rows of up to 65536 keys
-// The whole row lives in registers: 1024 threads hold 64 keys each (key m of thread t is
-// position 1024 m + t, so every load instruction of a wave reads 256 consecutive bytes). The row
-// is read from HBM once, with all 64 loads of a thread issued before the first is used.
-//  1. A strided sample (the rounds 0, 16, 32, 48: 4096 positions) gives a lower bound of the
-//     threshold: the lower edge of the first-digit bin of its ks-th largest key, with ks a
-//     quarter above the sample's share of k.
-//  2. Every key at or above that bound goes to an LDS list in position order (wave ballots per
-//     round; one block scan over the (round, wave) counts places the rounds).
-//  3. The exact Top-K of the list, by (key, position) composites, and the emission from it.
-// When the bound admits fewer than k keys or more than the list holds, the selection runs on
-// all keys in registers instead (radix passes with LDS histograms, emission with ballots).
-// Few LDS atomics hit the histograms on the list path: scores concentrate in a few first-digit
-// bins, and atomics of one wave on one address are serialised.
-constexpr int kRgT = 1024;            // threads
-constexpr int kRgW = kRgT / 64;       // waves
-constexpr int kRgM = 64;              // keys per thread
-constexpr int kRgMax = kRgT * kRgM;   // longest row
-constexpr int kRgList = 8192;         // candidate list (64 KiB)
-constexpr int kRgSample = 4;          // sampled rounds: 0, 16, 32, 48
-
+// A value the compiler may not take apart or move across other such values (asm statements keep
+// their program order).
 __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
     asm volatile("" : "+v"(x));
     return x;
-}
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Radix selection (11/11/10-bit digits) of the `need`-th largest among the non-zero keys kf(j),
-// j < J, of every thread: on return the top pbits bits of the threshold are `prefix`, `need` is
-// how many keys equal to that prefix are still to be taken, and `exact` says that all of them
-// are (the threshold bin was taken whole). Block-uniform; contains barriers.
-template <int J, int PASSES = 3, class KF>
-__device__ __forceinline__ void rg_radix(KF kf, uint32_t *hist, uint32_t *scan, uint32_t *res,
-                                         uint32_t &prefix, int &pbits, uint32_t &need, bool &exact) {
-    const int tid = threadIdx.x;
-    prefix = 0;
-    pbits = 0;
-    exact = false;
-    for (int pass = 0; pass < PASSES && need > 0; ++pass) {
-        const int bits = pass < 2 ? 11 : 10;
-        const int shift = 32 - pbits - bits;
-        const int nb = 1 << bits;
-        for (int i = tid; i < 2048; i += kRgT) hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-            // opaque: otherwise the tests k != 0, the same in every pass, are hoisted out of the
-            // pass loop as per-key masks that do not fit the scalar registers
-            const uint32_t k = opaque_u32(kf(j));
-            if (k != 0u && (pbits == 0 || (k >> (32 - pbits)) == prefix))
-                atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        // suffix scan: thread t owns bins [nb - 2 (t + 1), nb - 2 t)
-        uint32_t hv[2], csum = 0;
-        const int top = nb - 2 * tid - 1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            hv[j] = top - j >= 0 ? hist[top - j] : 0u;
-            csum += hv[j];
-        }
-        if (tid == 0) res[0] = 0u;
-        uint32_t tot;
-        uint32_t run = block_excl_scan<kRgT>(csum, scan, &tot);  // (its barriers order res[0])
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (run < need && run + hv[j] >= need) {
-                res[0] = (uint32_t)(top - j);
-                res[1] = run;
-                res[2] = hv[j];
-            }
-            run += hv[j];
-        }
-        __syncthreads();
-        need -= res[1];
-        prefix = (prefix << bits) | res[0];
-        pbits += bits;
-        const bool whole = res[2] == need;
-        __syncthreads();  // res is rewritten by the next pass
-        if (whole) {
-            exact = true;
-            break;
-        }
-    }
-}
-
-// Per round m (position 1024 m + t), the count of lanes of this wave whose predicate holds,
-// placed in position order: returns, in lane m, the number of keys before round m of this wave
-// (all rounds of all waves before it, plus earlier waves of round m). `cnt` holds kRgM * kRgW
-// words. Block-uniform; contains barriers.
-template <class PF>
-__device__ __forceinline__ uint32_t rg_round_offsets(PF pred, uint32_t *cnt, uint32_t *scan,
-                                                     uint32_t *total) {
-    const int tid = threadIdx.x, w = wave_id();
-    // opaque per call: the lane tests below are not shared (and kept) across calls
-    const int l = (int)opaque_u32((uint32_t)lane_id());
-    uint32_t mine = 0;  // lane m: this wave's count in round m
-#pragma unroll
-    for (int m = 0; m < kRgM; ++m) {
-        const uint32_t c = (uint32_t)__popcll(__ballot(pred(m)));
-        mine = l == m ? c : mine;
-    }
-    cnt[l * kRgW + w] = mine;
-    __syncthreads();
-    // entry tid = (round tid / 16, wave tid % 16), in position order
-    const uint32_t off = block_excl_scan<kRgT>(cnt[tid], scan, total);
-    __syncthreads();  // every entry has been read
-    cnt[tid] = off;
-    __syncthreads();
-    return cnt[l * kRgW + w];
-}
-
-__global__ __launch_bounds__(kRgT) void k_topk_rows_reg(TopkArgs a) {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t scan[2 * kRgW + 1];
-    __shared__ uint32_t res[4];
-    __shared__ uint32_t cnt[2][kRgM * kRgW];
-    __shared__ uint32_t lkey[kRgList];
-    __shared__ int32_t lpos[kRgList];
-    const int row = blockIdx.x, tid = threadIdx.x, l = lane_id(), w = wave_id();
-    int seq, qoff, qlen;
-    row_info(a.q_indptr, a.num_seqs, row, seq, qoff, qlen);
-    const int64_t pos_q = (int64_t)a.ctx_lens[seq] - qlen + qoff;
-    const int n = (int)min(pos_q + 1, a.ld);  // 1 <= n <= kRgMax (the host checks ld)
-    const float *sc = a.scores + (int64_t)row * a.ld;
-    int32_t *out = a.idx + (int64_t)row * a.k;
-    const uint32_t k_eff = (uint32_t)min(a.k, max(n, 0));
-
-    // ---- the row into registers: key 0 marks a position past the row (a score's key is never
-    //      0). Every load is issued (clamped to the last position, n >= 1), with no branch, and
-    //      masked afterwards by arithmetic, so no per-load condition stays alive.
-    uint32_t key[kRgM];
-#pragma unroll
-    for (int m = 0; m < kRgM; ++m) key[m] = __float_as_uint(sc[min(kRgT * m + tid, n - 1)]);
-#pragma unroll
-    for (int m = 0; m < kRgM; ++m) {
-        // all ones inside the row; opaque, so that no comparison mask is kept per key
-        const uint32_t inside = opaque_u32((uint32_t)((kRgT * m + tid - n) >> 31));
-        key[m] = float_key(__uint_as_float(key[m])) & inside;
-    }
-
-    // ---- 1. a lower bound of the threshold from the sample, 2. the list of keys at or above it
-    int len = 0;
-    if (k_eff > 0 && n >= 8192 && 8 * (int64_t)k_eff <= n) {
-        int ns = 0;  // valid sampled positions
-#pragma unroll
-        for (int j = 0; j < kRgSample; ++j) ns += min(kRgT, max(0, n - kRgT * 16 * j));
-        uint32_t need_s = (uint32_t)min<int64_t>(ns, ((int64_t)k_eff * ns + n - 1) / n * 5 / 4 + 16);
-        uint32_t pre_s;
-        int pb_s;
-        bool ex_s;
-        // one digit: the bound is the lower edge of the sample's threshold bin
-        rg_radix<kRgSample, 1>([&](int j) { return key[16 * j]; }, hist, scan, res, pre_s, pb_s,
-                               need_s, ex_s);
-        const uint32_t bound = pre_s << (32 - pb_s);  // >= 1: the sampled keys are non-zero
-        // the list in thread order (its order does not matter: the emission below goes through
-        // a position bitmap): a count per thread and one block scan place every thread's keys
-        uint32_t mine = 0;
-#pragma unroll
-        for (int m = 0; m < kRgM; ++m) {
-            const uint32_t k = opaque_u32(key[m]);
-            mine += (k != 0u && k >= bound) ? 1u : 0u;
-        }
-        uint32_t c_tot;
-        uint32_t dst = block_excl_scan<kRgT>(mine, scan, &c_tot);
-        if (c_tot >= k_eff && c_tot <= (uint32_t)kRgList) {
-#pragma unroll
-            for (int m = 0; m < kRgM; ++m) {
-                const uint32_t k = opaque_u32(key[m]);
-                if (k != 0u && k >= bound) {
-                    lkey[dst] = k;
-                    lpos[dst] = kRgT * m + tid;
-                    ++dst;
-                }
-            }
-            len = (int)c_tot;
-        }
-        __syncthreads();
-    }
-
-    if (len > 0) {
-        // ---- 3. exact Top-K of the list by composites (key << 32 | ~position: a larger composite
-        //      is a larger score or, for equal scores, a lower position), radix passes in LDS
-        uint64_t pre = 0;
-        int pb = 0;
-        uint32_t lneed = k_eff;
-        while (pb < 64) {
-            const int bits = min(11, 64 - pb);
-            const int shift = 64 - pb - bits;
-            const int nb = 1 << bits;
-            for (int i = tid; i < 2048; i += kRgT) hist[i] = 0u;
-            __syncthreads();
-            for (int j = tid; j < len; j += kRgT) {
-                const uint64_t c = ((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)lpos[j];
-                if (pb == 0 || (c >> (64 - pb)) == pre)
-                    atomicAdd(&hist[(uint32_t)(c >> shift) & (uint32_t)(nb - 1)], 1u);
-            }
-            __syncthreads();
-            uint32_t hv[2], csum = 0;
-            const int top = nb - 2 * tid - 1;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                hv[j] = top - j >= 0 ? hist[top - j] : 0u;
-                csum += hv[j];
-            }
-            if (tid == 0) res[0] = 0u;
-            uint32_t tot;
-            uint32_t run = block_excl_scan<kRgT>(csum, scan, &tot);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (run < lneed && run + hv[j] >= lneed) {
-                    res[0] = (uint32_t)(top - j);
-                    res[1] = run;
-                    res[2] = hv[j];
-                }
-                run += hv[j];
-            }
-            __syncthreads();
-            lneed -= res[1];
-            pre = (pre << bits) | res[0];
-            pb += bits;
-            const bool whole = res[2] == lneed;  // always true once all 64 bits are used
-            __syncthreads();
-            if (whole) break;
-        }
-        // emission in position order: a key is taken when its composite reaches the threshold
-        // composite. The taken positions go into a bitmap of the row (2048 words, the round-count
-        // area); thread t then owns positions [64 t, 64 t + 64), two words, and one block scan
-        // of their population counts gives each thread its first output slot.
-        const uint64_t thr = pb < 64 ? pre << (64 - pb) : pre;
-        uint32_t *bits = &cnt[0][0];  // 2 kRgM kRgW = 2048 words = 65536 positions
-        static_assert(2 * kRgM * kRgW * 32 >= kRgMax && kRgMax / 64 == kRgT, "bitmap covers the row");
-        bits[2 * tid] = 0u;
-        bits[2 * tid + 1] = 0u;
-        __syncthreads();
-        for (int j = tid; j < len; j += kRgT) {
-            const int pos = lpos[j];
-            if ((((uint64_t)lkey[j] << 32) | (uint32_t)~(uint32_t)pos) >= thr)
-                atomicOr(&bits[pos >> 5], 1u << (pos & 31));
-        }
-        __syncthreads();
-        uint32_t w0 = bits[2 * tid], w1 = bits[2 * tid + 1];
-        uint32_t tot;
-        uint32_t dst = block_excl_scan<kRgT>((uint32_t)(__popc(w0) + __popc(w1)), scan, &tot);
-        while (w0) {
-            const int b = __ffs(w0) - 1;
-            if (dst < k_eff) out[dst] = 64 * tid + b;
-            ++dst;
-            w0 &= w0 - 1u;
-        }
-        while (w1) {
-            const int b = __ffs(w1) - 1;
-            if (dst < k_eff) out[dst] = 64 * tid + 32 + b;
-            ++dst;
-            w1 &= w1 - 1u;
-        }
-    } else if (k_eff > 0) {
-        // ---- all keys in registers: threshold by radix passes, then the emission in position
-        //      order. A key is taken when its prefix is above the threshold prefix, or equal to
-        //      it while fewer than need_eq equal keys at earlier positions were taken (all of
-        //      them when the threshold bin is taken whole).
-        uint32_t prefix, need = k_eff;
-        int pbits;
-        bool exact;
-        rg_radix<kRgM>([&](int m) { return key[m]; }, hist, scan, res, prefix, pbits, need, exact);
-        const int shb = 32 - pbits;
-        const uint32_t need_eq = exact ? 0xFFFFFFFFu : need;
-        auto above = [&](uint32_t k) { return k != 0u && (k >> shb) > prefix; };
-        auto equal = [&](uint32_t k) { return k != 0u && (k >> shb) == prefix; };
-        uint32_t ta, te;
-        const uint32_t off_a = rg_round_offsets([&](int m) { return above(opaque_u32(key[m])); },
-                                                cnt[0], scan, &ta);
-        const uint32_t off_e = rg_round_offsets([&](int m) { return equal(opaque_u32(key[m])); },
-                                                cnt[1], scan, &te);
-#pragma unroll
-        for (int m = 0; m < kRgM; ++m) {
-            const uint32_t k = opaque_u32(key[m]);
-            const bool ia = above(k), ie = equal(k);
-            const uint64_t ba = __ballot(ia), be = __ballot(ie);
-            if (!ia && !ie) continue;
-            const uint32_t a_before = (uint32_t)__builtin_amdgcn_readlane((int)off_a, m) + lanes_below(ba);
-            const uint32_t e_before = (uint32_t)__builtin_amdgcn_readlane((int)off_e, m) + lanes_below(be);
-            if (ie && e_before >= need_eq) continue;
-            const uint32_t dst = a_before + min(e_before, need_eq);
-            if (dst < k_eff) out[dst] = kRgT * m + tid;
-        }
-    }
-    for (int j = (int)k_eff + tid; j < a.k; j += kRgT) out[j] = -1;
 }
 
 // ------------------------------------------------- rows of up to 65536 keys, one read
@@ -776,10 +494,17 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
         __syncthreads();
         if (whole) break;
     }
-    // ---- emission in position order through the bitmap (in the histogram's words, free since
-    //      the last pass's final barrier): thread t owns words 4 t .. 4 t + 3
+    // ---- emission in position order through a bitmap of the row (in the histogram's words, free
+    //      since the last pass's final barrier): the taken positions set their bits; thread t
+    //      owns words 4 t .. 4 t + 3, and one block scan of their population counts gives each
+    //      word the number of taken positions before it. A taken entry's output slot is that
+    //      count plus the taken positions before it in its own word. The index row is staged in
+    //      LDS (over the list's keys, which are not read again) and written out coalesced.
     const uint64_t thr = pb < 64 ? pre << (64 - pb) : pre;
     uint32_t *bits = hist;
+    uint32_t *wpre = reinterpret_cast<uint32_t *>(lpos) + kTqList - 2048;  // per-word counts
+    int32_t *stage = reinterpret_cast<int32_t *>(lkey);
+    static_assert(kTqList >= 2048 && kTqList >= kTqSmallK, "word counts and the index row fit");
 #pragma unroll
     for (int i = 0; i < 4; ++i) bits[4 * tid + i] = 0u;
     __syncthreads();
@@ -789,24 +514,44 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
             atomicOr(&bits[pos >> 5], 1u << (pos & 31));
     }
     __syncthreads();
-    uint32_t wv[4], cnt = 0;
+    {
+        uint32_t wv[4], c[4], cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        wv[i] = bits[4 * tid + i];
-        cnt += (uint32_t)__popc(wv[i]);
-    }
-    uint32_t tot;
-    uint32_t dst = block_excl_scan<kTqT>(cnt, scan, &tot);
+        for (int i = 0; i < 4; ++i) {
+            wv[i] = bits[4 * tid + i];
+            c[i] = (uint32_t)__popc(wv[i]);
+            cnt += c[i];
+        }
+        uint32_t tot;
+        uint32_t run = block_excl_scan<kTqT>(cnt, scan, &tot);
+        // the word counts go to the list's last 2048 position slots, so every listed position is
+        // read into registers first
+        int32_t pl[kTqList / kTqT + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t x = wv[i];
-        while (x) {
-            const int b = __ffs(x) - 1;
-            if (dst < k_eff) out[dst] = 128 * tid + 32 * i + b;
-            ++dst;
-            x &= x - 1u;
+        for (int q = 0; q < kTqList / kTqT + 1; ++q) {
+            const int j = tid + q * kTqT;
+            pl[q] = j < len ? lpos[j] : -1;
+        }
+        __syncthreads();  // every listed position is in registers
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wpre[4 * tid + i] = run;
+            run += c[i];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kTqList / kTqT + 1; ++q) {
+            const int pos = pl[q];
+            if (pos < 0) continue;
+            const uint32_t wd = bits[pos >> 5], bit = 1u << (pos & 31);
+            if (wd & bit) {
+                const uint32_t slot = wpre[pos >> 5] + (uint32_t)__popc(wd & (bit - 1u));
+                if (slot < k_eff) stage[slot] = pos;
+            }
         }
     }
+    __syncthreads();
+    for (int j = tid; j < (int)k_eff; j += kTqT) out[j] = stage[j];
     for (int j = (int)k_eff + tid; j < a.k; j += kTqT) out[j] = -1;
 }
 
