@@ -254,9 +254,10 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 // ------------------------------------------------- rows of up to 65536 keys, one read
 // Two 512-thread workgroups share a CU, so that the selection of one overlaps the loads of the
 // other, and the row is read from HBM once:
-//  1. A strided sample of 4096 positions, loaded ahead of the row, gives a lower bound of the
-//     threshold: the lower edge of the first-digit bin of its ks-th largest key, ks a quarter
-//     above the sample's share of k. It is found while the row's first loads are in flight.
+//  1. A sample of 4096 positions spread over the row, loaded ahead of it, gives a lower bound of the
+//     threshold: the lower edge of the 22-bit bin (two 11-bit digits) holding its ks-th largest
+//     key, ks a quarter above the sample's share of k, plus 16. It is found while the row's
+//     first loads are in flight.
 //  2. The row streams through registers in groups of 16 scores per thread, kTqDepth groups in
 //     flight; every score whose key reaches the bound goes with its position to an LDS list
 //     (per group one block-wide slot range per wave, from one LDS atomic). The listed set is
@@ -271,7 +272,7 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 constexpr int kTqT = kTkThreads;             // 512 threads, the streaming selection's block
 constexpr int kTqMax = 65536;                // longest row
 constexpr int kTqGroups = kTqMax / (16 * kTqT);  // groups of 16 scores per thread
-constexpr int kTqSample = 8;                 // sampled positions per thread: 8192 i + t
+constexpr int kTqSample = 8;                 // sampled positions per thread (tq_sample_pos)
 constexpr int kTqSmallK = 2048;              // largest k of the four-per-CU form
 static_assert(kTqGroups == 8 && kTqMax / 128 == kTqT && kTqSample * kTqT * 16 == kTqMax, "");
 template <int PERCU>
@@ -279,6 +280,13 @@ struct TqCfg {
     static constexpr int kList = PERCU == 4 ? 4000 : 7168;  // candidates
     static constexpr int kDepth = PERCU == 4 ? 2 : 3;       // groups in flight
 };
+
+// sampled position i (0..7) of thread t: the first 16 positions of every block of 256 (64-byte
+// pieces, evenly spread over the row, so that a row whose large scores gather in one region, as
+// recent positions may, is sampled there too)
+__device__ __forceinline__ int tq_sample_pos(int i, int t) {
+    return 8192 * i + 256 * (t >> 4) + (t & 15);
+}
 
 // position of score e (0..15) of group g, thread t
 template <int VEC>
@@ -314,7 +322,7 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
         //      neither hoist later groups' loads nor sink a group's work past them.
         float smp[kTqSample];
 #pragma unroll
-        for (int i = 0; i < kTqSample; ++i) smp[i] = sc[min(8192 * i + tid, n - 1)];
+        for (int i = 0; i < kTqSample; ++i) smp[i] = sc[min(tq_sample_pos(i, tid), n - 1)];
         float gb[kTqDepth][16];
         auto issue = [&](int g, float (&b)[16]) {
             const int t = (int)opaque_u32((uint32_t)threadIdx.x);
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
 #pragma unroll
         for (int i = 0; i < kTqSample; ++i) {
             const uint32_t k = float_key(smp[i]);
-            skey[i] = 8192 * i + tid < n ? k : 0u;  // 0: outside the row (or the NaN keyed 0)
+            skey[i] = tq_sample_pos(i, tid) < n ? k : 0u;  // 0: outside the row (or the NaN keyed 0)
         }
         // block-wide suffix scan of hist (thread t owns bins 2047 - 4 t - j, j < 4): the bin
         // holding the need-th largest entry goes to res[0], the count above it to res[1]

@@ -257,6 +257,25 @@ def test_topk_full_rows_large_k(k):
         np.testing.assert_array_equal(idx, ref, err_msg=f"stride {ld}")
 
 
+def test_topk_rows_with_large_scores_in_one_region():
+    """Rows of 65536 whose largest scores gather in one region, as recent positions may: a rising
+    trend with noise, a strictly increasing row, and a row whose Top-2048 lie in its last 2500
+    positions (the sample must see the region for the one-read path; the result is exact on
+    either path)."""
+    rng = np.random.default_rng(77)
+    n = 65536
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[n, n, n], seed_offset=77)
+    dw = device.to_device(wl)
+    s = np.empty((3, n), dtype=np.float32)
+    s[0] = (np.linspace(0.0, 6.0, n) + rng.standard_normal(n)).astype(np.float32)
+    s[1] = np.linspace(-1.0, 1.0, n).astype(np.float32)
+    s[2] = rng.standard_normal(n).astype(np.float32)
+    s[2, -2500:] = (5.0 + rng.random(2500)).astype(np.float32)
+    ref = oracle.topk(s.astype(np.float64), np.array(wl.ctx_lens), 2048)
+    idx = device.topk(dw, torch.from_numpy(s).cuda(), k=2048).cpu().numpy()
+    np.testing.assert_array_equal(idx, ref)
+
+
 def test_sparse_attn_on_oracle_indices():
     wl = inputs.make("decode32k", num_seqs=3, ctx=[3000, 40, 2100])
     dw = device.to_device(wl)
