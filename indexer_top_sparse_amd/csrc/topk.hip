@@ -252,15 +252,15 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 }
 
 // ------------------------------------------------- rows of up to 65536 keys, one read
-// Two 512-thread workgroups share a CU, so that the selection of one overlaps the loads of the
-// other, and the row is read from HBM once:
+// Several 512-thread workgroups share a CU, so that the selection work of some overlaps the
+// loads of others, and the row is read from HBM once:
 //  1. A sample of 4096 positions spread over the row, loaded ahead of it, gives a lower bound of the
 //     threshold: the lower edge of the 22-bit bin (two 11-bit digits) holding its ks-th largest
 //     key, ks a quarter above the sample's share of k, plus 16. It is found while the row's
 //     first loads are in flight.
 //  2. The row streams through registers in groups of 16 scores per thread, kTqDepth groups in
 //     flight; every score whose key reaches the bound goes with its position to an LDS list
-//     (per group one block-wide slot range per wave, from one LDS atomic). The listed set is
+//     (per group, one slot range per wave from one LDS atomic). The listed set is
 //     closed upwards in the key order, so when it holds at least k positions it holds the Top-K.
 //  3. The exact Top-K of the list by (key, position) composites, radix passes in LDS, and the
 //     emission through a bitmap of the row (positions 128 t .. 128 t + 127 belong to thread t).
@@ -512,7 +512,8 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
     uint32_t *bits = hist;
     uint32_t *wpre = reinterpret_cast<uint32_t *>(lpos) + kTqList - 2048;  // per-word counts
     int32_t *stage = reinterpret_cast<int32_t *>(lkey);
-    static_assert(kTqList >= 2048 && kTqList >= kTqSmallK, "word counts and the index row fit");
+    // (k_eff <= len <= kTqList, so the index row fits over the keys)
+    static_assert(kTqList >= 2048, "the word counts fit in the list's positions");
 #pragma unroll
     for (int i = 0; i < 4; ++i) bits[4 * tid + i] = 0u;
     __syncthreads();
