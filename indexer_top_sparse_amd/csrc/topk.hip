@@ -281,11 +281,11 @@ struct TqCfg {
     static constexpr int kDepth = PERCU == 4 ? 2 : 3;       // groups in flight
 };
 
-// sampled position i (0..7) of thread t: the first 16 positions of every block of 256 (64-byte
-// pieces, evenly spread over the row, so that a row whose large scores gather in one region, as
-// recent positions may, is sampled there too)
+// sampled position i (0..7) of thread t: the first 32 positions of every block of 512 (whole
+// 128-byte lines, evenly spread over the row, so that a row whose large scores gather in one
+// region, as recent positions may, is sampled there too)
 __device__ __forceinline__ int tq_sample_pos(int i, int t) {
-    return 8192 * i + 256 * (t >> 4) + (t & 15);
+    return 8192 * i + 512 * (t >> 5) + (t & 31);
 }
 
 // position of score e (0..15) of group g, thread t
