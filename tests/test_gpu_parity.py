@@ -162,11 +162,10 @@ def test_index_score_matches_oracle():
         assert np.all(np.isneginf(s[b, n:]))
 
 
-# Row Top-K runs the register-resident kernel when the row stride is at most 65536 and the
-# streaming kernel above that: the exact tests below run at both strides (the wider one pads
-# the rows with -inf, which no row's visible range reaches).
-# row strides: the scores' own width (16-byte loads), 20001 (not a multiple of four: 4-byte
-# loads) and 70000 (rows longer than 65536 take the streaming kernel)
+# Row Top-K runs the one-read kernel when the row stride is at most 65536 and the streaming
+# kernel above that. The exact tests below run at three strides: the scores' own width (16-byte
+# loads), 20001 (not a multiple of four: 4-byte loads) and 70000 (the streaming kernel); the
+# wider strides pad the rows with -inf, which no row's visible range reaches.
 TOPK_STRIDES = (None, 20001, 70000)
 
 
