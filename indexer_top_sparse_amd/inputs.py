@@ -254,7 +254,10 @@ def make(preset: str, seed_offset: int = 0, **overrides) -> Workload:
         w = torch.randn((nq, H_I), generator=gw, dtype=torch.float32) / 8.0
 
     dtype = p["dtype"]
-    idx_dtype = p.get("idx_dtype", dtype)
+    # the indexer keys follow the cache dtype unless given; tile scales are defined for latent KV
+    # rows only, so with them the keys default to bf16
+    idx_dtype = p.get("idx_dtype", dtype if dtype in ("bf16", "fp8") else "bf16")
+    assert idx_dtype in ("bf16", "fp8", "mxfp8"), f"indexer key dtype {idx_dtype!r}"
     idx_mx_scale = None
     if idx_dtype == "mxfp8":
         idx_keys, idx_mx_scale = quantize_rows_mxfp8(kf)

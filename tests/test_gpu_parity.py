@@ -309,6 +309,31 @@ def test_prefill_path_small():
     assert msg == "", msg
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "fp8t128"])
+def test_prefill_path_fp8(dtype):
+    """Prefill rows over E4M3 caches: E4M3 indexer keys with row scales and E4M3 latent rows
+    with row scales (fp8), or bf16 keys and latent rows with a scale per 128-entry tile
+    (fp8t128). Scores against the oracle on the same codes, the row Top-K exact on the GPU's
+    scores, the attention within the fp8 tolerance."""
+    wl = inputs.make("prefill64k", ctx=2500, q_len=40, dtype=dtype, seed_offset=21)
+    _say(f"prefill {dtype}: ctx 2500, 40 query rows")
+    dw = device.to_device(wl)
+    s = device.index_score(dw).cpu().numpy()
+    ref_s = oracle.index_scores(wl, ncols=s.shape[1])
+    pos = wl.q_pos().numpy()
+    for r in range(wl.num_queries):
+        n = pos[r] + 1
+        err = np.abs(s[r, :n] - ref_s[r, :n]).max()
+        assert err <= 1e-4 * np.abs(ref_s[r, :n]).max(), (r, err)
+    idx = device.topk(dw, torch.from_numpy(s).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(idx, oracle.topk(s.astype(np.float64), pos + 1, wl.topk))
+    ws = device.new_workspace(dw)
+    out = device.sparse_attn(dw, torch.from_numpy(idx).cuda(), ws).float().cpu().numpy()
+    err, msg = output_error(out, oracle.sparse_attn(wl, idx), 5e-2)
+    _say(f"  attention max abs error {err:.3e}")
+    assert msg == "", msg
+
+
 def test_prefill_batch_of_sequences():
     # several sequences in one prefill call: a short one, one with no new rows, a long one,
     # and one made only of new rows (no prefix); row blocks of the indexer GEMM never span two
