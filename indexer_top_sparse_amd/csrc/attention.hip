@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // registers) and output accumulators (128) take most of its 256, so addresses are rebuilt per
 // tile and LDS reads run only a few fragments ahead of their MFMAs.
 // Rows move from HBM straight into LDS (global_load_lds_dwordx4) through a ring of tiles of 32
-// rows (T = 1: three, two in flight while one is computed; T = 2: four, one step of two tiles
+// rows (T = 1: four, three in flight while one is computed; T = 2: four, one step of two tiles
 // in flight while the other is computed), and the copies use no registers. With T = 2 a step's
 // copies are issued as soon as a barrier shows the slots they overwrite free, before the wait
 // for the step about to be computed, so that its single step ahead never drains. Every wave
@@ -554,8 +554,11 @@ __device__ __forceinline__ void lat_merge_units(const AttnArgs &a, int row, int 
 // head groups x 2 phases (64 heads), the phases taking alternate tiles.
 template <int T>
 struct LatCfg {
-    static constexpr int kRing = T == 1 ? 3 : 4;   // staged tiles
-    static constexpr int kAhead = T == 1 ? 2 : 1;  // steps in flight while one is computed
+    static constexpr int kRing = 4;                // staged tiles
+    static constexpr int kAhead = T == 1 ? 3 : 1;  // steps in flight while one is computed
+    // T = 2 keeps a table of logit biases (0 or -inf per selected row); T = 1 derives them from
+    // the slot table, whose LDS then holds a fourth tile
+    static constexpr bool kBiasTable = T == 2;
     static constexpr int kCPW = T == 1 ? 5 : 9;    // 1 KiB copies per wave per step
     static constexpr int kHPW = 128 / T;           // query heads per workgroup
     static constexpr int kHW = 8 / T;              // groups of 16 heads per workgroup
@@ -566,7 +569,7 @@ template <int T>
 __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
     using C = LatCfg<T>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    // dynamic LDS: ring [kRing][36864] | slots [split_len] int32 | logit bias [split_len] fp32
+    // dynamic LDS: ring [kRing][36864] | slots [split_len] int32 | (T = 2) logit bias [split_len] fp32
     uint8_t *ring = lds;
     int32_t *s_slot = reinterpret_cast<int32_t *>(lds + C::kRing * kLatTileB);
     float *s_bias = reinterpret_cast<float *>(s_slot + a.split_len);
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
             }
         }
         s_slot[j] = slot;
-        s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
+        if constexpr (C::kBiasTable) s_bias[j] = slot < 0 ? -__builtin_inff() : 0.f;
     }
     // every load above completes here (the query fragments included): inside the tile loop the
     // only vector-memory operations in flight are this wave's tile copies, which the waits
@@ -674,8 +677,9 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
         for (int st = 0; st < C::kAhead; ++st) issue(st);
     for (int st = 0; st < nsteps; ++st) {
         if constexpr (T == 1) {
-            // step st has landed once at most the copies of step st + 1 are outstanding
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::kCPW));
+            // step st has landed once at most the copies of steps st + 1 .. st + kAhead - 1 are
+            // outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm((C::kAhead - 1) * C::kCPW));
             lds_barrier();            // every wave's copies of step st landed; st - 1 fully read
             issue(st + C::kAhead);    // into the slots step st - 1 occupied
         } else {
@@ -722,9 +726,21 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         // ---- logits in the log2 domain: rows 16 mt + 4 g + i of head L
-        const float *bia = s_bias + t * kTile + 4 * g;
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(bia);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(bia + 16);
+        f32x4 b0, b1;
+        if constexpr (C::kBiasTable) {
+            const float *bia = s_bias + t * kTile + 4 * g;
+            b0 = *reinterpret_cast<const f32x4 *>(bia);
+            b1 = *reinterpret_cast<const f32x4 *>(bia + 16);
+        } else {
+            const int32_t *sli = s_slot + t * kTile + 4 * g;
+            const u32x4 q0 = *reinterpret_cast<const u32x4 *>(sli);
+            const u32x4 q1 = *reinterpret_cast<const u32x4 *>(sli + 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b0[i] = (int32_t)q0[i] < 0 ? -__builtin_inff() : 0.f;
+                b1[i] = (int32_t)q1[i] < 0 ? -__builtin_inff() : 0.f;
+            }
+        }
         float x[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -909,7 +925,8 @@ __global__ __launch_bounds__(kLatThreads, 1) void k_attn_latent(AttnArgs a) {
 
 size_t attn_latent_lds(int tphases, int split_len) {
     const int ring = tphases == 1 ? LatCfg<1>::kRing : LatCfg<2>::kRing;
-    return (size_t)ring * kLatTileB + (size_t)split_len * 8;
+    const bool bias = tphases == 1 ? LatCfg<1>::kBiasTable : LatCfg<2>::kBiasTable;
+    return (size_t)ring * kLatTileB + (size_t)split_len * (bias ? 8 : 4);
 }
 
 int attn_latent_max_rows(int tphases) {
