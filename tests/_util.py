@@ -129,6 +129,39 @@ def check_topk_row(got, ref, ref_scores_row, n_visible, k, rel=1e-3):
     return ""
 
 
+def check_topk_in(got, ref, ref_scores_row, candidates, k, rel=1e-3):
+    """check_topk_row when only some positions are candidates (the tokens of the kept blocks of a
+    hierarchical selection): candidates is a bool array over the sequence's positions; the GPU
+    set must hold exactly k_eff = min(k, number of candidates) distinct candidates and then -1s,
+    and the near-tie rule applies as in check_topk_row. Returns an error string or ''."""
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    cand = np.asarray(candidates, dtype=bool)
+    k_eff = min(k, int(cand.sum()))
+    g = got[got >= 0]
+    if len(g) != k_eff:
+        return f"expected {k_eff} valid indices, got {len(g)}"
+    if np.any(got[got < 0] != -1):
+        return "negative index other than -1"
+    if np.sum(got == -1) != k - k_eff:
+        return "padding is not -1"
+    if len(np.unique(g)) != len(g):
+        return "duplicate indices"
+    if np.any(g >= len(cand)) or not np.all(cand[g]):
+        return "index outside the candidates"
+    r = ref[ref >= 0]
+    if k_eff == 0:
+        return ""
+    theta = float(np.min(ref_scores_row[r]))
+    tol = rel * abs(theta)
+    diff = np.setxor1d(g, r)
+    bad = [int(t) for t in diff if abs(float(ref_scores_row[t]) - theta) > tol]
+    if bad:
+        return (f"{len(diff)} differing positions, {len(bad)} outside the near-tie band "
+                f"(theta={theta:.6g}, e.g. pos {bad[0]} score {float(ref_scores_row[bad[0]]):.6g})")
+    return ""
+
+
 # Attention outputs pass two gates. ABS: the acceptance tolerance against the fp32/fp64
 # definition (2e-2 for bf16 caches, 5e-2 for E4M3 caches). REL: a regression gate relative to
 # the largest reference output. Outputs here are small (at the 576-wide latent shapes the

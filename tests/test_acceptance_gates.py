@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from indexer_top_sparse_amd import inputs
-from tests._util import check_topk_row, output_error
+from tests._util import check_topk_in, check_topk_row, output_error
 
 
 def test_output_gate_rejects_a_three_percent_softmax_scale_error():
@@ -51,3 +51,22 @@ def test_index_gate():
     assert check_topk_row(np.array([0, 1, 2, -1]), ref4, s, 3, 4) == ""
     assert check_topk_row(np.array([0, 1, 2, -2]), ref4, s, 3, 4) != ""
     assert check_topk_row(np.array([0, 1, -1, -1]), ref4, s, 3, 4) != ""
+
+
+def test_index_gate_over_candidates():
+    """Hierarchical selection: only the tokens of the kept blocks are candidates, and there may
+    be fewer of them than K."""
+    s = np.array([9.0, 8.0, 5.0, 4.0, 3.0, 3.0005, 1.0, 0.0])
+    cand = np.array([False, False, True, True, True, True, False, True])  # 0, 1, 6 not kept
+    ref = np.array([2, 3, 5])
+    assert check_topk_in(np.array([2, 3, 5]), ref, s, cand, 3) == ""
+    assert check_topk_in(np.array([2, 3, 4]), ref, s, cand, 3) == ""   # near tie at theta
+    # a larger score outside the candidates, or a clear miss, is rejected
+    assert check_topk_in(np.array([0, 2, 3]), ref, s, cand, 3) != ""
+    assert check_topk_in(np.array([2, 3, 7]), ref, s, cand, 3) != ""
+    # K above the candidate count (5): the candidates, then exactly -1
+    ref7 = np.array([2, 3, 4, 5, 7, -1, -1])
+    assert check_topk_in(np.array([2, 3, 4, 5, 7, -1, -1]), ref7, s, cand, 7) == ""
+    assert check_topk_in(np.array([2, 3, 4, 5, 6, -1, -1]), ref7, s, cand, 7) != ""
+    assert check_topk_in(np.array([2, 3, 4, 5, -1, -1, -1]), ref7, s, cand, 7) != ""
+    assert check_topk_in(np.array([2, 3, 4, 5, 7, -1, -2]), ref7, s, cand, 7) != ""

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from indexer_top_sparse_amd import binding, device, inputs
-from tests._util import check_topk_row, custom_workload, output_error, to_bf16
+from tests._util import check_topk_in, check_topk_row, custom_workload, output_error, to_bf16
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -148,6 +148,54 @@ def test_decode_unusual_k(topk):
     torch.cuda.synchronize()
     assert binding.workspace_error(ws) == 0
     _check_decode(wl, out, idx, 2e-2)
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 256])
+def test_decode_page_sizes(page_size):
+    """The fused decode step at page sizes other than 64: one token per page (every key row and
+    latent row its own page), 16 (a 16-token key tile is one page) and 256 (several tiles per
+    page), on permuted pages."""
+    wl = inputs.make("decode32k", num_seqs=3, ctx=[3000, 700, 4097], page_size=page_size,
+                     seed_offset=60 + page_size)
+    _say(f"decode page_size {page_size}, ctx {wl.ctx_lens}")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2)
+
+
+def test_two_level_page_size_16():
+    """Hierarchical selection with blocks of 16 tokens (a block is a page): blocks against the
+    oracle's block scores, then tokens against the oracle's fine stage on the GPU's blocks."""
+    wl = inputs.make("long1m", num_seqs=2, ctx=[20000, 3000], block_topk=64, page_size=16,
+                     seed_offset=76)
+    _say(f"two-level page_size 16, ctx {wl.ctx_lens}")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    blocks = device.block_select(dw, ws).cpu().numpy()
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    bs = oracle.block_scores(wl)
+    nblk = [-(-n // wl.page_size) for n in wl.ctx_lens]
+    ref_blocks = oracle.topk(bs, np.array(nblk), wl.block_topk)
+    got = idx.cpu().numpy()
+    ref_tok = oracle.topk_in_blocks(wl, blocks, k=wl.topk)
+    P = wl.page_size
+    for b, n in enumerate(wl.ctx_lens):
+        msg = check_topk_row(blocks[b], ref_blocks[b], bs[b], nblk[b], wl.block_topk)
+        assert msg == "", f"seq {b} blocks: {msg}"
+        # 64 kept blocks of 16 tokens: at most 1024 candidates, fewer than K
+        cand = np.zeros(n, dtype=bool)
+        for j in blocks[b][blocks[b] >= 0]:
+            cand[j * P:min((j + 1) * P, n)] = True
+        msg = check_topk_in(got[b], ref_tok[b], oracle.index_scores(wl, rows=[b])[0], cand, wl.topk)
+        assert msg == "", f"seq {b} tokens: {msg}"
+    err, msg = output_error(out.float().cpu().numpy(), oracle.sparse_attn(wl, got), 2e-2)
+    _say(f"  max abs error {err:.3e}")
+    assert msg == "", msg
 
 
 def test_index_score_matches_oracle():
