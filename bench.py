@@ -272,6 +272,9 @@ def main():
     # about 300 steps (some 30 ms of work) bring the GPU to its steady clocks; launches timed
     # before that run several percent slower
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--settle-ms", type=float, default=30.0,
+                    help="after the warm-up, run untimed steps for this long (their count is "
+                         "reported as settle_steps)")
     ap.add_argument("--workload", default="decode32k",
                     help="input preset (decode32k is the headline configuration)")
     ap.add_argument("--replicas", type=int, default=3)
@@ -345,6 +348,17 @@ def main():
     torch.cuda.synchronize()
     assert B.workspace_error(ws) == 0, "device-side wait failed"
     log(f"[bench] warmup {args.warmup} done")
+
+    # the clocks settle after some 30 ms of sustained work; a short warm-up leaves the first
+    # timed steps several percent slower, so untimed steps run for that long after it
+    settle, s0 = 0, time.perf_counter()
+    while settle < 100000 and (time.perf_counter() - s0) * 1e3 < args.settle_ms:
+        for j in range(10):
+            step(args.warmup + settle + j)
+        settle += 10
+        torch.cuda.synchronize()
+    assert B.workspace_error(ws) == 0, "device-side wait failed"
+    log(f"[bench] settle: {settle} more untimed steps")
 
     # ---- headline: K fused decode steps
     stream = torch.cuda.current_stream()
@@ -499,6 +513,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
