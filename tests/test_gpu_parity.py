@@ -166,6 +166,45 @@ def test_decode_page_sizes(page_size):
     _check_decode(wl, out, idx, 2e-2)
 
 
+@pytest.mark.parametrize("ctx", [32768, 1])
+def test_decode_single_sequence(ctx):
+    """A batch of one sequence: at 32768 tokens the whole selection grid serves one sequence
+    (many workgroups meet at its barriers); at one token the step has a single candidate."""
+    wl = inputs.make("decode32k", num_seqs=1, ctx=[ctx], seed_offset=90 + ctx % 7)
+    _say(f"decode B=1 ctx {ctx}")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    _check_decode(wl, out, idx, 2e-2)
+
+
+def test_two_level_keeping_every_block_is_single_level():
+    """When block_k is at least a sequence's block count, every block is kept and the two-level
+    selection must be the single-level Top-K over the whole context."""
+    wl = inputs.make("long1m", num_seqs=3, ctx=[8000, 5000, 2100], block_topk=128, seed_offset=81)
+    _say(f"two-level keeping every block, ctx {wl.ctx_lens}")
+    dw = device.to_device(wl)
+    ws = device.new_workspace(dw)
+    blocks = device.block_select(dw, ws).cpu().numpy()
+    out, idx = device.decode_step(dw, ws)
+    torch.cuda.synchronize()
+    assert binding.workspace_error(ws) == 0
+    got = idx.cpu().numpy()
+    for b, n in enumerate(wl.ctx_lens):
+        nblk = -(-n // wl.page_size)
+        assert nblk <= wl.block_topk
+        assert sorted(blocks[b][blocks[b] >= 0].tolist()) == list(range(nblk)), f"seq {b}"
+        s_row = oracle.index_scores(wl, rows=[b])[0]
+        ref = oracle.topk(s_row[None, :n], np.array([n]), wl.topk)[0]
+        msg = check_topk_row(got[b], ref, s_row, n, wl.topk)
+        assert msg == "", f"seq {b}: {msg}"
+    err, msg = output_error(out.float().cpu().numpy(), oracle.sparse_attn(wl, got), 2e-2)
+    _say(f"  max abs error {err:.3e}")
+    assert msg == "", msg
+
+
 def test_two_level_page_size_16():
     """Hierarchical selection with blocks of 16 tokens (a block is a page): blocks against the
     oracle's block scores, then tokens against the oracle's fine stage on the GPU's blocks."""
