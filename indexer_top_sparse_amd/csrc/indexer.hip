@@ -538,7 +538,9 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
         for (int pp = 0; pp < NN / 2; ++pp) {
             const int64_t tok = t0 + 64 * pp + l;
             const float x = l < 32 ? v[2 * pp] : v[2 * pp + 1];
-            if (tok < tb1) out[tok] = tok <= p_row ? x : -__builtin_inff();
+            // streamed out (nontemporal): the row Top-K reads them once, and they do not
+            // displace reused lines from the caches
+            if (tok < tb1) __builtin_nontemporal_store(tok <= p_row ? x : -__builtin_inff(), &out[tok]);
         }
     };
     // step t: tile t + 1 moves global -> registers while tile t is computed, then registers
@@ -558,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void k_prefill_score(ScoreArgs a) {
     // ---- columns past every row of the workgroup
     if (live)
         for (int64_t tok = tb0 + (int64_t)ntiles * kPfTile + l; tok < tb1; tok += 64)
-            out[tok] = -__builtin_inff();
+            __builtin_nontemporal_store(-__builtin_inff(), &out[tok]);
 }
 
 // ================================================================ decode selection (fused)

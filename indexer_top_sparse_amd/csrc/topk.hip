@@ -266,7 +266,7 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 //     emission through a bitmap of the row (positions 128 t .. 128 t + 127 belong to thread t).
 // Rows shorter than 8192, with k above an eighth of the row, or whose list is too short or too
 // long take the streaming selection. VEC = 4 reads 16 bytes per load (the row start 16-byte
-// aligned), VEC = 1 four bytes.
+// aligned), VEC = 1 four bytes; both with the nontemporal hint (the row is read once).
 // PERCU resident workgroups per CU: four (k up to 2048: a list of 4000 candidates, 64 registers,
 // two groups in flight) or two (larger k: 7168 candidates, three groups in flight).
 constexpr int kTqT = kTkThreads;             // 512 threads, the streaming selection's block
@@ -322,24 +322,22 @@ __global__ __launch_bounds__(kTqT, PERCU * kTqT / 256) void k_topk_rows_1r(TopkA
         //      neither hoist later groups' loads nor sink a group's work past them.
         float smp[kTqSample];
 #pragma unroll
-        for (int i = 0; i < kTqSample; ++i) smp[i] = sc[min(tq_sample_pos(i, tid), n - 1)];
+        for (int i = 0; i < kTqSample; ++i)
+            smp[i] = __builtin_nontemporal_load(&sc[min(tq_sample_pos(i, tid), n - 1)]);
         float gb[kTqDepth][16];
         auto issue = [&](int g, float (&b)[16]) {
             const int t = (int)opaque_u32((uint32_t)threadIdx.x);
             if constexpr (VEC == 4) {
-                const float4 *s4 = reinterpret_cast<const float4 *>(sc);
                 const int last = (n - 1) >> 2;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float4 v = s4[min(kTqT * (4 * g + i) + t, last)];
-                    b[4 * i] = v.x;
-                    b[4 * i + 1] = v.y;
-                    b[4 * i + 2] = v.z;
-                    b[4 * i + 3] = v.w;
+                    const u32x4 v = ldg16_stream(sc + 4 * min(kTqT * (4 * g + i) + t, last));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) b[4 * i + e] = __uint_as_float(v[e]);
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) b[e] = sc[min(tq_pos<1>(g, e, t), n - 1)];
+                for (int e = 0; e < 16; ++e) b[e] = __builtin_nontemporal_load(&sc[min(tq_pos<1>(g, e, t), n - 1)]);
             }
         };
 #pragma unroll
